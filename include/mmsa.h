@@ -1,0 +1,191 @@
+/*
+ * mmsa.h — C ABI of libmmsa: modality-aware dynamic sparse-attention prefill
+ * for one causal attention layer on an AMD Instinct MI355X (gfx950).
+ *
+ * What is computed (sources: the MInference 1.0 summary page, "Approach";
+ * the MMInference summary page, "Approach"; the MMInference verdict page,
+ * fields key_machinery and core_discovery):
+ *   per attention head, online index estimation from the last 64 queries
+ *   (vertical / slash lines), from 64-token mean-pooled blocks (block-sparse),
+ *   or from a stride/phase scan (grid); a modality-aware permutation of rows
+ *   and key columns; a FlashAttention-style causal prefill over only the
+ *   selected 64x64 tiles; and the inverse permutation of the output.
+ *
+ * Call order, all on one HIP stream, with one descriptor and one workspace:
+ *   mmsa_estimate_vs     (vertical-slash, boundary and grid heads)
+ *   mmsa_estimate_blocks (block-sparse heads)          -- 1 and 2 in any order
+ *   mmsa_permute         (row orders, gathers, per-tile sparse plan)
+ *   mmsa_sparse_prefill  (the attention itself)
+ *   mmsa_unpermute       (inverse permutation into O)
+ *
+ * Conventions shared by every entry point:
+ *  - Ownership: the caller owns all device memory (Q, K, V, O, LSE and the
+ *    workspace).  The library never allocates or frees device memory and keeps
+ *    no pointer after a call returns.  Host arrays named in the descriptor are
+ *    read only during the call.
+ *  - Asynchrony: every call enqueues work on `stream` (a hipStream_t; NULL is
+ *    the null stream) and returns without waiting for the device.
+ *  - Tensors: bf16, element strides (batch, head, row) with the last (head
+ *    dimension) contiguous; base pointers 16-byte aligned; row strides a
+ *    multiple of 8 elements.  d is 64 or 128.
+ *  - Errors: arguments are validated on the host before anything is enqueued;
+ *    on any error nothing is launched or written, and mmsa_last_error() gives
+ *    a thread-local message.  No C++ exception crosses this interface.
+ *  - Budgets above the number of candidates are clamped, not errors.
+ *  - NaN or Inf in Q/K/V give undefined (but memory-safe) results.
+ *  - Limits: L < 2^22 tokens (tile indices are packed in 16 bits), B*Hq <= 4096.
+ */
+#ifndef MMSA_H
+#define MMSA_H
+
+#include <stddef.h>
+#include <stdint.h>
+
+#ifdef __cplusplus
+extern "C" {
+#endif
+
+#define MMSA_ABI_VERSION 1
+#define MMSA_TILE 64       /* query and key tile (the 64-token blocks)      */
+#define MMSA_EST_ROWS 64   /* estimation rows: the last 64 queries          */
+
+typedef int32_t mmsa_status;
+enum {
+  MMSA_OK = 0,
+  MMSA_INVALID_ARGUMENT = 1,  /* null pointer, shape, stride, budget, segments, combination */
+  MMSA_UNSUPPORTED = 2,       /* d, alignment, size limits                                  */
+  MMSA_WORKSPACE_TOO_SMALL = 3,
+  MMSA_HIP_ERROR = 4          /* a launch failed; detail in mmsa_last_error()               */
+};
+
+/* Per-head sparse pattern (the offline per-head assignment; MInference summary
+ * page, "Approach": A-shape, vertical-slash, block-sparse; MMInference
+ * verdict page, core_discovery: grid, Q-boundary, 2D-boundary). */
+enum { MMSA_ASHAPE = 0, MMSA_VS = 1, MMSA_BLOCK = 2, MMSA_GRID = 3 };
+/* Layout (how modality boundaries are handled; MMInference verdict page,
+ * core_discovery: row-wise permutation grouping same-modality queries, 2D
+ * permutation isolating each modality pair). */
+enum {
+  MMSA_PLAIN = 0,             /* no modality handling                              */
+  MMSA_Q_BOUNDARY = 1,        /* VS only: rows grouped by modality, one index set per query modality */
+  MMSA_BOUNDARY_2D = 2,       /* VS only: rows and keys grouped, one index set per (query, key) modality pair */
+  MMSA_MODALITY_GROUPED = 3   /* GRID only: stride/phase measured on the modality-grouped order */
+};
+enum { MMSA_TEXT = 0, MMSA_VIDEO = 1 };
+
+/* Flags of mmsa_layer_desc.flags */
+#define MMSA_FLAG_EXPORT_SCORES 1u /* keep the block-score matrix of BLOCK heads in the workspace */
+
+typedef struct {
+  int32_t pattern;      /* MMSA_ASHAPE / VS / BLOCK / GRID                          */
+  int32_t layout;       /* MMSA_PLAIN / Q_BOUNDARY / BOUNDARY_2D / MODALITY_GROUPED  */
+  int32_t sink;         /* A-shape: keys j < sink are kept                           */
+  int32_t window;       /* A-shape: keys with i - j < window are kept (>= 1)         */
+  int32_t k_vertical;   /* VS: vertical columns kept (per index set)                 */
+  int32_t k_slash;      /* VS: slash diagonals kept (per index set)                  */
+  int32_t k_blocks;     /* BLOCK: key blocks kept per query block                    */
+  int32_t grid_phases;  /* GRID: number of phases w kept at the winning stride (>=1) */
+  int32_t stride_lo;    /* GRID: smallest stride searched (>= 1)                     */
+  int32_t stride_hi;    /* GRID: largest stride searched (>= stride_lo, <= 4096)     */
+  int32_t grid_clip;    /* GRID: clip constant C of the line score (1..64; 0 -> 8)   */
+} mmsa_head_cfg;
+
+/* A run of tokens of one modality.  Segments must tile [0, L) in order. */
+typedef struct {
+  int64_t start, len;
+  int32_t modality;     /* MMSA_TEXT or MMSA_VIDEO */
+  int32_t _pad;
+} mmsa_segment;
+
+typedef struct {
+  int32_t B, Hq, Hkv, L, d;
+  int32_t _pad0;
+  int64_t q_strides[3], k_strides[3], v_strides[3], o_strides[3]; /* elements: batch, head, row */
+  float scale;                      /* softmax scale; 0 -> 1/sqrt(d)                 */
+  uint32_t flags;                   /* MMSA_FLAG_*                                   */
+  const int32_t* kv_head_of;        /* host [Hq] or NULL -> h / (Hq / Hkv)           */
+  const mmsa_head_cfg* heads;       /* host [Hq]                                     */
+  const mmsa_segment* segs;         /* host [n_segs]; NULL / 0 -> one text segment   */
+  int32_t n_segs;
+  int32_t _pad1;
+} mmsa_layer_desc;
+
+/* Bytes of device workspace the five calls need for this descriptor; 0 on an
+ * invalid descriptor (then mmsa_last_error() says why).  The workspace must be
+ * 256-byte aligned and is used by all five calls in sequence. */
+size_t mmsa_workspace_bytes(const mmsa_layer_desc* desc);
+
+/* Where a named intermediate of one (batch*Hq + head) `bh` lives in the
+ * workspace, so a caller can read it after the stream has drained.
+ * `part` selects the index set (0/1: query modality text/video for boundary
+ * heads; for 2D heads part = 2*query_modality + key_modality).  On success
+ * *offset_bytes and *count (elements) are set; a buffer that does not exist
+ * for that head gives count 0.  Buffers: */
+enum {
+  MMSA_BUF_V_SCORES = 0,   /* float[count]  vertical (column) scores                     */
+  MMSA_BUF_S_SCORES = 1,   /* float[count]  slash (diagonal) scores                      */
+  MMSA_BUF_V_INDEX = 2,    /* int32[count]  selected vertical indices, ascending         */
+  MMSA_BUF_S_INDEX = 3,    /* int32[count]  selected slash indices, ascending            */
+  MMSA_BUF_NSEL = 4,       /* int32[2]      number selected (vertical, slash)            */
+  MMSA_BUF_GRID = 5,       /* int32[2+w]    stride, w, then w ascending phases           */
+  MMSA_BUF_BLOCK_INDEX = 6,/* int32[nB*kb]  per query block, kb key blocks (-1 unused)   */
+  MMSA_BUF_BLOCK_SCORES = 7,/* float[nB*nB] pooled logits (only with EXPORT_SCORES)      */
+  MMSA_BUF_ROW_ORDER = 8,  /* int32[count]  original position of each permuted row, -1 pad */
+  MMSA_BUF_TILE_PAIRS = 9, /* int64[count]  selected (query, key) pairs per query tile    */
+  MMSA_BUF_TILE_WORK = 10, /* int32[count]  64x64 key tiles computed per query tile       */
+  MMSA_BUF_EST_STATS = 11, /* float[2*64*count] row max / row sum of the estimation rows  */
+  MMSA_BUF_SCORE_META = 12 /* int32[4]  vertical candidates [0,a), slash candidates [b,c), slash index shift */
+};
+mmsa_status mmsa_workspace_view(const mmsa_layer_desc* desc, int32_t buf, int32_t bh, int32_t part,
+                                int64_t* offset_bytes, int64_t* count);
+
+/* 1. Vertical-slash, boundary and grid estimation (MInference summary page,
+ *    "Approach": last-64-query attention for vertical/slash lines; MMInference
+ *    verdict page, key_machinery: grid stride and phase searched on the
+ *    approximate attention of the last 64 queries; pith_summary: index from the
+ *    last 64 queries of each modality segment).
+ *    q, k: device bf16 with the descriptor's strides.  No-op when no head needs it. */
+mmsa_status mmsa_estimate_vs(const mmsa_layer_desc* desc, const void* q, const void* k,
+                             void* ws, size_t ws_bytes, void* stream);
+
+/* 2. Block-sparse estimation: 64-row mean pooling of Q and K, pooled logits,
+ *    top-k key blocks per query block (MInference summary page, "Approach":
+ *    mean-pooled 64-block attention).  No-op when there is no BLOCK head. */
+mmsa_status mmsa_estimate_blocks(const mmsa_layer_desc* desc, const void* q, const void* k,
+                                 void* ws, size_t ws_bytes, void* stream);
+
+/* 3. Permutation and plan: row orders (grid: line rows first; boundary:
+ *    modality-grouped), gathered copies of permuted Q rows and grouped K/V, and
+ *    the per-query-tile list of key tiles and gathered key columns
+ *    (MMInference verdict page, core_discovery: row-wise, column-wise and 2D
+ *    permutations; key_machinery: kernels load only the permuted blocks). */
+mmsa_status mmsa_permute(const mmsa_layer_desc* desc, const void* q, const void* k, const void* v,
+                         void* ws, size_t ws_bytes, void* stream);
+
+/* 4. Block-sparse causal prefill over the planned tiles (MMInference verdict
+ *    page, key_machinery: block-sparse FlashAttention-style kernels that keep
+ *    matrix-core compute dense).  q, k, v as above; o: device bf16 [B,Hq,L,d]
+ *    with o_strides — rows of heads whose row order is the identity are written
+ *    here, the others go to the workspace until mmsa_unpermute.  lse: device
+ *    float [B,Hq,L] (contiguous) or NULL; natural-log sum of exp of the scaled
+ *    logits over the selected keys, -inf for a row with none. */
+mmsa_status mmsa_sparse_prefill(const mmsa_layer_desc* desc, const void* q, const void* k,
+                                const void* v, void* ws, size_t ws_bytes, void* o, float* lse,
+                                void* stream);
+
+/* 5. Inverse permutation: rows of permuted heads are scattered from the
+ *    workspace back to their original positions in o (MMInference verdict page,
+ *    core_discovery: the permutation leaves the model unchanged).  After this
+ *    call every row of o holds the attention output (0 for a row with no
+ *    selected key). */
+mmsa_status mmsa_unpermute(const mmsa_layer_desc* desc, void* ws, size_t ws_bytes, void* o,
+                           void* stream);
+
+const char* mmsa_status_string(mmsa_status s);
+const char* mmsa_last_error(void);
+int32_t mmsa_abi_version(void);
+
+#ifdef __cplusplus
+}
+#endif
+#endif /* MMSA_H */
