@@ -1,0 +1,183 @@
+// Block-sparse index estimation (MInference 1.0 summary page, "Approach":
+// mean-pooled 64-token block attention).  Q and K are mean-pooled per 64-row
+// block in fp32, the pooled logits z[b][c] = scale * Qp[b] . Kp[c] are formed
+// for c <= b, and each query block keeps its top-k key blocks (ties to the
+// lower block index, output ascending).  Ranking uses the pre-softmax logits:
+// a softmax is monotone within a row, so the selected set is the same.
+#include "mmsa_device.h"
+
+namespace mmsa {
+
+// grid (blocks, pool tasks), block 256.
+template <int D>
+__global__ __launch_bounds__(256) void k_pool(Dims dm, Tables tb, char* ws, const bf16_t* __restrict__ q,
+                                              const bf16_t* __restrict__ k) {
+  const PoolTask T = wsp<const PoolTask>(ws, tb.off_pool)[blockIdx.y];
+  const bf16_t* src = (T.is_k ? k : q) + T.src_off;
+  constexpr int CH = D / 8;            // 16-byte chunks per row
+  constexpr int RG = 256 / CH;         // row groups
+  constexpr int RPT = 64 / RG;         // rows per thread
+  __shared__ float part[RG][D];
+  const int b = blockIdx.x, tid = threadIdx.x;
+  const int rq = tid / CH, dc = tid % CH;
+  const int r_begin = b * 64, n = min(64, dm.L - r_begin);
+  float acc[8];
+#pragma unroll
+  for (int e = 0; e < 8; ++e) acc[e] = 0.f;
+#pragma unroll
+  for (int rr = 0; rr < RPT; ++rr) {
+    const int r = rq + RG * rr;
+    if (r < n) {
+      uint4 u = ld16(src + (int64_t)(r_begin + r) * T.row_stride + 8 * dc);
+      const uint32_t w4[4] = {u.x, u.y, u.z, u.w};
+#pragma unroll
+      for (int e = 0; e < 4; ++e) {
+        acc[2 * e] += __uint_as_float(w4[e] << 16);
+        acc[2 * e + 1] += __uint_as_float(w4[e] & 0xffff0000u);
+      }
+    }
+  }
+#pragma unroll
+  for (int e = 0; e < 8; ++e) part[rq][8 * dc + e] = acc[e];
+  __syncthreads();
+  if (tid < D) {
+    float s = 0.f;
+    for (int g = 0; g < RG; ++g) s += part[g][tid];
+    wsp<float>(ws, T.ws_dst)[(int64_t)b * D + tid] = s / (float)n;
+  }
+}
+
+// Lower-triangle 64x64 tiles of z.  grid (tiles, block heads), block 256.
+template <int D>
+__global__ __launch_bounds__(256) void k_block_logits(Dims dm, Tables tb, char* ws, int nB) {
+  const BlockTask T = wsp<const BlockTask>(ws, tb.off_block)[blockIdx.y];
+  const int r = blockIdx.x;
+  int bt = (int)((sqrtf(8.f * r + 1.f) - 1.f) * 0.5f);
+  while ((bt + 1) * (bt + 2) / 2 <= r) ++bt;
+  while (bt * (bt + 1) / 2 > r) --bt;
+  const int ct = r - bt * (bt + 1) / 2;
+  __shared__ float Qs[64][D + 1];
+  __shared__ float Ks[64][D + 1];
+  const float* qp = wsp<const float>(ws, T.ws_qp);
+  const float* kp = wsp<const float>(ws, T.ws_kp);
+  const int tid = threadIdx.x;
+  for (int i = tid; i < 64 * D; i += 256) {
+    const int rr = i / D, cc = i % D;
+    const int bq = 64 * bt + rr, bk = 64 * ct + rr;
+    Qs[rr][cc] = bq < nB ? qp[(int64_t)bq * D + cc] : 0.f;
+    Ks[rr][cc] = bk < nB ? kp[(int64_t)bk * D + cc] : 0.f;
+  }
+  __syncthreads();
+  const int ty = tid >> 4, tx = tid & 15;
+  float acc[4][4];
+#pragma unroll
+  for (int i = 0; i < 4; ++i)
+#pragma unroll
+    for (int j = 0; j < 4; ++j) acc[i][j] = 0.f;
+  for (int d = 0; d < D; ++d) {
+    float a[4], bv[4];
+#pragma unroll
+    for (int i = 0; i < 4; ++i) a[i] = Qs[4 * ty + i][d];
+#pragma unroll
+    for (int j = 0; j < 4; ++j) bv[j] = Ks[4 * tx + j][d];
+#pragma unroll
+    for (int i = 0; i < 4; ++i)
+#pragma unroll
+      for (int j = 0; j < 4; ++j) acc[i][j] = fmaf(a[i], bv[j], acc[i][j]);
+  }
+  float* z = wsp<float>(ws, T.ws_z);
+#pragma unroll
+  for (int i = 0; i < 4; ++i) {
+    const int b = 64 * bt + 4 * ty + i;
+#pragma unroll
+    for (int j = 0; j < 4; ++j) {
+      const int c = 64 * ct + 4 * tx + j;
+      if (b < nB && c <= b) z[(int64_t)b * nB + c] = acc[i][j] * dm.scale;
+    }
+  }
+}
+
+// Top-k key blocks of one query block from its LDS-resident logit row.
+// grid (query blocks, block heads), block 256, dynamic LDS nB floats.
+__global__ __launch_bounds__(256) void k_block_topk(Tables tb, char* ws, int nB) {
+  const BlockTask T = wsp<const BlockTask>(ws, tb.off_block)[blockIdx.y];
+  extern __shared__ float zs[];
+  __shared__ uint32_t hist[256];
+  __shared__ uint32_t sh_pref, sh_mask, sh_krem;
+  __shared__ int red[5];
+  const int b = blockIdx.x, tid = threadIdx.x;
+  const int n = b + 1;
+  const int k = min(T.kb, n);
+  const float* zrow = wsp<const float>(ws, T.ws_z) + (int64_t)b * nB;
+  for (int i = tid; i < n; i += 256) zs[i] = zrow[i];
+  int32_t* out = wsp<int32_t>(ws, T.ws_idx) + (int64_t)b * T.kb;
+  for (int i = k + tid; i < T.kb; i += 256) out[i] = -1;
+  __syncthreads();
+  uint32_t pref = 0, pmask = 0, krem = (uint32_t)k;
+  if (k < n) {
+    for (int shift = 24; shift >= 0; shift -= 8) {
+      hist[tid] = 0;
+      __syncthreads();
+      for (int i = tid; i < n; i += 256) {
+        const uint32_t key = order_key(zs[i]);
+        if ((key & pmask) == pref) atomicAdd(&hist[(key >> shift) & 255u], 1u);
+      }
+      __syncthreads();
+      if (tid == 0) {
+        uint32_t cum = 0;
+        int bb = 255;
+        for (; bb > 0; --bb) {
+          if (cum + hist[bb] >= krem) break;
+          cum += hist[bb];
+        }
+        sh_krem = krem - cum;
+        sh_pref = pref | ((uint32_t)bb << shift);
+        sh_mask = pmask | (255u << shift);
+      }
+      __syncthreads();
+      pref = sh_pref;
+      pmask = sh_mask;
+      krem = sh_krem;
+      __syncthreads();
+    }
+  } else {
+    pref = 0;
+    krem = (uint32_t)n;
+  }
+  const uint32_t thr = pref;
+  const int need = (int)krem;
+  int base = 0, eqb = 0;
+  for (int s0 = 0; s0 < n; s0 += 256) {
+    const int i = s0 + tid;
+    const bool in = i < n;
+    const uint32_t key = in ? order_key(zs[i]) : 0u;
+    const bool eq = in && key == thr, gt = in && key > thr;
+    int eq_tot, sel_tot;
+    const int eq_rank = eqb + block_excl_count(eq, red, &eq_tot);
+    const bool sel = gt || (eq && eq_rank < need);
+    const int r = base + block_excl_count(sel, red, &sel_tot);
+    if (sel) out[r] = i;
+    base += sel_tot;
+    eqb += eq_tot;
+  }
+}
+
+hipError_t launch_block_estimate(const Dims& dm, const Tables& tb, char* ws, const void* q, const void* k, int nB,
+                                 hipStream_t s) {
+  if (tb.n_block == 0) return hipSuccess;
+  const bf16_t* qq = (const bf16_t*)q;
+  const bf16_t* kk = (const bf16_t*)k;
+  const int nBt = (nB + 63) / 64;
+  const int ntri = nBt * (nBt + 1) / 2;
+  if (dm.d == 128) {
+    k_pool<128><<<dim3(nB, (unsigned)tb.n_pool), 256, 0, s>>>(dm, tb, ws, qq, kk);
+    k_block_logits<128><<<dim3(ntri, (unsigned)tb.n_block), 256, 0, s>>>(dm, tb, ws, nB);
+  } else {
+    k_pool<64><<<dim3(nB, (unsigned)tb.n_pool), 256, 0, s>>>(dm, tb, ws, qq, kk);
+    k_block_logits<64><<<dim3(ntri, (unsigned)tb.n_block), 256, 0, s>>>(dm, tb, ws, nB);
+  }
+  k_block_topk<<<dim3(nB, (unsigned)tb.n_block), 256, (size_t)nB * sizeof(float), s>>>(tb, ws, nB);
+  return hipGetLastError();
+}
+
+}  // namespace mmsa

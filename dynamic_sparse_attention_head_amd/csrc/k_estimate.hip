@@ -1,0 +1,524 @@
+// Online index estimation for vertical-slash, boundary and grid heads.
+//
+// Pages: MInference 1.0 summary page, "Approach" (vertical and slash lines
+// from the attention of the last 64 queries); MMInference verdict page,
+// key_machinery (grid stride and phase found by scanning an approximate
+// attention matrix of the last 64 queries) and pith_summary (index from the
+// last 64 queries of each modality segment).
+//
+// The attention of the estimation rows is exact: pass 1 streams K once for the
+// row max and the sum of exponentials, pass 2 streams K again and forms the
+// normalised probabilities, their column sums (vertical scores) and their
+// diagonal sums (slash scores).  Each workgroup takes 256 keys and every
+// estimation region of its KV head, so K is read twice in total.  QK^T uses
+// bf16 MFMA with fp32 accumulation.  Diagonal sums cross workgroups; they are
+// added as 2^-40 fixed-point integers, so the result does not depend on the
+// order in which workgroups finish.
+#include "mmsa_device.h"
+
+namespace mmsa {
+
+// ---------------------------------------------------------------------------
+// Fragments of 64 keys x D dims of K for the A operand (rows = keys).
+// ---------------------------------------------------------------------------
+template <int D>
+__device__ __forceinline__ void load_k_frags(bf16x8 (&kf)[4][D / 32], const bf16_t* __restrict__ kbase,
+                                             int64_t k_sl, const int* kpos, int lane) {
+  const int qc = lane & 15, g4 = lane >> 4;
+#pragma unroll
+  for (int kb = 0; kb < 4; ++kb) {
+    int p = kpos[kb];
+#pragma unroll
+    for (int c = 0; c < D / 32; ++c) {
+      uint4 u = make_uint4(0, 0, 0, 0);
+      if (p >= 0) u = ld16(kbase + (int64_t)p * k_sl + 32 * c + 8 * g4);
+      kf[kb][c] = as_bf16x8(u);
+    }
+  }
+  (void)qc;
+}
+
+template <int D>
+__device__ __forceinline__ void load_q_frag(bf16x8 (&qf)[D / 32], const bf16_t* __restrict__ qbase, int64_t q_sl,
+                                            int pos, int lane) {
+  const int g4 = lane >> 4;
+#pragma unroll
+  for (int c = 0; c < D / 32; ++c) {
+    uint4 u = make_uint4(0, 0, 0, 0);
+    if (pos >= 0) u = ld16(qbase + (int64_t)pos * q_sl + 32 * c + 8 * g4);
+    qf[c] = as_bf16x8(u);
+  }
+}
+
+// ---------------------------------------------------------------------------
+// Pass 1: partial (max, sum of exp2) of each estimation row over 256 keys.
+// grid (chunks of 256 keys, pass-1 groups), block 256 = 4 waves x 64 keys.
+// ---------------------------------------------------------------------------
+template <int D>
+__global__ __launch_bounds__(256) void k_est_pass1(Dims dm, Tables tb, char* ws, const bf16_t* __restrict__ q,
+                                                   const bf16_t* __restrict__ k) {
+  const EstGroup G = wsp<const EstGroup>(ws, tb.off_groups1)[blockIdx.y];
+  const EstJob* jobs = wsp<const EstJob>(ws, tb.off_jobs);
+  const int j0 = blockIdx.x * EST_CK;
+  const int tid = threadIdx.x, w = tid >> 6, lane = tid & 63, qc = lane & 15, g4 = lane >> 4;
+  int gimax = -1;
+  for (int jb = G.job_begin; jb < G.job_end; ++jb) gimax = max(gimax, jobs[jb].imax);
+  if (j0 > gimax) return;   // no estimation row sees these keys (their partials are never read)
+
+  int kp[4];
+#pragma unroll
+  for (int kb = 0; kb < 4; ++kb) {
+    int key = j0 + 64 * w + 16 * kb + qc;
+    kp[kb] = key < dm.L ? key : -1;
+  }
+  bf16x8 kf[4][D / 32];
+  load_k_frags<D>(kf, k + G.k_off, dm.k_sl, kp, lane);
+
+  __shared__ float2 red[2][4][64];
+  int it = 0;
+  for (int jb = G.job_begin; jb < G.job_end; ++jb, ++it) {
+    const EstJob& J = jobs[jb];
+    const int par = it & 1;
+#pragma unroll
+    for (int qb = 0; qb < 4; ++qb) {
+      const int row = 16 * qb + qc;
+      const bool rv = row < J.n_rows;
+      const int pos = rv ? J.rows[row] : -1;
+      bf16x8 qf[D / 32];
+      load_q_frag<D>(qf, q + J.q_off, dm.q_sl, pos, lane);
+      float xs[16];
+      float mx = -INFINITY;
+#pragma unroll
+      for (int kb = 0; kb < 4; ++kb) {
+        floatx4 acc = {0.f, 0.f, 0.f, 0.f};
+#pragma unroll
+        for (int c = 0; c < D / 32; ++c) acc = mfma16(kf[kb][c], qf[c], acc);
+#pragma unroll
+        for (int i = 0; i < 4; ++i) {
+          const int key = j0 + 64 * w + 16 * kb + 4 * g4 + i;
+          const float x = (rv && key <= pos) ? acc[i] * dm.scale_log2 : -INFINITY;
+          xs[4 * kb + i] = x;
+          mx = fmaxf(mx, x);
+        }
+      }
+      float sm = 0.f;
+      if (mx != -INFINITY) {
+#pragma unroll
+        for (int e = 0; e < 16; ++e) sm += exp2f(xs[e] - mx);
+      }
+      float2 st = make_float2(mx, sm);
+#pragma unroll
+      for (int m = 16; m <= 32; m <<= 1) {
+        float2 o = make_float2(shfl_xor_f(st.x, m), shfl_xor_f(st.y, m));
+        st = lse2_merge(st, o);
+      }
+      if (g4 == 0) red[par][w][row] = st;
+    }
+    __syncthreads();
+    if (tid < 64) {
+      float2 st = red[par][0][tid];
+#pragma unroll
+      for (int ww = 1; ww < 4; ++ww) st = lse2_merge(st, red[par][ww][tid]);
+      wsp<float2>(ws, J.ws_part)[(int64_t)blockIdx.x * 64 + tid] = st;
+    }
+  }
+}
+
+// Final (max, sum) per estimation row, merging chunk partials in order.
+__global__ __launch_bounds__(64) void k_est_combine(Tables tb, char* ws) {
+  const EstJob& J = wsp<const EstJob>(ws, tb.off_jobs)[blockIdx.x];
+  const int r = threadIdx.x;
+  const float2* part = wsp<const float2>(ws, J.ws_part);
+  const int last = J.imax / EST_CK + 1;
+  float2 st = make_float2(-INFINITY, 0.f);
+  for (int c = 0; c < last; ++c) st = lse2_merge(st, part[(int64_t)c * 64 + r]);
+  wsp<float2>(ws, J.ws_stats)[r] = st;
+}
+
+// ---------------------------------------------------------------------------
+// Pass 2: probabilities, column sums (v) and diagonal sums (s).
+// grid (chunks of 256 view slots, pass-2 groups), block 256.
+// ---------------------------------------------------------------------------
+template <int D>
+__global__ __launch_bounds__(256) void k_est_pass2(Dims dm, Tables tb, char* ws, const bf16_t* __restrict__ q,
+                                                   const bf16_t* __restrict__ k) {
+  const EstGroup G = wsp<const EstGroup>(ws, tb.off_groups2)[blockIdx.y];
+  const EstJob* jobs = wsp<const EstJob>(ws, tb.off_jobs);
+  const int x0 = blockIdx.x * EST_CK;
+  if (x0 >= G.n_keys) return;
+  const int tid = threadIdx.x, w = tid >> 6, lane = tid & 63, qc = lane & 15, g4 = lane >> 4;
+
+  __shared__ int kp_s[EST_CK];
+  __shared__ float P[EST_ROWS][EST_CK + 4];
+  {
+    const int slot = x0 + tid;
+    int pos;
+    if (G.view == VIEW_IDENTITY) pos = slot < dm.L ? slot : -1;
+    else pos = wsp<const int32_t>(ws, dm.ws_pgrp)[slot];
+    kp_s[tid] = pos;
+  }
+  __syncthreads();
+  int kmin = 0x7fffffff;
+  {
+    // smallest key position of the chunk: skip jobs whose rows see none of it
+    int mine = kp_s[tid] >= 0 ? kp_s[tid] : 0x7fffffff;
+    for (int m = 1; m < 64; m <<= 1) mine = min(mine, __shfl_xor(mine, m, 64));
+    __shared__ int wmin[4];
+    if (lane == 0) wmin[w] = mine;
+    __syncthreads();
+    kmin = min(min(wmin[0], wmin[1]), min(wmin[2], wmin[3]));
+  }
+  int kp[4];
+#pragma unroll
+  for (int kb = 0; kb < 4; ++kb) kp[kb] = kp_s[64 * w + 16 * kb + qc];
+  bf16x8 kf[4][D / 32];
+  load_k_frags<D>(kf, k + G.k_off, dm.k_sl, kp, lane);
+
+  const int m_chunk = (G.view == VIEW_GROUPED && x0 >= dm.video_base) ? MMSA_VIDEO : MMSA_TEXT;
+  const int chunk_base = (m_chunk == MMSA_VIDEO) ? dm.video_base : dm.text_base;
+
+  for (int jb = G.job_begin; jb < G.job_end; ++jb) {
+    const EstJob& J = jobs[jb];
+    if (J.imax < kmin) continue;   // uniform
+    const float2* stats = wsp<const float2>(ws, J.ws_stats);
+#pragma unroll
+    for (int qb = 0; qb < 4; ++qb) {
+      const int row = 16 * qb + qc;
+      const bool rv = row < J.n_rows;
+      const int pos = rv ? J.rows[row] : -1;
+      const float2 st = stats[row];
+      const float inv_l = (rv && st.y > 0.f) ? 1.0f / st.y : 0.f;
+      bf16x8 qf[D / 32];
+      load_q_frag<D>(qf, q + J.q_off, dm.q_sl, pos, lane);
+#pragma unroll
+      for (int kb = 0; kb < 4; ++kb) {
+        floatx4 acc = {0.f, 0.f, 0.f, 0.f};
+#pragma unroll
+        for (int c = 0; c < D / 32; ++c) acc = mfma16(kf[kb][c], qf[c], acc);
+        const int4 kq = *reinterpret_cast<const int4*>(&kp_s[64 * w + 16 * kb + 4 * g4]);
+        const int kk[4] = {kq.x, kq.y, kq.z, kq.w};
+        float4 pv;
+        float* pp = reinterpret_cast<float*>(&pv);
+#pragma unroll
+        for (int i = 0; i < 4; ++i) {
+          const bool valid = rv && kk[i] >= 0 && kk[i] <= pos;
+          pp[i] = valid ? exp2f(acc[i] * dm.scale_log2 - st.x) * inv_l : 0.f;
+        }
+        *reinterpret_cast<float4*>(&P[row][64 * w + 16 * kb + 4 * g4]) = pv;
+      }
+    }
+    __syncthreads();
+
+    // column sums -> vertical scores (or grid line scores)
+    {
+      const int kpos = kp_s[tid];
+      if (kpos >= 0 && kpos <= J.imax) {
+        float sum = 0.f;
+        for (int r = 0; r < J.n_rows; ++r) sum += P[r][tid];
+        const int slot = x0 + tid;
+        if (J.kind == JOB_VS_ORIG || J.kind == JOB_GRID_PLAIN) {
+          wsp<float>(ws, J.pair[0].ws_v)[kpos] = sum;
+        } else if (J.kind == JOB_GRID_GROUPED) {
+          const int xg = (slot < dm.video_base) ? slot : dm.n_text + (slot - dm.video_base);
+          wsp<float>(ws, J.pair[0].ws_v)[xg] = sum;
+        } else {
+          const int pi = (J.pair[0].m_k == m_chunk) ? 0 : 1;
+          wsp<float>(ws, J.pair[pi].ws_v)[slot - chunk_base] = sum;
+        }
+      }
+    }
+    // diagonal sums -> slash scores
+    if (J.kind == JOB_VS_ORIG || J.kind == JOB_VS_2D) {
+      const int pi = (J.kind == JOB_VS_2D && J.pair[0].m_k != m_chunk) ? 1 : 0;
+      const PairDev& Pd = J.pair[pi];
+      unsigned long long* sacc = wsp<unsigned long long>(ws, Pd.ws_sacc);
+      const int n_runs = (J.kind == JOB_VS_2D) ? 1 : J.n_runs;
+      for (int ru = 0; ru < n_runs; ++ru) {
+        int r0, len, A;
+        if (J.kind == JOB_VS_2D) {
+          r0 = 0;
+          len = J.n_rows;
+          A = J.rho0 + Pd.n_k - 1 - (x0 - chunk_base);
+        } else {
+          r0 = J.run_r0[ru];
+          len = J.run_len[ru];
+          A = J.rows[r0] - r0 - x0;
+        }
+        const int span = len + EST_CK - 1;
+        const int idx_lo = A + r0 - (EST_CK - 1);
+        for (int ii = tid; ii < span; ii += 256) {
+          const int idx = idx_lo + ii;
+          if (idx < 0 || idx >= Pd.Ds) continue;
+          const int rlo = max(r0, idx - A), rhi = min(r0 + len, idx - A + EST_CK);
+          float sum = 0.f;
+          for (int r = rlo; r < rhi; ++r) sum += P[r][A + r - idx];
+          if (sum != 0.f) atomicAdd(&sacc[idx], (unsigned long long)llrint((double)sum * SFIX));
+        }
+      }
+    }
+    __syncthreads();
+  }
+}
+
+// Fixed-point slash sums -> float32 scores.
+__global__ __launch_bounds__(256) void k_s_finalize(Tables tb, char* ws) {
+  const EstJob& J = wsp<const EstJob>(ws, tb.off_jobs)[blockIdx.y >> 1];
+  const int pi = blockIdx.y & 1;
+  if (!(J.kind == JOB_VS_ORIG || J.kind == JOB_VS_2D) || pi >= J.n_pairs) return;
+  const PairDev& Pd = J.pair[pi];
+  const long long* sacc = wsp<const long long>(ws, Pd.ws_sacc);
+  float* s = wsp<float>(ws, Pd.ws_s);
+  for (int i = blockIdx.x * 256 + threadIdx.x; i < Pd.Ds; i += gridDim.x * 256)
+    s[i] = (float)((double)sacc[i] * (1.0 / SFIX));
+}
+
+// ---------------------------------------------------------------------------
+// Exact top-k of a float32 vector over [lo, hi): value descending, ties to
+// the lowest index, output ascending.  Radix select on the 32-bit orderable
+// key (4 rounds of 8 bits), then one compaction pass in index order.
+// grid (tasks), block 1024.
+// ---------------------------------------------------------------------------
+__global__ __launch_bounds__(1024) void k_topk(Tables tb, char* ws) {
+  const TopkTask T = wsp<const TopkTask>(ws, tb.off_topk)[blockIdx.x];
+  const float* __restrict__ x = wsp<const float>(ws, T.ws_x);
+  int32_t* out = wsp<int32_t>(ws, T.ws_out);
+  const int tid = threadIdx.x, nthr = blockDim.x;
+  const int lo = T.lo, hi = T.hi, n = hi - lo;
+  const int k = min(T.k, n);
+  __shared__ uint32_t hist[256];
+  __shared__ uint32_t sh_pref, sh_mask, sh_krem;
+  __shared__ int red[17];
+  if (k <= 0) {
+    if (tid == 0) *wsp<int32_t>(ws, T.ws_cnt) = 0;
+    return;
+  }
+  uint32_t pref = 0, pmask = 0, krem = (uint32_t)k;
+  if (k < n) {
+    for (int shift = 24; shift >= 0; shift -= 8) {
+      for (int i = tid; i < 256; i += nthr) hist[i] = 0;
+      __syncthreads();
+      for (int i = lo + tid; i < hi; i += nthr) {
+        const uint32_t key = order_key(x[i]);
+        if ((key & pmask) == pref) atomicAdd(&hist[(key >> shift) & 255u], 1u);
+      }
+      __syncthreads();
+      if (tid == 0) {
+        uint32_t cum = 0;
+        int b = 255;
+        for (; b > 0; --b) {
+          if (cum + hist[b] >= krem) break;
+          cum += hist[b];
+        }
+        sh_krem = krem - cum;
+        sh_pref = pref | ((uint32_t)b << shift);
+        sh_mask = pmask | (255u << shift);
+      }
+      __syncthreads();
+      pref = sh_pref;
+      pmask = sh_mask;
+      krem = sh_krem;
+      __syncthreads();
+    }
+  } else {
+    pref = 0;
+    krem = (uint32_t)n;
+  }
+  const uint32_t thr = pref;
+  const int need = (int)krem;
+  int base = 0, eqb = 0;
+  for (int s0 = lo; s0 < hi; s0 += nthr) {
+    const int i = s0 + tid;
+    const bool in = i < hi;
+    const uint32_t key = in ? order_key(x[i]) : 0u;
+    const bool eq = in && key == thr;
+    const bool gt = in && key > thr;
+    int eq_tot, sel_tot;
+    const int eq_rank = eqb + block_excl_count(eq, red, &eq_tot);
+    const bool sel = gt || (eq && eq_rank < need);
+    const int r = base + block_excl_count(sel, red, &sel_tot);
+    if (sel) out[r] = i;
+    base += sel_tot;
+    eqb += eq_tot;
+  }
+  if (tid == 0) *wsp<int32_t>(ws, T.ws_cnt) = base;
+}
+
+// ---------------------------------------------------------------------------
+// Grid stride / phase rule on clipped fixed-point line scores.
+// ---------------------------------------------------------------------------
+__device__ __forceinline__ int64_t grid_u(float v, int64_t cap) {
+  const int64_t u = (int64_t)floorf(v * 16777216.0f);
+  return u < cap ? u : cap;
+}
+
+__global__ __launch_bounds__(1024) void k_grid_sum(Tables tb, char* ws) {
+  const GridTask T = wsp<const GridTask>(ws, tb.off_grid)[blockIdx.x];
+  const float* v = wsp<const float>(ws, T.ws_v);
+  __shared__ long long part[1024];
+  long long s = 0;
+  for (int x = threadIdx.x; x < T.D; x += blockDim.x) s += grid_u(v[x], T.cap);
+  part[threadIdx.x] = s;
+  __syncthreads();
+  for (int st = 512; st > 0; st >>= 1) {
+    if ((int)threadIdx.x < st) part[threadIdx.x] += part[threadIdx.x + st];
+    __syncthreads();
+  }
+  if (threadIdx.x == 0) *wsp<long long>(ws, T.ws_U) = part[0];
+}
+
+struct GridCand {
+  long long X;
+  int cnt, phase;
+};
+
+// +1 if candidate a beats b (higher score; on a tie the smaller phase).
+__device__ __forceinline__ bool grid_better(const GridCand& a, const GridCand& b) {
+  if (a.phase < 0) return false;
+  if (b.phase < 0) return true;
+  const int c = grid_cmp(a.X, a.cnt, b.X, b.cnt);
+  return c > 0 || (c == 0 && a.phase < b.phase);
+}
+
+// grid (strides, grid tasks), block 1024: the best phases at one stride.
+__global__ __launch_bounds__(1024) void k_grid_scan(Tables tb, char* ws) {
+  const GridTask T = wsp<const GridTask>(ws, tb.off_grid)[blockIdx.y];
+  const int sig = T.s_lo + blockIdx.x;
+  if (sig > T.s_hi) return;
+  const float* v = wsp<const float>(ws, T.ws_v);
+  const long long U = *wsp<const long long>(ws, T.ws_U);
+  __shared__ GridCand c[MAX_STRIDE];
+  __shared__ int idx[MAX_STRIDE];
+  const int f = threadIdx.x;
+  GridCand me{0, 0, -1};
+  if (f < sig) {
+    long long F = 0;
+    for (int x = f; x < T.D; x += sig) F += grid_u(v[x], T.cap);
+    const int cnt = (T.D - f + sig - 1) / sig;
+    me.X = (long long)T.D * F - (long long)cnt * U;
+    me.cnt = cnt;
+    me.phase = f;
+  }
+  c[f] = me;
+  const int w = min(T.w, sig);
+  GridCand* outc = wsp<GridCand>(ws, T.ws_cand) + (int64_t)blockIdx.x * MAX_PHASES;
+  for (int round = 0; round < w; ++round) {
+    idx[f] = f;
+    __syncthreads();
+    for (int st = MAX_STRIDE / 2; st > 0; st >>= 1) {
+      if (f < st) {
+        const int a = idx[f], b = idx[f + st];
+        idx[f] = grid_better(c[b], c[a]) ? b : a;
+      }
+      __syncthreads();
+    }
+    const int win = idx[0];
+    if (f == 0) outc[round] = c[win];
+    __syncthreads();
+    if (f == win) c[f].phase = -1;
+    __syncthreads();
+  }
+}
+
+// grid (grid tasks), block 512: the winning stride and its phases.
+__global__ __launch_bounds__(512) void k_grid_select(Tables tb, char* ws) {
+  const GridTask T = wsp<const GridTask>(ws, tb.off_grid)[blockIdx.x];
+  const GridCand* cand = wsp<const GridCand>(ws, T.ws_cand);
+  const int ns = T.s_hi - T.s_lo + 1;
+  __shared__ GridCand bc[512];
+  __shared__ int bs[512];
+  GridCand me{0, 0, -1};
+  int msig = -1;
+  for (int i = threadIdx.x; i < ns; i += 512) {   // ascending strides: strict improvement only
+    const GridCand c = cand[(int64_t)i * MAX_PHASES];
+    if (msig < 0 || grid_cmp(c.X, c.cnt, me.X, me.cnt) > 0) {
+      me = c;
+      msig = T.s_lo + i;
+    }
+  }
+  bc[threadIdx.x] = me;
+  bs[threadIdx.x] = msig;
+  __syncthreads();
+  for (int st = 256; st > 0; st >>= 1) {
+    const int t = threadIdx.x;
+    if (t < st) {
+      const int sa = bs[t], sb = bs[t + st];
+      bool take_b = false;
+      if (sb >= 0) {
+        if (sa < 0) take_b = true;
+        else {
+          const int cmpv = grid_cmp(bc[t + st].X, bc[t + st].cnt, bc[t].X, bc[t].cnt);
+          take_b = cmpv > 0 || (cmpv == 0 && sb < sa);
+        }
+      }
+      if (take_b) {
+        bc[t] = bc[t + st];
+        bs[t] = sb;
+      }
+    }
+    __syncthreads();
+  }
+  if (threadIdx.x == 0) {
+    const int sig = bs[0];
+    const int w = min(T.w, sig);
+    int32_t* out = wsp<int32_t>(ws, T.ws_out);
+    int ph[MAX_PHASES];
+    const GridCand* cs = cand + (int64_t)(sig - T.s_lo) * MAX_PHASES;
+    for (int i = 0; i < w; ++i) ph[i] = cs[i].phase;
+    for (int i = 1; i < w; ++i)
+      for (int j = i; j > 0 && ph[j - 1] > ph[j]; --j) {
+        int t = ph[j];
+        ph[j] = ph[j - 1];
+        ph[j - 1] = t;
+      }
+    out[0] = sig;
+    out[1] = w;
+    for (int i = 0; i < w; ++i) out[3 + i] = ph[i];
+  }
+}
+
+// ---------------------------------------------------------------------------
+// Launchers
+// ---------------------------------------------------------------------------
+hipError_t launch_est_pass1(const Dims& dm, const Tables& tb, char* ws, const void* q, const void* k,
+                            int n_chunks1, hipStream_t s) {
+  if (tb.n_groups1 == 0) return hipSuccess;
+  dim3 grid(n_chunks1, (unsigned)tb.n_groups1);
+  if (dm.d == 128)
+    k_est_pass1<128><<<grid, 256, 0, s>>>(dm, tb, ws, (const bf16_t*)q, (const bf16_t*)k);
+  else
+    k_est_pass1<64><<<grid, 256, 0, s>>>(dm, tb, ws, (const bf16_t*)q, (const bf16_t*)k);
+  k_est_combine<<<(unsigned)tb.n_jobs, 64, 0, s>>>(tb, ws);
+  return hipGetLastError();
+}
+
+hipError_t launch_est_pass2(const Dims& dm, const Tables& tb, char* ws, const void* q, const void* k,
+                            int n_chunks2, int max_ds, hipStream_t s) {
+  if (tb.n_groups2 == 0) return hipSuccess;
+  dim3 grid(n_chunks2, (unsigned)tb.n_groups2);
+  if (dm.d == 128)
+    k_est_pass2<128><<<grid, 256, 0, s>>>(dm, tb, ws, (const bf16_t*)q, (const bf16_t*)k);
+  else
+    k_est_pass2<64><<<grid, 256, 0, s>>>(dm, tb, ws, (const bf16_t*)q, (const bf16_t*)k);
+  if (max_ds > 0) {
+    dim3 g2((unsigned)min(64, (max_ds + 255) / 256), (unsigned)(2 * tb.n_jobs));
+    k_s_finalize<<<g2, 256, 0, s>>>(tb, ws);
+  }
+  return hipGetLastError();
+}
+
+hipError_t launch_topk(const Tables& tb, char* ws, hipStream_t s) {
+  if (tb.n_topk == 0) return hipSuccess;
+  k_topk<<<(unsigned)tb.n_topk, 1024, 0, s>>>(tb, ws);
+  return hipGetLastError();
+}
+
+hipError_t launch_grid(const Dims& dm, const Tables& tb, char* ws, int max_strides, hipStream_t s) {
+  (void)dm;
+  if (tb.n_grid == 0) return hipSuccess;
+  k_grid_sum<<<(unsigned)tb.n_grid, 1024, 0, s>>>(tb, ws);
+  k_grid_scan<<<dim3(max_strides, (unsigned)tb.n_grid), MAX_STRIDE, 0, s>>>(tb, ws);
+  k_grid_select<<<(unsigned)tb.n_grid, 512, 0, s>>>(tb, ws);
+  return hipGetLastError();
+}
+
+}  // namespace mmsa

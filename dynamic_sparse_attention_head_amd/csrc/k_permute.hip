@@ -1,0 +1,485 @@
+// Modality-aware permutation and the per-query-tile sparse plan.
+//
+// Pages: MMInference verdict page, core_discovery (row-wise permutation
+// grouping same-modality queries, column-wise permutation aligning key
+// strides, 2D permutation isolating each modality pair) and key_machinery
+// (tensors permuted so grid lines become contiguous; kernels load only the
+// permuted blocks).
+//
+// Row orders:  grid heads put their line rows first (x mod stride in the kept
+// phases), then the other rows, each group ascending and padded to 64;
+// boundary heads use the modality-grouped order (text, then video, each
+// ascending and padded to 256).  Grid key lines are the same positions, so the
+// first rows of a grid head's row order are also its gathered key list.
+//
+// The plan of one query tile is a bitmap over the 64-key tiles of the head's
+// key view (identity, or modality-grouped for 2D-boundary heads) plus a list of
+// gathered key positions that no listed tile holds, the exact number of
+// selected (query, key) pairs, and a cost (tiles + gathered chunks) used to
+// order the attention work queue from most to least expensive.
+#include "mmsa_device.h"
+
+namespace mmsa {
+
+__global__ __launch_bounds__(256) void k_fill_u32(uint32_t* p, uint32_t value, int64_t n) {
+  for (int64_t i = blockIdx.x * 256ll + threadIdx.x; i < n; i += (int64_t)gridDim.x * 256) p[i] = value;
+}
+
+hipError_t launch_fill_u32(void* p, uint32_t value, int64_t n_words, hipStream_t s) {
+  if (n_words <= 0) return hipSuccess;
+  int64_t blocks = (n_words + 255) / 256;
+  if (blocks > 65536) blocks = 65536;
+  k_fill_u32<<<(unsigned)blocks, 256, 0, s>>>((uint32_t*)p, value, n_words);
+  return hipGetLastError();
+}
+
+// Modality, rank and grouped slot of every position.  grid (L/256), block 256.
+__global__ __launch_bounds__(256) void k_seg_tables(Dims dm, Tables tb, char* ws) {
+  const int p = blockIdx.x * 256 + threadIdx.x;
+  if (p >= dm.L) return;
+  const SegDev* segs = wsp<const SegDev>(ws, tb.off_segs);
+  int lo = 0, hi = (int)tb.n_segs - 1;
+  while (lo < hi) {
+    const int mid = (lo + hi + 1) >> 1;
+    if (segs[mid].start <= p) lo = mid;
+    else hi = mid - 1;
+  }
+  const SegDev sg = segs[lo];
+  const int rank = sg.rank_start + (int)(p - sg.start);
+  const int slot = (sg.modality == MMSA_VIDEO ? dm.video_base : dm.text_base) + rank;
+  wsp<int32_t>(ws, dm.ws_gslot)[p] = slot;
+  wsp<int32_t>(ws, dm.ws_pgrp)[slot] = p;
+}
+
+hipError_t launch_seg_tables(const Dims& dm, const Tables& tb, char* ws, hipStream_t s) {
+  hipError_t e = launch_fill_u32(ws + dm.ws_pgrp, 0xffffffffu, dm.L_grp, s);
+  if (e != hipSuccess) return e;
+  if (dm.L > 0) k_seg_tables<<<(dm.L + 255) / 256, 256, 0, s>>>(dm, tb, ws);
+  return hipGetLastError();
+}
+
+// ---------------------------------------------------------------------------
+// Grid row orders.  cl(y) = number of grid-line coordinates in [0, y).
+// ---------------------------------------------------------------------------
+struct GridLines {
+  int sig, w, ph[MAX_PHASES];
+};
+
+__device__ __forceinline__ GridLines load_lines(const int32_t* out) {
+  // clamped so that a result never written (calls out of order) stays harmless
+  GridLines g;
+  g.sig = max(out[0], 1);
+  g.w = min(max(out[1], 0), min(MAX_PHASES, g.sig));
+#pragma unroll
+  for (int i = 0; i < MAX_PHASES; ++i) g.ph[i] = (i < g.w) ? min(max(out[3 + i], 0), g.sig - 1) : 0;
+  return g;
+}
+__device__ __forceinline__ int lines_below(const GridLines& g, int y) {
+  int c = 0;
+  for (int i = 0; i < g.w; ++i) c += (y > g.ph[i]) ? (y - g.ph[i] + g.sig - 1) / g.sig : 0;
+  return c;
+}
+__device__ __forceinline__ bool on_line(const GridLines& g, int x) {
+  const int r = x % g.sig;
+  bool on = false;
+  for (int i = 0; i < g.w; ++i) on |= (r == g.ph[i]);
+  return on;
+}
+
+// grid (L/256, grid tasks), block 256.
+__global__ __launch_bounds__(256) void k_grid_rows(Dims dm, Tables tb, char* ws) {
+  const GridTask T = wsp<const GridTask>(ws, tb.off_grid)[blockIdx.y];
+  const HeadDev& H = wsp<const HeadDev>(ws, tb.off_heads)[T.bh];
+  int32_t* gout = wsp<int32_t>(ws, T.ws_out);
+  const GridLines gl = load_lines(gout);
+  const int n_line = lines_below(gl, dm.L);
+  const int nl_pad = (n_line + 63) & ~63;
+  const int p = blockIdx.x * 256 + threadIdx.x;
+  if (blockIdx.x == 0 && threadIdx.x == 0) gout[2] = n_line;
+  if (p >= dm.L) return;
+  int x, prefix;
+  if (T.grouped) {
+    const int slot = wsp<const int32_t>(ws, dm.ws_gslot)[p];
+    const bool vid = slot >= dm.video_base && dm.n_video > 0 && (dm.video_base > 0 || dm.n_text == 0);
+    const int rank = vid ? slot - dm.video_base : slot - dm.text_base;
+    x = vid ? dm.n_text + rank : rank;
+    const int kt = vid ? p - rank : rank;      // text positions before p
+    const int kv = p - kt;                      // video positions before p
+    prefix = lines_below(gl, kt) + lines_below(gl, dm.n_text + kv) - lines_below(gl, dm.n_text);
+  } else {
+    x = p;
+    prefix = lines_below(gl, p);
+  }
+  const int slot = on_line(gl, x) ? prefix : nl_pad + (p - prefix);
+  if (slot >= 0 && slot < H.n_row_slots) wsp<int32_t>(ws, H.ws_row_order)[slot] = p;
+}
+
+hipError_t launch_grid_rows(const Dims& dm, const Tables& tb, char* ws, hipStream_t s) {
+  if (tb.n_grid == 0 || dm.L == 0) return hipSuccess;
+  k_grid_rows<<<dim3((dm.L + 255) / 256, (unsigned)tb.n_grid), 256, 0, s>>>(dm, tb, ws);
+  return hipGetLastError();
+}
+
+// ---------------------------------------------------------------------------
+// Row gathers (Q of permuted heads, grouped K/V) and the output scatter.
+// grid (slots*chunks/256, tasks), block 256; one thread moves 16 bytes.
+// ---------------------------------------------------------------------------
+__global__ __launch_bounds__(256) void k_gather(Dims dm, Tables tb, char* ws, const bf16_t* __restrict__ q,
+                                                const bf16_t* __restrict__ k, const bf16_t* __restrict__ v) {
+  const GatherTask T = wsp<const GatherTask>(ws, tb.off_gather)[blockIdx.y];
+  const int CH = dm.d / 8;
+  const int64_t idx = (int64_t)blockIdx.x * 256 + threadIdx.x;
+  const int slot = (int)(idx / CH), ch = (int)(idx % CH);
+  if (slot >= T.n_slots) return;
+  const bf16_t* src = (T.which == 0 ? q : T.which == 1 ? k : v) + T.src_off;
+  const int row = wsp<const int32_t>(ws, T.ws_rows)[slot];
+  uint4 val = make_uint4(0, 0, 0, 0);
+  if (row >= 0) val = ld16(src + (int64_t)row * T.row_stride + 8 * ch);
+  st16(wsp<bf16_t>(ws, T.ws_dst) + (int64_t)slot * dm.d + 8 * ch, val);
+}
+
+hipError_t launch_gather(const Dims& dm, const Tables& tb, char* ws, const void* q, const void* k, const void* v,
+                         int max_slots, hipStream_t s) {
+  if (tb.n_gather == 0) return hipSuccess;
+  const int64_t n = (int64_t)max_slots * (dm.d / 8);
+  k_gather<<<dim3((unsigned)((n + 255) / 256), (unsigned)tb.n_gather), 256, 0, s>>>(
+      dm, tb, ws, (const bf16_t*)q, (const bf16_t*)k, (const bf16_t*)v);
+  return hipGetLastError();
+}
+
+__global__ __launch_bounds__(256) void k_unpermute(Dims dm, Tables tb, char* ws, bf16_t* __restrict__ o) {
+  const UnpermTask T = wsp<const UnpermTask>(ws, tb.off_unperm)[blockIdx.y];
+  const int CH = dm.d / 8;
+  const int64_t idx = (int64_t)blockIdx.x * 256 + threadIdx.x;
+  const int slot = (int)(idx / CH), ch = (int)(idx % CH);
+  if (slot >= T.n_slots) return;
+  const int row = wsp<const int32_t>(ws, T.ws_rows)[slot];
+  if (row < 0) return;
+  const uint4 val = ld16(wsp<const bf16_t>(ws, T.ws_src) + (int64_t)slot * dm.d + 8 * ch);
+  st16(o + T.o_off + (int64_t)row * dm.o_sl + 8 * ch, val);
+}
+
+hipError_t launch_unpermute(const Dims& dm, const Tables& tb, char* ws, void* o, int max_slots, hipStream_t s) {
+  if (tb.n_unperm == 0) return hipSuccess;
+  const int64_t n = (int64_t)max_slots * (dm.d / 8);
+  k_unpermute<<<dim3((unsigned)((n + 255) / 256), (unsigned)tb.n_unperm), 256, 0, s>>>(dm, tb, ws, (bf16_t*)o);
+  return hipGetLastError();
+}
+
+// ---------------------------------------------------------------------------
+// Plan compile: one workgroup per (head, query tile).
+// grid (max query tiles, heads), block 256, dynamic LDS = bitmap words.
+// ---------------------------------------------------------------------------
+__device__ __forceinline__ int queue_bin(int cost) {
+  const int b = cost < 512 ? cost : min(QUEUE_BINS - 1, 512 + ((cost - 512) >> 5));
+  return QUEUE_BINS - 1 - b;   // most expensive first
+}
+
+__device__ __forceinline__ void bm_set(uint64_t* bm, int bit) {
+  atomicOr((unsigned long long*)&bm[bit >> 6], 1ull << (bit & 63));
+}
+__device__ __forceinline__ bool bm_get(const uint64_t* bm, int bit) { return (bm[bit >> 6] >> (bit & 63)) & 1ull; }
+
+// set bits [a, b] (inclusive), words split across the workgroup
+__device__ __forceinline__ void bm_set_range(uint64_t* bm, int a, int b) {
+  if (a > b) return;
+  const int w0 = a >> 6, w1 = b >> 6;
+  for (int w = w0 + (int)threadIdx.x; w <= w1; w += blockDim.x) {
+    const int lo = max(a, w << 6) - (w << 6), hi = min(b, (w << 6) + 63) - (w << 6);
+    const uint64_t m = (hi == 63 ? ~0ull : ((1ull << (hi + 1)) - 1)) & ~((1ull << lo) - 1);
+    atomicOr((unsigned long long*)&bm[w], m);
+  }
+}
+
+// number of set bits strictly below `bit`
+__device__ __forceinline__ int bm_popc_below(const uint64_t* bm, int bit) {
+  int c = 0;
+  const int wl = bit >> 6;
+  for (int w = 0; w < wl; ++w) c += __popcll(bm[w]);
+  if (bit & 63) c += __popcll(bm[wl] & ((1ull << (bit & 63)) - 1));
+  return c;
+}
+
+__device__ __forceinline__ int count_le(const int32_t* a, int n, int p) {   // entries <= p of an ascending array
+  int lo = 0, hi = n;
+  while (lo < hi) {
+    const int mid = (lo + hi) >> 1;
+    if (a[mid] <= p) lo = mid + 1;
+    else hi = mid;
+  }
+  return lo;
+}
+
+__global__ __launch_bounds__(256) void k_plan(Dims dm, Tables tb, char* ws) {
+  const int bh = blockIdx.y, t = blockIdx.x;
+  const HeadDev& H = wsp<const HeadDev>(ws, tb.off_heads)[bh];
+  if (t >= H.nT_rows) return;
+  const int tid = threadIdx.x, lane = tid & 63, wv = tid >> 6;
+  extern __shared__ uint64_t bm[];
+  __shared__ int rows_s[64];
+  __shared__ int red[8];
+  __shared__ long long pred[4];
+  __shared__ int sh_run_r0[64], sh_run_len[64], sh_nruns, sh_gpart;
+  const int W = H.bm_words;
+  const int32_t* pgrp = wsp<const int32_t>(ws, dm.ws_pgrp);
+
+  for (int w = tid; w < W; w += 256) bm[w] = 0ull;
+  int pos = -1;
+  if (tid < 64) {
+    const int slot = 64 * t + tid;
+    if (H.row_kind == ROW_IDENTITY) pos = slot < dm.L ? slot : -1;
+    else pos = wsp<const int32_t>(ws, H.ws_row_order)[slot];
+    rows_s[tid] = pos;
+  }
+  // tile row statistics (wave 0)
+  int qmin = 0x7fffffff, qmax = -1, nrows = 0;
+  if (wv == 0) {
+    int mn = pos >= 0 ? pos : 0x7fffffff, mx = pos, nv = pos >= 0 ? 1 : 0;
+    for (int m = 1; m < 64; m <<= 1) {
+      mn = min(mn, __shfl_xor(mn, m, 64));
+      mx = max(mx, __shfl_xor(mx, m, 64));
+      nv += __shfl_xor(nv, m, 64);
+    }
+    if (lane == 0) {
+      red[0] = mn;
+      red[1] = mx;
+      red[2] = nv;
+    }
+  }
+  __syncthreads();
+  qmin = red[0];
+  qmax = red[1];
+  nrows = red[2];
+  int4* info = wsp<int4>(ws, H.ws_info) + t;
+  long long* pairs_out = wsp<long long>(ws, H.ws_pairs) + t;
+  uint64_t* bm_out = wsp<uint64_t>(ws, H.ws_bm) + (int64_t)t * W;
+  if (nrows == 0) {
+    for (int w = tid; w < W; w += 256) bm_out[w] = 0ull;
+    if (tid == 0) {
+      *info = make_int4(0, 0, 0, 0);
+      *pairs_out = 0;
+    }
+    return;
+  }
+  int g_cnt = 0;
+  int32_t* gl = (H.gcap > 0) ? wsp<int32_t>(ws, H.ws_gather) + (int64_t)t * H.gcap : nullptr;
+  // per-row pair counting needs, per pattern, different data
+  int grid_nline = 0, grid_is_line = 0;
+  const int32_t* grid_lines = nullptr;
+  __syncthreads();
+
+  if (H.pattern == MMSA_ASHAPE) {
+    const int tmax = qmax >> 6;
+    const int ns = min((H.sink + 63) / 64, tmax + 1);
+    bm_set_range(bm, 0, ns - 1);
+    bm_set_range(bm, max(0, qmin - H.window + 1) >> 6, tmax);
+  } else if (H.pattern == MMSA_BLOCK) {
+    const int32_t* ci = wsp<const int32_t>(ws, H.ws_blk_idx) + (int64_t)t * H.k_blocks;
+    for (int i = tid; i < H.k_blocks; i += 256) {
+      const int c = ci[i];
+      if (c >= 0) bm_set(bm, c);
+    }
+  } else if (H.pattern == MMSA_GRID) {
+    const GridTask& G = wsp<const GridTask>(ws, tb.off_grid)[H.grid_task];
+    grid_nline = min(max(wsp<const int32_t>(ws, G.ws_out)[2], 0), dm.L);
+    const int nl_pad = (grid_nline + 63) & ~63;
+    grid_is_line = (64 * t) < nl_pad;
+    grid_lines = wsp<const int32_t>(ws, H.ws_row_order);
+    if (grid_is_line) bm_set_range(bm, 0, qmax >> 6);
+    else g_cnt = count_le(grid_lines, grid_nline, qmax);
+  } else {  // vertical-slash family
+    const bool twod = H.layout == MMSA_BOUNDARY_2D;
+    const bool grouped_rows = H.row_kind == ROW_GROUPED;
+    int m_q = MMSA_TEXT;
+    if (grouped_rows) m_q = (64 * t >= dm.video_base && dm.n_video > 0 && (dm.video_base > 0 || dm.n_text == 0)) ? MMSA_VIDEO : MMSA_TEXT;
+    const EstJob& J = wsp<const EstJob>(ws, tb.off_jobs)[H.job[grouped_rows ? m_q : 0]];
+    // runs of the tile's rows in the slash coordinate (positions; ranks for 2D)
+    if (tid == 0) {
+      if (twod) {
+        sh_nruns = 1;
+        sh_run_r0[0] = 64 * t - (m_q == MMSA_VIDEO ? dm.video_base : dm.text_base);  // first rank
+        sh_run_len[0] = nrows;
+      } else {
+        int nr = 0, r = 0;
+        while (r < 64 && rows_s[r] >= 0) {
+          int e = r + 1;
+          while (e < 64 && rows_s[e] == rows_s[e - 1] + 1) ++e;
+          sh_run_r0[nr] = rows_s[r];   // first position of the run
+          sh_run_len[nr] = e - r;
+          ++nr;
+          r = e;
+        }
+        sh_nruns = nr;
+      }
+    }
+    __syncthreads();
+    const int nruns = sh_nruns;
+    for (int pi = 0; pi < J.n_pairs; ++pi) {
+      const PairDev& Pd = J.pair[pi];
+      const int32_t* nsel = wsp<const int32_t>(ws, Pd.ws_nsel);
+      const int ns = min(max(nsel[1], 0), Pd.ks);
+      const int32_t* S = wsp<const int32_t>(ws, Pd.ws_sidx);
+      const int tile_base = twod ? ((Pd.m_k == MMSA_VIDEO ? dm.video_base : dm.text_base) >> 6) : 0;
+      for (int e = tid; e < ns; e += 256) {
+        const int o = twod ? S[e] - (Pd.n_k - 1) : max(S[e], 0);
+        for (int ru = 0; ru < nruns; ++ru) {
+          const int a = sh_run_r0[ru], len = sh_run_len[ru];
+          int khi = a + len - 1 - o, klo = a - o;
+          if (twod) {
+            khi = min(khi, Pd.n_k - 1);
+            klo = max(klo, 0);
+          } else {
+            klo = max(klo, 0);
+          }
+          if (khi < klo) continue;
+          for (int c = klo >> 6; c <= (khi >> 6); ++c) bm_set(bm, tile_base + c);
+        }
+      }
+    }
+    __syncthreads();
+    if (twod) {
+      // drop view tiles whose first key comes after the tile's last row
+      for (int w = tid; w < W; w += 256) {
+        uint64_t bits = bm[w], keep = bits;
+        while (bits) {
+          const int b = __ffsll((unsigned long long)bits) - 1;
+          bits &= bits - 1;
+          const int first = pgrp[(int64_t)(64 * w + b) * 64];
+          if (first < 0 || first > qmax) keep &= ~(1ull << b);
+        }
+        bm[w] = keep;
+      }
+      __syncthreads();
+    }
+    // gathered verticals not held by a listed tile, ascending per key modality
+    int gbase = 0;
+    for (int pi = 0; pi < J.n_pairs; ++pi) {
+      const PairDev& Pd = J.pair[pi];
+      const int nv = min(max(wsp<const int32_t>(ws, Pd.ws_nsel)[0], 0), Pd.kv);
+      const int32_t* V = wsp<const int32_t>(ws, Pd.ws_vidx);
+      const int kbase = twod ? (Pd.m_k == MMSA_VIDEO ? dm.video_base : dm.text_base) : 0;
+      for (int s0 = 0; s0 < nv; s0 += 256) {
+        const int e = s0 + tid;
+        bool keep = false;
+        int p = -1;
+        if (e < nv) {
+          const int c = V[e];
+          const bool inr = c >= 0 && c < (twod ? Pd.n_k : dm.L);
+          p = inr ? (twod ? pgrp[kbase + c] : c) : -1;
+          const int vt = twod ? ((kbase + c) >> 6) : (c >> 6);
+          keep = inr && p >= 0 && p <= qmax && !bm_get(bm, vt);
+        }
+        int tot;
+        const int r = block_excl_count(keep, red, &tot);
+        if (keep) gl[gbase + r] = p;
+        gbase += tot;
+      }
+      if (pi == 0 && tid == 0) sh_gpart = gbase;
+    }
+    g_cnt = gbase;
+    __syncthreads();
+  }
+  __syncthreads();
+
+  // exact selected pairs of each row
+  long long my_pairs = 0;
+  if (tid < 64 && pos >= 0) {
+    const int p = pos;
+    if (H.pattern == MMSA_ASHAPE) {
+      my_pairs = min(p + 1, H.window) + max(0, min(H.sink, p + 1 - H.window));
+    } else if (H.pattern == MMSA_GRID) {
+      my_pairs = grid_is_line ? (p + 1) : count_le(grid_lines, grid_nline, p);
+    } else if (H.view_kind == VIEW_IDENTITY) {
+      const int cp = p >> 6;
+      my_pairs = 64ll * bm_popc_below(bm, cp) + (bm_get(bm, cp) ? (p - 64 * cp + 1) : 0);
+      if (H.pattern == MMSA_VS) my_pairs += count_le(gl, g_cnt, p);
+    } else {  // grouped key view (2D boundary)
+      const int slot = wsp<const int32_t>(ws, dm.ws_gslot)[p];
+      const bool vid = dm.n_video > 0 && slot >= dm.video_base && (dm.video_base > 0 || dm.n_text == 0);
+      const int rank = vid ? slot - dm.video_base : slot - dm.text_base;
+      const int kt = vid ? (p - rank) : (rank + 1);          // text keys <= p
+      const int kv = (p + 1) - kt;                             // video keys <= p
+      const int ntt = (dm.n_text + 63) >> 6;
+      const int tb0 = dm.text_base >> 6, vb0 = dm.video_base >> 6;
+      long long c = 0;
+      if (kt > 0) {
+        const int ct = kt >> 6;
+        c += 64ll * (bm_popc_below(bm, tb0 + ct) - bm_popc_below(bm, tb0));
+        if ((kt & 63) && ct < ntt && bm_get(bm, tb0 + ct)) c += kt & 63;
+      }
+      if (kv > 0) {
+        const int ntv = (dm.n_video + 63) >> 6;
+        const int cv = kv >> 6;
+        c += 64ll * (bm_popc_below(bm, vb0 + cv) - bm_popc_below(bm, vb0));
+        if ((kv & 63) && cv < ntv && bm_get(bm, vb0 + cv)) c += kv & 63;
+      }
+      const int gp = sh_gpart;
+      c += count_le(gl, gp, p) + count_le(gl + gp, g_cnt - gp, p);
+      my_pairs = c;
+    }
+  }
+  for (int m = 1; m < 64; m <<= 1) my_pairs += __shfl_xor(my_pairs, m, 64);
+  // tiles in the bitmap
+  int nt = 0;
+  for (int w = tid; w < W; w += 256) {
+    nt += __popcll(bm[w]);
+    bm_out[w] = bm[w];
+  }
+  for (int m = 1; m < 64; m <<= 1) nt += __shfl_xor(nt, m, 64);
+  if (lane == 0) {
+    red[wv] = nt;
+    pred[wv] = my_pairs;
+  }
+  __syncthreads();
+  if (tid == 0) {
+    const int ntiles = red[0] + red[1] + red[2] + red[3];
+    const int cost = ntiles + (g_cnt + 63) / 64;
+    *info = make_int4(ntiles, g_cnt, cost, nrows);
+    *pairs_out = pred[0];
+    if (cost > 0) atomicAdd(wsp<int32_t>(ws, dm.ws_qhist) + queue_bin(cost), 1);
+  }
+}
+
+// Exclusive scan of the queue histogram (one workgroup of 1024).
+__global__ __launch_bounds__(1024) void k_queue_scan(Dims dm, char* ws) {
+  int32_t* hist = wsp<int32_t>(ws, dm.ws_qhist);
+  __shared__ int sh[QUEUE_BINS];
+  const int t = threadIdx.x;
+  sh[t] = hist[t];
+  __syncthreads();
+  for (int off = 1; off < QUEUE_BINS; off <<= 1) {
+    const int v = t >= off ? sh[t - off] : 0;
+    __syncthreads();
+    sh[t] += v;
+    __syncthreads();
+  }
+  const int incl = sh[t];
+  hist[t] = incl - hist[t];          // exclusive start = cursor
+  if (t == QUEUE_BINS - 1) hist[QUEUE_BINS] = incl;
+}
+
+// Place every non-empty (head, tile) in cost order.  grid (tiles, heads).
+__global__ __launch_bounds__(64) void k_queue_scatter(Dims dm, Tables tb, char* ws) {
+  const int bh = blockIdx.y;
+  const HeadDev& H = wsp<const HeadDev>(ws, tb.off_heads)[bh];
+  const int t = blockIdx.x * 64 + threadIdx.x;
+  if (t >= H.nT_rows) return;
+  const int cost = wsp<const int4>(ws, H.ws_info)[t].z;
+  if (cost <= 0) return;
+  const int pos = atomicAdd(wsp<int32_t>(ws, dm.ws_qhist) + queue_bin(cost), 1);
+  wsp<int32_t>(ws, dm.ws_queue)[pos] = (bh << 16) | t;
+}
+
+hipError_t launch_plan(const Dims& dm, const Tables& tb, char* ws, int max_tiles, int max_bm_words,
+                       hipStream_t s) {
+  hipError_t e = launch_fill_u32(ws + dm.ws_qhist, 0, QUEUE_BINS + 1, s);
+  if (e != hipSuccess) return e;
+  if (max_tiles > 0 && tb.n_heads > 0) {
+    k_plan<<<dim3(max_tiles, (unsigned)tb.n_heads), 256, (size_t)max_bm_words * 8, s>>>(dm, tb, ws);
+    k_queue_scan<<<1, QUEUE_BINS, 0, s>>>(dm, ws);
+    k_queue_scatter<<<dim3((max_tiles + 63) / 64, (unsigned)tb.n_heads), 64, 0, s>>>(dm, tb, ws);
+  }
+  return hipGetLastError();
+}
+
+}  // namespace mmsa

@@ -1,0 +1,963 @@
+// Host side of libmmsa: argument validation, workspace layout, the tables the
+// kernels read, and the five ABI entry points declared in include/mmsa.h.
+//
+// Everything here runs on the host before any HIP call, so an invalid
+// descriptor is rejected without touching the device.  The per-call tables
+// (heads, estimation regions, tasks) are rebuilt from the descriptor by every
+// call and uploaded with one asynchronous copy to the start of the workspace.
+#include <algorithm>
+#include <cmath>
+#include <cstdarg>
+#include <cstdio>
+#include <cstring>
+#include <string>
+#include <vector>
+
+#include "mmsa_internal.h"
+
+using namespace mmsa;
+
+namespace {
+
+thread_local std::string g_err;
+
+void set_err(const char* fmt, ...) {
+  char buf[512];
+  va_list ap;
+  va_start(ap, fmt);
+  vsnprintf(buf, sizeof buf, fmt, ap);
+  va_end(ap);
+  g_err = buf;
+}
+
+int64_t pad_to(int64_t x, int64_t a) { return (x + a - 1) / a * a; }
+
+struct Bump {
+  int64_t off = 0;
+  int64_t take(int64_t bytes) {
+    off = pad_to(off, 256);
+    const int64_t r = off;
+    off += std::max<int64_t>(bytes, 0);
+    return r;
+  }
+};
+
+struct Seg {
+  int64_t start, len;
+  int modality, rank_start;
+};
+
+struct Layout {
+  Dims dm{};
+  Tables tb{};
+  int B = 0, Hq = 0, Hkv = 0, L = 0, d = 0, nT = 0, BH = 0;
+  std::vector<int> kvmap;
+  std::vector<mmsa_head_cfg> cfg;
+  std::vector<Seg> segs;
+  int n_mod[2] = {0, 0};
+  std::vector<HeadDev> heads;
+  std::vector<EstJob> jobs;
+  std::vector<EstGroup> g1, g2;
+  std::vector<TopkTask> topk;
+  std::vector<GridTask> grids;
+  std::vector<PoolTask> pools;
+  std::vector<BlockTask> blocks;
+  std::vector<GatherTask> gathers;
+  std::vector<UnpermTask> unperms;
+  std::vector<char> blob;
+  int64_t ws_total = 0;
+  int n_chunks1 = 0, n_chunks2 = 0, max_ds = 0, max_strides = 0, nB = 0, max_tiles = 0, max_bm_words = 0;
+  int max_gather_slots = 0, max_unperm_slots = 0;
+  int64_t max_items = 0;
+  int64_t zero_off = 0, zero_bytes = 0;       // vertical scores and slash accumulators
+  int64_t gridrow_off = 0, gridrow_bytes = 0; // grid row orders (filled with -1)
+  bool need_seg = false, any_vs_est = false, any_block = false;
+  bool empty = false;
+  // per (bh, part) index-set facts for mmsa_index_meta / views: job index and pair index
+  std::vector<std::vector<std::pair<int, int>>> set_of;   // [bh][part] -> (job, pair) or (-1,-1)
+};
+
+// number of tokens of modality m at positions <= i
+int64_t count_mod_le(const Layout& Lo, int m, int64_t i) {
+  int64_t c = 0;
+  for (const Seg& s : Lo.segs) {
+    if (s.start > i) break;
+    if (s.modality == m) c += std::min<int64_t>(s.len, i - s.start + 1);
+  }
+  return c;
+}
+
+// the last `count` positions of modality m, ascending
+std::vector<int> last_positions(const Layout& Lo, int m, int count) {
+  std::vector<int> out;
+  for (int si = (int)Lo.segs.size() - 1; si >= 0 && (int)out.size() < count; --si) {
+    const Seg& s = Lo.segs[si];
+    if (s.modality != m) continue;
+    for (int64_t p = s.start + s.len - 1; p >= s.start && (int)out.size() < count; --p) out.push_back((int)p);
+  }
+  std::reverse(out.begin(), out.end());
+  return out;
+}
+
+void set_runs(EstJob& J) {
+  J.n_runs = 0;
+  int r = 0;
+  while (r < J.n_rows) {
+    int e = r + 1;
+    while (e < J.n_rows && J.rows[e] == J.rows[e - 1] + 1) ++e;
+    J.run_r0[J.n_runs] = r;
+    J.run_len[J.n_runs] = e - r;
+    ++J.n_runs;
+    r = e;
+  }
+}
+
+bool valid_combo(int pattern, int layout) {
+  switch (pattern) {
+    case MMSA_ASHAPE:
+    case MMSA_BLOCK: return layout == MMSA_PLAIN;
+    case MMSA_VS: return layout == MMSA_PLAIN || layout == MMSA_Q_BOUNDARY || layout == MMSA_BOUNDARY_2D;
+    case MMSA_GRID: return layout == MMSA_PLAIN || layout == MMSA_MODALITY_GROUPED;
+    default: return false;
+  }
+}
+
+mmsa_status build_layout(const mmsa_layer_desc* desc, Layout& Lo) {
+  if (!desc) {
+    set_err("desc is NULL");
+    return MMSA_INVALID_ARGUMENT;
+  }
+  const mmsa_layer_desc& D = *desc;
+  if (D.B < 0 || D.L < 0 || D.Hq < 0 || D.Hkv < 0) {
+    set_err("negative shape (B=%d Hq=%d Hkv=%d L=%d)", D.B, D.Hq, D.Hkv, D.L);
+    return MMSA_INVALID_ARGUMENT;
+  }
+  if (D.d != 64 && D.d != 128) {
+    set_err("head dimension d=%d is not supported (64 or 128)", D.d);
+    return MMSA_UNSUPPORTED;
+  }
+  if (D.flags != 0) {
+    set_err("flags must be 0");
+    return MMSA_INVALID_ARGUMENT;
+  }
+  if (D.L >= (1 << 22)) {
+    set_err("L=%d exceeds the supported 2^22 tokens", D.L);
+    return MMSA_UNSUPPORTED;
+  }
+  if ((int64_t)D.B * D.Hq > 4096) {
+    set_err("B*Hq=%lld exceeds 4096", (long long)D.B * D.Hq);
+    return MMSA_UNSUPPORTED;
+  }
+  Lo.B = D.B;
+  Lo.Hq = D.Hq;
+  Lo.Hkv = D.Hkv;
+  Lo.L = D.L;
+  Lo.d = D.d;
+  Lo.BH = D.B * D.Hq;
+  Lo.nT = (D.L + TILE - 1) / TILE;
+  if (D.Hq > 0 && D.Hkv <= 0) {
+    set_err("Hkv must be >= 1");
+    return MMSA_INVALID_ARGUMENT;
+  }
+  if (!(std::isfinite(D.scale)) || D.scale < 0.f) {
+    set_err("scale must be finite and >= 0");
+    return MMSA_INVALID_ARGUMENT;
+  }
+  const int64_t* st[4] = {D.q_strides, D.k_strides, D.v_strides, D.o_strides};
+  const char* nm[4] = {"q", "k", "v", "o"};
+  for (int i = 0; i < 4; ++i) {
+    if (st[i][0] < 0 || st[i][1] < 0 || st[i][2] < D.d || (st[i][2] % 8) != 0 || (st[i][1] % 8) != 0 ||
+        (st[i][0] % 8) != 0) {
+      set_err("%s strides (%lld, %lld, %lld) must be non-negative multiples of 8 with row stride >= d", nm[i],
+              (long long)st[i][0], (long long)st[i][1], (long long)st[i][2]);
+      return MMSA_INVALID_ARGUMENT;
+    }
+  }
+  // heads
+  Lo.kvmap.assign(D.Hq, 0);
+  if (D.Hq > 0) {
+    if (!D.heads) {
+      set_err("heads is NULL");
+      return MMSA_INVALID_ARGUMENT;
+    }
+    if (D.kv_head_of) {
+      for (int h = 0; h < D.Hq; ++h) {
+        if (D.kv_head_of[h] < 0 || D.kv_head_of[h] >= D.Hkv) {
+          set_err("kv_head_of[%d]=%d out of range [0,%d)", h, D.kv_head_of[h], D.Hkv);
+          return MMSA_INVALID_ARGUMENT;
+        }
+        Lo.kvmap[h] = D.kv_head_of[h];
+      }
+    } else {
+      if (D.Hq % D.Hkv != 0) {
+        set_err("Hq=%d is not a multiple of Hkv=%d and kv_head_of is NULL", D.Hq, D.Hkv);
+        return MMSA_INVALID_ARGUMENT;
+      }
+      for (int h = 0; h < D.Hq; ++h) Lo.kvmap[h] = h / (D.Hq / D.Hkv);
+    }
+  }
+  Lo.cfg.assign(D.heads, D.heads + D.Hq);
+  for (int h = 0; h < D.Hq; ++h) {
+    mmsa_head_cfg& c = Lo.cfg[h];
+    if (!valid_combo(c.pattern, c.layout)) {
+      set_err("head %d: pattern %d with layout %d is not a valid combination", h, c.pattern, c.layout);
+      return MMSA_INVALID_ARGUMENT;
+    }
+    if (c.pattern == MMSA_ASHAPE && (c.sink < 0 || c.window < 1)) {
+      set_err("head %d: A-shape needs sink >= 0 and window >= 1", h);
+      return MMSA_INVALID_ARGUMENT;
+    }
+    if (c.pattern == MMSA_VS && (c.k_vertical < 0 || c.k_slash < 0)) {
+      set_err("head %d: negative vertical/slash budget", h);
+      return MMSA_INVALID_ARGUMENT;
+    }
+    if (c.pattern == MMSA_BLOCK) {
+      if (c.k_blocks < 0) {
+        set_err("head %d: negative block budget", h);
+        return MMSA_INVALID_ARGUMENT;
+      }
+      if (D.L > (1 << 20)) {
+        set_err("head %d: BLOCK heads support L <= 2^20", h);
+        return MMSA_UNSUPPORTED;
+      }
+    }
+    if (c.pattern == MMSA_GRID) {
+      if (c.grid_clip == 0) c.grid_clip = 8;
+      if (c.grid_phases < 1 || c.grid_phases > MAX_PHASES || c.stride_lo < 16 || c.stride_hi < c.stride_lo ||
+          c.stride_hi > MAX_STRIDE || c.grid_clip < 1 || c.grid_clip > 64) {
+        set_err("head %d: grid needs 1<=phases<=%d, 16<=stride_lo<=stride_hi<=%d, 1<=clip<=64", h, MAX_PHASES,
+                MAX_STRIDE);
+        return MMSA_INVALID_ARGUMENT;
+      }
+    }
+  }
+  // segments
+  Lo.segs.clear();
+  if (D.segs && D.n_segs > 0) {
+    int64_t pos = 0;
+    int rank[2] = {0, 0};
+    for (int i = 0; i < D.n_segs; ++i) {
+      const mmsa_segment& s = D.segs[i];
+      if (s.start != pos || s.len <= 0 || (s.modality != MMSA_TEXT && s.modality != MMSA_VIDEO)) {
+        set_err("segment %d (start %lld, len %lld, modality %d) does not continue the tiling of [0, L)", i,
+                (long long)s.start, (long long)s.len, s.modality);
+        return MMSA_INVALID_ARGUMENT;
+      }
+      Lo.segs.push_back(Seg{s.start, s.len, s.modality, rank[s.modality]});
+      rank[s.modality] += (int)s.len;
+      pos += s.len;
+    }
+    if (pos != D.L) {
+      set_err("segments cover %lld tokens, L=%d", (long long)pos, D.L);
+      return MMSA_INVALID_ARGUMENT;
+    }
+  } else if (D.n_segs < 0 || (D.n_segs > 0 && !D.segs)) {
+    set_err("n_segs=%d with segs=%p", D.n_segs, (const void*)D.segs);
+    return MMSA_INVALID_ARGUMENT;
+  } else if (D.L > 0) {
+    Lo.segs.push_back(Seg{0, D.L, MMSA_TEXT, 0});
+  }
+  for (const Seg& s : Lo.segs) Lo.n_mod[s.modality] += (int)s.len;
+
+  Dims& dm = Lo.dm;
+  dm.B = D.B;
+  dm.Hq = D.Hq;
+  dm.Hkv = D.Hkv;
+  dm.L = D.L;
+  dm.d = D.d;
+  dm.nT = Lo.nT;
+  dm.n_text = Lo.n_mod[MMSA_TEXT];
+  dm.n_video = Lo.n_mod[MMSA_VIDEO];
+  dm.text_base = 0;
+  dm.video_base = (int)pad_to(dm.n_text, GRP_PAD);
+  dm.L_grp = (int)(pad_to(dm.n_text, GRP_PAD) + pad_to(dm.n_video, GRP_PAD));
+  dm.scale = D.scale > 0.f ? D.scale : 1.0f / std::sqrt((float)D.d);
+  dm.scale_log2 = dm.scale * 1.4426950408889634f;
+  dm.q_sb = D.q_strides[0];
+  dm.q_sh = D.q_strides[1];
+  dm.q_sl = D.q_strides[2];
+  dm.k_sb = D.k_strides[0];
+  dm.k_sh = D.k_strides[1];
+  dm.k_sl = D.k_strides[2];
+  dm.v_sb = D.v_strides[0];
+  dm.v_sh = D.v_strides[1];
+  dm.v_sl = D.v_strides[2];
+  dm.o_sb = D.o_strides[0];
+  dm.o_sh = D.o_strides[1];
+  dm.o_sl = D.o_strides[2];
+
+  Lo.empty = (Lo.BH == 0 || D.L == 0);
+  if (Lo.empty) {
+    Lo.ws_total = 256;
+    return MMSA_OK;
+  }
+
+  const int L = D.L, nT = Lo.nT;
+  Lo.nB = nT;
+  Lo.set_of.assign(Lo.BH, std::vector<std::pair<int, int>>(4, {-1, -1}));
+  // ---- heads, estimation jobs, tasks (offsets filled later) ----
+  Lo.heads.resize(Lo.BH);
+  for (int b = 0; b < D.B; ++b) {
+    for (int h = 0; h < D.Hq; ++h) {
+      const int bh = b * D.Hq + h;
+      const mmsa_head_cfg& c = Lo.cfg[h];
+      HeadDev& H = Lo.heads[bh];
+      std::memset(&H, 0, sizeof H);
+      H.b = b;
+      H.h = h;
+      H.g = Lo.kvmap[h];
+      H.pattern = c.pattern;
+      H.layout = c.layout;
+      H.sink = c.sink;
+      H.window = c.window;
+      H.k_blocks = std::min(c.k_blocks, Lo.nB);
+      H.grid_task = -1;
+      H.job[0] = H.job[1] = -1;
+      H.q_off = b * dm.q_sb + h * dm.q_sh;
+      H.k_off = b * dm.k_sb + H.g * dm.k_sh;
+      H.v_off = b * dm.v_sb + H.g * dm.v_sh;
+      H.o_off = b * dm.o_sb + h * dm.o_sh;
+      H.ws_row_order = H.ws_qperm = H.ws_operm = H.ws_kgrp = H.ws_vgrp = -1;
+      H.ws_gather = H.ws_blk_idx = H.ws_qp = H.ws_kp = H.ws_z = -1;
+      H.row_kind = ROW_IDENTITY;
+      H.view_kind = VIEW_IDENTITY;
+      H.n_row_slots = nT * TILE;
+      if (c.pattern == MMSA_VS && c.layout != MMSA_PLAIN) {
+        H.row_kind = ROW_GROUPED;
+        H.n_row_slots = dm.L_grp;
+        if (c.layout == MMSA_BOUNDARY_2D) H.view_kind = VIEW_GROUPED;
+        Lo.need_seg = true;
+      }
+      if (c.pattern == MMSA_GRID) {
+        H.row_kind = ROW_GRID;
+        H.n_row_slots = (int)pad_to(L, TILE) + TILE;
+        if (c.layout == MMSA_MODALITY_GROUPED) Lo.need_seg = true;
+      }
+      H.nT_rows = H.n_row_slots / TILE;
+      H.nT_view = H.view_kind == VIEW_GROUPED ? dm.L_grp / TILE : nT;
+      H.bm_words = (H.nT_view + 63) / 64;
+      if (c.pattern == MMSA_BLOCK) Lo.any_block = true;
+
+      // estimation jobs
+      auto new_job = [&](int kind, int view, int m_q, const std::vector<int>& rows) -> int {
+        EstJob J;
+        std::memset(&J, 0, sizeof J);
+        J.bh = bh;
+        J.kind = kind;
+        J.view = view;
+        J.m_q = m_q;
+        J.n_rows = (int)rows.size();
+        for (int i = 0; i < J.n_rows; ++i) J.rows[i] = rows[i];
+        J.imax = rows.back();
+        J.q_off = H.q_off;
+        J.k_off = H.k_off;
+        set_runs(J);
+        Lo.jobs.push_back(J);
+        return (int)Lo.jobs.size() - 1;
+      };
+      auto orig_pair = [&](EstJob& J) {
+        PairDev& P = J.pair[0];
+        std::memset(&P, 0, sizeof P);
+        P.m_k = -1;
+        P.Dv = L;
+        P.Ds = L;
+        P.n_k = L;
+        P.v_lo = 0;
+        P.v_hi = J.imax + 1;
+        P.s_lo = 0;
+        P.s_hi = J.imax + 1;
+        P.kv = std::min(c.k_vertical, P.v_hi - P.v_lo);
+        P.ks = std::min(c.k_slash, P.s_hi - P.s_lo);
+        J.n_pairs = 1;
+      };
+      if (c.pattern == MMSA_VS) {
+        Lo.any_vs_est = true;
+        if (c.layout == MMSA_PLAIN) {
+          std::vector<int> rows;
+          for (int p = std::max(0, L - EST_ROWS); p < L; ++p) rows.push_back(p);
+          const int j = new_job(JOB_VS_ORIG, VIEW_IDENTITY, -1, rows);
+          orig_pair(Lo.jobs[j]);
+          H.job[0] = j;
+          Lo.set_of[bh][0] = {j, 0};
+          H.gcap = Lo.jobs[j].pair[0].kv;
+        } else {
+          int gcap = 0;
+          for (int m = 0; m < 2; ++m) {
+            if (Lo.n_mod[m] == 0) continue;
+            const std::vector<int> rows = last_positions(Lo, m, EST_ROWS);
+            const bool twod = c.layout == MMSA_BOUNDARY_2D;
+            const int j = new_job(twod ? JOB_VS_2D : JOB_VS_ORIG, twod ? VIEW_GROUPED : VIEW_IDENTITY, m, rows);
+            EstJob& J = Lo.jobs[j];
+            H.job[m] = j;
+            if (!twod) {
+              orig_pair(J);
+              Lo.set_of[bh][m] = {j, 0};
+              gcap = std::max(gcap, J.pair[0].kv);
+            } else {
+              const int n_q = Lo.n_mod[m];
+              J.rho0 = n_q - J.n_rows;
+              J.n_pairs = 0;
+              int gsum = 0;
+              for (int mk = 0; mk < 2; ++mk) {
+                if (Lo.n_mod[mk] == 0) continue;
+                PairDev& P = J.pair[J.n_pairs];
+                std::memset(&P, 0, sizeof P);
+                const int n_k = Lo.n_mod[mk];
+                P.m_k = mk;
+                P.n_k = n_k;
+                P.Dv = n_k;
+                P.Ds = n_q + n_k - 1;
+                // candidates: columns and diagonals met by the causal part of the rows
+                int lo = 1 << 30, hi = -1, vhi = 0;
+                for (int r = 0; r < J.n_rows; ++r) {
+                  const int nv = (int)count_mod_le(Lo, mk, J.rows[r]);
+                  vhi = std::max(vhi, nv);
+                  if (nv >= 1) {
+                    const int rho = J.rho0 + r;
+                    hi = std::max(hi, rho);
+                    lo = std::min(lo, rho - nv + 1);
+                  }
+                }
+                P.v_lo = 0;
+                P.v_hi = vhi;
+                if (hi >= 0) {
+                  P.s_lo = lo + n_k - 1;
+                  P.s_hi = hi + n_k;
+                } else {
+                  P.s_lo = P.s_hi = 0;
+                }
+                P.kv = std::min(c.k_vertical, P.v_hi - P.v_lo);
+                P.ks = std::min(c.k_slash, P.s_hi - P.s_lo);
+                gsum += P.kv;
+                Lo.set_of[bh][2 * m + mk] = {j, J.n_pairs};
+                ++J.n_pairs;
+              }
+              H.n_pairs = J.n_pairs;
+              gcap = std::max(gcap, gsum);
+            }
+          }
+          H.gcap = gcap;
+        }
+      } else if (c.pattern == MMSA_GRID) {
+        const bool grouped = c.layout == MMSA_MODALITY_GROUPED;
+        std::vector<int> rows;
+        if (!grouped) {
+          for (int p = std::max(0, L - EST_ROWS); p < L; ++p) rows.push_back(p);
+        } else {
+          rows = last_positions(Lo, MMSA_VIDEO, EST_ROWS);
+          if ((int)rows.size() < EST_ROWS) {
+            std::vector<int> t = last_positions(Lo, MMSA_TEXT, EST_ROWS - (int)rows.size());
+            rows.insert(rows.end(), t.begin(), t.end());
+            std::sort(rows.begin(), rows.end());
+          }
+        }
+        const int j = new_job(grouped ? JOB_GRID_GROUPED : JOB_GRID_PLAIN, grouped ? VIEW_GROUPED : VIEW_IDENTITY,
+                              -1, rows);
+        EstJob& J = Lo.jobs[j];
+        PairDev& P = J.pair[0];
+        std::memset(&P, 0, sizeof P);
+        P.m_k = -1;
+        P.Dv = L;
+        J.n_pairs = 1;
+        H.job[0] = j;
+        Lo.set_of[bh][0] = {j, 0};
+        GridTask T;
+        std::memset(&T, 0, sizeof T);
+        T.job = j;
+        T.bh = bh;
+        int Dg;
+        if (!grouped) {
+          Dg = J.imax + 1;
+        } else {
+          const int64_t nt = count_mod_le(Lo, MMSA_TEXT, J.imax), nv = count_mod_le(Lo, MMSA_VIDEO, J.imax);
+          int64_t mx = nt - 1;
+          if (nv >= 1) mx = std::max<int64_t>(mx, dm.n_text + nv - 1);
+          Dg = (int)mx + 1;
+        }
+        T.D = Dg;
+        T.n_rows = J.n_rows;
+        T.s_lo = std::min(c.stride_lo, Dg);
+        T.s_hi = std::min(c.stride_hi, Dg);
+        T.w = c.grid_phases;
+        T.grouped = grouped ? 1 : 0;
+        const long long capll = ((long long)c.grid_clip * T.n_rows * (1ll << 24)) / Dg;
+        T.cap = capll;
+        H.grid_task = (int)Lo.grids.size();
+        Lo.grids.push_back(T);
+        Lo.max_strides = std::max(Lo.max_strides, T.s_hi - T.s_lo + 1);
+      }
+    }
+  }
+  // ---- groups (jobs sorted by (b, g, view)) ----
+  {
+    std::vector<int> order(Lo.jobs.size());
+    for (size_t i = 0; i < order.size(); ++i) order[i] = (int)i;
+    std::stable_sort(order.begin(), order.end(), [&](int a, int b2) {
+      const HeadDev& A = Lo.heads[Lo.jobs[a].bh];
+      const HeadDev& Bq = Lo.heads[Lo.jobs[b2].bh];
+      if (A.b != Bq.b) return A.b < Bq.b;
+      if (A.g != Bq.g) return A.g < Bq.g;
+      return Lo.jobs[a].view < Lo.jobs[b2].view;
+    });
+    std::vector<int> newidx(order.size());
+    std::vector<EstJob> sorted;
+    for (size_t i = 0; i < order.size(); ++i) {
+      newidx[order[i]] = (int)i;
+      sorted.push_back(Lo.jobs[order[i]]);
+    }
+    Lo.jobs.swap(sorted);
+    for (HeadDev& H : Lo.heads)
+      for (int m = 0; m < 2; ++m)
+        if (H.job[m] >= 0) H.job[m] = newidx[H.job[m]];
+    for (GridTask& T : Lo.grids) T.job = newidx[T.job];
+    for (auto& v : Lo.set_of)
+      for (auto& pr : v)
+        if (pr.first >= 0) pr.first = newidx[pr.first];
+    for (size_t i = 0; i < Lo.jobs.size();) {
+      const HeadDev& H0 = Lo.heads[Lo.jobs[i].bh];
+      size_t e = i;
+      while (e < Lo.jobs.size() && Lo.heads[Lo.jobs[e].bh].b == H0.b && Lo.heads[Lo.jobs[e].bh].g == H0.g) ++e;
+      EstGroup G1{H0.b, H0.g, 0, (int)i, (int)e, L, H0.k_off, -1};
+      Lo.g1.push_back(G1);
+      for (size_t s = i; s < e;) {
+        size_t f = s;
+        while (f < e && Lo.jobs[f].view == Lo.jobs[s].view) ++f;
+        const int view = Lo.jobs[s].view;
+        EstGroup G2{H0.b, H0.g, view, (int)s, (int)f, view == VIEW_GROUPED ? dm.L_grp : L, H0.k_off, -1};
+        Lo.g2.push_back(G2);
+        s = f;
+      }
+      i = e;
+    }
+  }
+  Lo.n_chunks1 = (L + EST_CK - 1) / EST_CK;
+  Lo.n_chunks2 = (std::max(L, dm.L_grp) + EST_CK - 1) / EST_CK;
+
+  // ---- sizes of the uploaded tables ----
+  Tables& tb = Lo.tb;
+  tb.n_heads = Lo.BH;
+  tb.n_jobs = (int64_t)Lo.jobs.size();
+  tb.n_groups1 = (int64_t)Lo.g1.size();
+  tb.n_groups2 = (int64_t)Lo.g2.size();
+  tb.n_grid = (int64_t)Lo.grids.size();
+  tb.n_segs = (int64_t)Lo.segs.size();
+  // topk / pool / block / gather / unpermute task counts are known once offsets exist; reserve the maxima
+  int64_t n_topk = 0;
+  for (const EstJob& J : Lo.jobs)
+    if (J.kind == JOB_VS_ORIG || J.kind == JOB_VS_2D) n_topk += 2 * J.n_pairs;
+  int64_t n_block = 0, n_perm = 0;
+  std::vector<int> kv_pool, kv_grp;   // (b*Hkv + g) needing pooled K / grouped K,V
+  for (const HeadDev& H : Lo.heads) {
+    if (H.pattern == MMSA_BLOCK) {
+      ++n_block;
+      kv_pool.push_back(H.b * D.Hkv + H.g);
+    }
+    if (H.row_kind != ROW_IDENTITY) ++n_perm;
+    if (H.view_kind == VIEW_GROUPED) kv_grp.push_back(H.b * D.Hkv + H.g);
+  }
+  std::sort(kv_pool.begin(), kv_pool.end());
+  kv_pool.erase(std::unique(kv_pool.begin(), kv_pool.end()), kv_pool.end());
+  std::sort(kv_grp.begin(), kv_grp.end());
+  kv_grp.erase(std::unique(kv_grp.begin(), kv_grp.end()), kv_grp.end());
+  tb.n_topk = n_topk;
+  tb.n_pool = n_block + (int64_t)kv_pool.size();
+  tb.n_block = n_block;
+  tb.n_gather = n_perm + 2 * (int64_t)kv_grp.size();
+  tb.n_unperm = n_perm;
+
+  Bump bp;
+  tb.off_heads = bp.take((int64_t)sizeof(HeadDev) * tb.n_heads);
+  tb.off_jobs = bp.take((int64_t)sizeof(EstJob) * tb.n_jobs);
+  tb.off_groups1 = bp.take((int64_t)sizeof(EstGroup) * tb.n_groups1);
+  tb.off_groups2 = bp.take((int64_t)sizeof(EstGroup) * tb.n_groups2);
+  tb.off_topk = bp.take((int64_t)sizeof(TopkTask) * tb.n_topk);
+  tb.off_grid = bp.take((int64_t)sizeof(GridTask) * tb.n_grid);
+  tb.off_segs = bp.take((int64_t)sizeof(SegDev) * tb.n_segs);
+  tb.off_pool = bp.take((int64_t)sizeof(PoolTask) * tb.n_pool);
+  tb.off_block = bp.take((int64_t)sizeof(BlockTask) * tb.n_block);
+  tb.off_gather = bp.take((int64_t)sizeof(GatherTask) * tb.n_gather);
+  tb.off_unperm = bp.take((int64_t)sizeof(UnpermTask) * tb.n_unperm);
+  const int64_t blob_bytes = pad_to(bp.off, 256);
+
+  // ---- device buffers ----
+  const int dd = D.d;
+  dm.ws_flag = bp.take(256);
+  dm.ws_qhist = bp.take(4 * (QUEUE_BINS + 1));
+  dm.ws_pgrp = bp.take(4ll * std::max(dm.L_grp, 1));
+  dm.ws_gslot = bp.take(4ll * L);
+  for (const HeadDev& H : Lo.heads) Lo.max_items += H.nT_rows;
+  dm.ws_queue = bp.take(4 * Lo.max_items);
+  // estimation: stats and partials
+  for (EstJob& J : Lo.jobs) {
+    J.ws_stats = bp.take(8ll * EST_ROWS);
+    J.ws_part = bp.take(8ll * EST_ROWS * Lo.n_chunks1);
+  }
+  // zero region: vertical scores and slash accumulators
+  bp.off = pad_to(bp.off, 256);
+  Lo.zero_off = bp.off;
+  for (EstJob& J : Lo.jobs) {
+    for (int pi = 0; pi < J.n_pairs; ++pi) {
+      PairDev& P = J.pair[pi];
+      P.ws_v = bp.take(4ll * P.Dv);
+      P.ws_sacc = P.Ds > 0 ? bp.take(8ll * P.Ds) : -1;
+    }
+  }
+  bp.off = pad_to(bp.off, 256);
+  Lo.zero_bytes = bp.off - Lo.zero_off;
+  for (EstJob& J : Lo.jobs) {
+    for (int pi = 0; pi < J.n_pairs; ++pi) {
+      PairDev& P = J.pair[pi];
+      if (J.kind == JOB_VS_ORIG || J.kind == JOB_VS_2D) {
+        P.ws_s = bp.take(4ll * P.Ds);
+        P.ws_vidx = bp.take(4ll * std::max(P.kv, 1));
+        P.ws_sidx = bp.take(4ll * std::max(P.ks, 1));
+        P.ws_nsel = bp.take(8);
+        Lo.max_ds = std::max(Lo.max_ds, P.Ds);
+        Lo.topk.push_back(TopkTask{P.ws_v, P.ws_vidx, P.ws_nsel, P.v_lo, P.v_hi, P.kv, 0});
+        Lo.topk.push_back(TopkTask{P.ws_s, P.ws_sidx, P.ws_nsel + 4, P.s_lo, P.s_hi, P.ks, 0});
+      } else {
+        P.ws_s = P.ws_vidx = P.ws_sidx = P.ws_nsel = -1;
+      }
+    }
+  }
+  for (GridTask& T : Lo.grids) {
+    T.ws_v = Lo.jobs[T.job].pair[0].ws_v;
+    T.ws_U = bp.take(8);
+    T.ws_cand = bp.take(16ll * MAX_PHASES * std::max(T.s_hi - T.s_lo + 1, 1));
+    T.ws_out = bp.take(4ll * GRID_OUT);
+  }
+  // blocks
+  {
+    std::vector<int64_t> kp_off(kv_pool.size());
+    for (size_t i = 0; i < kv_pool.size(); ++i) {
+      kp_off[i] = bp.take(4ll * Lo.nB * dd);
+      const int b = kv_pool[i] / D.Hkv, g = kv_pool[i] % D.Hkv;
+      Lo.pools.push_back(PoolTask{b * dm.k_sb + g * dm.k_sh, dm.k_sl, kp_off[i], 1, 0});
+    }
+    for (HeadDev& H : Lo.heads) {
+      if (H.pattern != MMSA_BLOCK) continue;
+      H.ws_qp = bp.take(4ll * Lo.nB * dd);
+      H.ws_z = bp.take(4ll * Lo.nB * Lo.nB);
+      H.ws_blk_idx = bp.take(4ll * Lo.nB * std::max(H.k_blocks, 1));
+      const int key = H.b * D.Hkv + H.g;
+      const size_t pi = std::lower_bound(kv_pool.begin(), kv_pool.end(), key) - kv_pool.begin();
+      H.ws_kp = kp_off[pi];
+      Lo.pools.push_back(PoolTask{H.q_off, dm.q_sl, H.ws_qp, 0, 0});
+      Lo.blocks.push_back(BlockTask{(int)(&H - &Lo.heads[0]), H.k_blocks, H.ws_qp, H.ws_kp, H.ws_z, H.ws_blk_idx});
+    }
+  }
+  // permutation buffers
+  bp.off = pad_to(bp.off, 256);
+  Lo.gridrow_off = bp.off;
+  for (HeadDev& H : Lo.heads)
+    if (H.row_kind == ROW_GRID) H.ws_row_order = bp.take(4ll * H.n_row_slots);
+  bp.off = pad_to(bp.off, 256);
+  Lo.gridrow_bytes = bp.off - Lo.gridrow_off;
+  {
+    std::vector<int64_t> kg_off(kv_grp.size()), vg_off(kv_grp.size());
+    for (size_t i = 0; i < kv_grp.size(); ++i) {
+      kg_off[i] = bp.take(2ll * dm.L_grp * dd);
+      vg_off[i] = bp.take(2ll * dm.L_grp * dd);
+      const int b = kv_grp[i] / D.Hkv, g = kv_grp[i] % D.Hkv;
+      Lo.gathers.push_back(GatherTask{b * dm.k_sb + g * dm.k_sh, dm.k_sl, dm.ws_pgrp, kg_off[i], dm.L_grp, 1});
+      Lo.gathers.push_back(GatherTask{b * dm.v_sb + g * dm.v_sh, dm.v_sl, dm.ws_pgrp, vg_off[i], dm.L_grp, 2});
+      Lo.max_gather_slots = std::max(Lo.max_gather_slots, dm.L_grp);
+    }
+    for (HeadDev& H : Lo.heads) {
+      if (H.row_kind == ROW_GROUPED) H.ws_row_order = dm.ws_pgrp;
+      if (H.row_kind != ROW_IDENTITY) {
+        H.ws_qperm = bp.take(2ll * H.n_row_slots * dd);
+        H.ws_operm = bp.take(2ll * H.n_row_slots * dd);
+        Lo.gathers.push_back(GatherTask{H.q_off, dm.q_sl, H.ws_row_order, H.ws_qperm, H.n_row_slots, 0});
+        Lo.unperms.push_back(UnpermTask{H.ws_operm, H.ws_row_order, H.o_off, H.n_row_slots, 0});
+        Lo.max_gather_slots = std::max(Lo.max_gather_slots, H.n_row_slots);
+        Lo.max_unperm_slots = std::max(Lo.max_unperm_slots, H.n_row_slots);
+      }
+      if (H.view_kind == VIEW_GROUPED) {
+        const int key = H.b * D.Hkv + H.g;
+        const size_t i = std::lower_bound(kv_grp.begin(), kv_grp.end(), key) - kv_grp.begin();
+        H.ws_kgrp = kg_off[i];
+        H.ws_vgrp = vg_off[i];
+      }
+    }
+  }
+  // plans
+  for (HeadDev& H : Lo.heads) {
+    H.ws_bm = bp.take(8ll * H.nT_rows * H.bm_words);
+    H.ws_info = bp.take(16ll * H.nT_rows);
+    H.ws_pairs = bp.take(8ll * H.nT_rows);
+    if (H.gcap > 0) H.ws_gather = bp.take(4ll * H.nT_rows * H.gcap);
+    Lo.max_tiles = std::max(Lo.max_tiles, H.nT_rows);
+    Lo.max_bm_words = std::max(Lo.max_bm_words, H.bm_words);
+  }
+  Lo.ws_total = pad_to(bp.off, 256);
+
+  // ---- serialize the tables ----
+  Lo.blob.assign(blob_bytes, 0);
+  auto put = [&](int64_t off, const void* src, size_t bytes) {
+    if (bytes) std::memcpy(Lo.blob.data() + off, src, bytes);
+  };
+  std::vector<SegDev> sd;
+  for (const Seg& s : Lo.segs) sd.push_back(SegDev{s.start, s.len, s.modality, s.rank_start});
+  put(tb.off_heads, Lo.heads.data(), sizeof(HeadDev) * Lo.heads.size());
+  put(tb.off_jobs, Lo.jobs.data(), sizeof(EstJob) * Lo.jobs.size());
+  put(tb.off_groups1, Lo.g1.data(), sizeof(EstGroup) * Lo.g1.size());
+  put(tb.off_groups2, Lo.g2.data(), sizeof(EstGroup) * Lo.g2.size());
+  put(tb.off_topk, Lo.topk.data(), sizeof(TopkTask) * Lo.topk.size());
+  put(tb.off_grid, Lo.grids.data(), sizeof(GridTask) * Lo.grids.size());
+  put(tb.off_segs, sd.data(), sizeof(SegDev) * sd.size());
+  put(tb.off_pool, Lo.pools.data(), sizeof(PoolTask) * Lo.pools.size());
+  put(tb.off_block, Lo.blocks.data(), sizeof(BlockTask) * Lo.blocks.size());
+  put(tb.off_gather, Lo.gathers.data(), sizeof(GatherTask) * Lo.gathers.size());
+  put(tb.off_unperm, Lo.unperms.data(), sizeof(UnpermTask) * Lo.unperms.size());
+  return MMSA_OK;
+}
+
+mmsa_status check_ptr(const void* p, const char* name) {
+  if (!p) {
+    set_err("%s is NULL", name);
+    return MMSA_INVALID_ARGUMENT;
+  }
+  if (reinterpret_cast<uintptr_t>(p) % 16 != 0) {
+    set_err("%s is not 16-byte aligned", name);
+    return MMSA_UNSUPPORTED;
+  }
+  return MMSA_OK;
+}
+
+mmsa_status prepare(const mmsa_layer_desc* desc, void* ws, size_t ws_bytes, Layout& Lo) {
+  mmsa_status st = build_layout(desc, Lo);
+  if (st != MMSA_OK) return st;
+  if (Lo.empty) return MMSA_OK;
+  if (!ws) {
+    set_err("workspace is NULL");
+    return MMSA_INVALID_ARGUMENT;
+  }
+  if (reinterpret_cast<uintptr_t>(ws) % 256 != 0) {
+    set_err("workspace is not 256-byte aligned");
+    return MMSA_UNSUPPORTED;
+  }
+  if ((int64_t)ws_bytes < Lo.ws_total) {
+    set_err("workspace has %zu bytes, %lld needed", ws_bytes, (long long)Lo.ws_total);
+    return MMSA_WORKSPACE_TOO_SMALL;
+  }
+  return MMSA_OK;
+}
+
+mmsa_status hip_status(hipError_t e, const char* where) {
+  if (e == hipSuccess) return MMSA_OK;
+  set_err("%s: %s", where, hipGetErrorString(e));
+  return MMSA_HIP_ERROR;
+}
+
+mmsa_status upload(const Layout& Lo, void* ws, hipStream_t s) {
+  return hip_status(hipMemcpyAsync(ws, Lo.blob.data(), Lo.blob.size(), hipMemcpyHostToDevice, s), "table upload");
+}
+
+#define MMSA_TRY(expr)                       \
+  do {                                       \
+    mmsa_status _st = (expr);                \
+    if (_st != MMSA_OK) return _st;          \
+  } while (0)
+#define MMSA_HIP(expr, where) MMSA_TRY(hip_status((expr), where))
+
+}  // namespace
+
+extern "C" {
+
+int32_t mmsa_abi_version(void) { return MMSA_ABI_VERSION; }
+
+const char* mmsa_status_string(mmsa_status s) {
+  switch (s) {
+    case MMSA_OK: return "ok";
+    case MMSA_INVALID_ARGUMENT: return "invalid argument";
+    case MMSA_UNSUPPORTED: return "unsupported";
+    case MMSA_WORKSPACE_TOO_SMALL: return "workspace too small";
+    case MMSA_HIP_ERROR: return "HIP error";
+    default: return "unknown status";
+  }
+}
+
+const char* mmsa_last_error(void) { return g_err.c_str(); }
+
+size_t mmsa_workspace_bytes(const mmsa_layer_desc* desc) {
+  Layout Lo;
+  if (build_layout(desc, Lo) != MMSA_OK) return 0;
+  return (size_t)Lo.ws_total;
+}
+
+mmsa_status mmsa_workspace_view(const mmsa_layer_desc* desc, int32_t buf, int32_t bh, int32_t part,
+                                int64_t* offset_bytes, int64_t* count) {
+  if (!offset_bytes || !count) {
+    set_err("offset_bytes/count is NULL");
+    return MMSA_INVALID_ARGUMENT;
+  }
+  Layout Lo;
+  MMSA_TRY(build_layout(desc, Lo));
+  *offset_bytes = 0;
+  *count = 0;
+  if (Lo.empty) return MMSA_OK;
+  if (bh < 0 || bh >= Lo.BH || part < 0 || part > 3) {
+    set_err("bh=%d / part=%d out of range", bh, part);
+    return MMSA_INVALID_ARGUMENT;
+  }
+  const HeadDev& H = Lo.heads[bh];
+  const std::pair<int, int> sp = Lo.set_of[bh][part];
+  const PairDev* P = sp.first >= 0 ? &Lo.jobs[sp.first].pair[sp.second] : nullptr;
+  const EstJob* J = sp.first >= 0 ? &Lo.jobs[sp.first] : nullptr;
+  switch (buf) {
+    case MMSA_BUF_V_SCORES:
+      if (P) *offset_bytes = P->ws_v, *count = P->Dv;
+      break;
+    case MMSA_BUF_S_SCORES:
+      if (P && P->ws_s >= 0) *offset_bytes = P->ws_s, *count = P->Ds;
+      break;
+    case MMSA_BUF_V_INDEX:
+      if (P && P->ws_vidx >= 0) *offset_bytes = P->ws_vidx, *count = P->kv;
+      break;
+    case MMSA_BUF_S_INDEX:
+      if (P && P->ws_sidx >= 0) *offset_bytes = P->ws_sidx, *count = P->ks;
+      break;
+    case MMSA_BUF_NSEL:
+      if (P && P->ws_nsel >= 0) *offset_bytes = P->ws_nsel, *count = 2;
+      break;
+    case MMSA_BUF_GRID:
+      if (H.grid_task >= 0) {
+        const GridTask& T = Lo.grids[H.grid_task];
+        *offset_bytes = T.ws_out;
+        *count = 3 + std::min(T.w, MAX_PHASES);
+      }
+      break;
+    case MMSA_BUF_BLOCK_INDEX:
+      if (H.pattern == MMSA_BLOCK) *offset_bytes = H.ws_blk_idx, *count = (int64_t)Lo.nB * H.k_blocks;
+      break;
+    case MMSA_BUF_BLOCK_SCORES:
+      if (H.pattern == MMSA_BLOCK) *offset_bytes = H.ws_z, *count = (int64_t)Lo.nB * Lo.nB;
+      break;
+    case MMSA_BUF_ROW_ORDER:
+      if (H.row_kind != ROW_IDENTITY) *offset_bytes = H.ws_row_order, *count = H.n_row_slots;
+      break;
+    case MMSA_BUF_TILE_PAIRS: *offset_bytes = H.ws_pairs, *count = H.nT_rows; break;
+    case MMSA_BUF_TILE_INFO: *offset_bytes = H.ws_info, *count = 4ll * H.nT_rows; break;
+    case MMSA_BUF_EST_STATS:
+      if (J) *offset_bytes = J->ws_stats, *count = 2 * EST_ROWS;
+      break;
+    default: set_err("unknown buffer %d", buf); return MMSA_INVALID_ARGUMENT;
+  }
+  return MMSA_OK;
+}
+
+mmsa_status mmsa_index_meta(const mmsa_layer_desc* desc, int32_t bh, int32_t part, int32_t out[8]) {
+  if (!out) {
+    set_err("out is NULL");
+    return MMSA_INVALID_ARGUMENT;
+  }
+  Layout Lo;
+  MMSA_TRY(build_layout(desc, Lo));
+  for (int i = 0; i < 8; ++i) out[i] = 0;
+  if (Lo.empty) return MMSA_OK;
+  if (bh < 0 || bh >= Lo.BH || part < 0 || part > 3) {
+    set_err("bh=%d / part=%d out of range", bh, part);
+    return MMSA_INVALID_ARGUMENT;
+  }
+  const std::pair<int, int> sp = Lo.set_of[bh][part];
+  if (sp.first < 0) return MMSA_OK;
+  const EstJob& J = Lo.jobs[sp.first];
+  const PairDev& P = J.pair[sp.second];
+  const HeadDev& H = Lo.heads[bh];
+  if (H.grid_task >= 0) {
+    out[0] = 0;
+    out[1] = Lo.grids[H.grid_task].D;
+  } else {
+    out[0] = P.v_lo;
+    out[1] = P.v_hi;
+    out[2] = P.s_lo;
+    out[3] = P.s_hi;
+    out[4] = P.kv;
+    out[5] = P.ks;
+    out[6] = J.kind == JOB_VS_2D ? P.n_k - 1 : 0;
+  }
+  out[7] = J.n_rows;
+  return MMSA_OK;
+}
+
+mmsa_status mmsa_estimate_vs(const mmsa_layer_desc* desc, const void* q, const void* k, void* ws, size_t ws_bytes,
+                             void* stream) {
+  Layout Lo;
+  MMSA_TRY(prepare(desc, ws, ws_bytes, Lo));
+  if (Lo.empty || Lo.jobs.empty()) return MMSA_OK;
+  MMSA_TRY(check_ptr(q, "q"));
+  MMSA_TRY(check_ptr(k, "k"));
+  hipStream_t s = (hipStream_t)stream;
+  char* w = (char*)ws;
+  MMSA_TRY(upload(Lo, ws, s));
+  if (Lo.need_seg) MMSA_HIP(launch_seg_tables(Lo.dm, Lo.tb, w, s), "segment tables");
+  MMSA_HIP(launch_est_pass1(Lo.dm, Lo.tb, w, q, k, Lo.n_chunks1, s), "estimation pass 1");
+  MMSA_HIP(launch_fill_u32(w + Lo.zero_off, 0u, Lo.zero_bytes / 4, s), "score clear");
+  MMSA_HIP(launch_est_pass2(Lo.dm, Lo.tb, w, q, k, Lo.n_chunks2, Lo.max_ds, s), "estimation pass 2");
+  MMSA_HIP(launch_topk(Lo.tb, w, s), "top-k");
+  MMSA_HIP(launch_grid(Lo.dm, Lo.tb, w, Lo.max_strides, s), "grid rule");
+  return MMSA_OK;
+}
+
+mmsa_status mmsa_estimate_blocks(const mmsa_layer_desc* desc, const void* q, const void* k, void* ws,
+                                 size_t ws_bytes, void* stream) {
+  Layout Lo;
+  MMSA_TRY(prepare(desc, ws, ws_bytes, Lo));
+  if (Lo.empty || !Lo.any_block) return MMSA_OK;
+  MMSA_TRY(check_ptr(q, "q"));
+  MMSA_TRY(check_ptr(k, "k"));
+  hipStream_t s = (hipStream_t)stream;
+  MMSA_TRY(upload(Lo, ws, s));
+  MMSA_HIP(launch_block_estimate(Lo.dm, Lo.tb, (char*)ws, q, k, Lo.nB, s), "block estimation");
+  return MMSA_OK;
+}
+
+mmsa_status mmsa_permute(const mmsa_layer_desc* desc, const void* q, const void* k, const void* v, void* ws,
+                         size_t ws_bytes, void* stream) {
+  Layout Lo;
+  MMSA_TRY(prepare(desc, ws, ws_bytes, Lo));
+  if (Lo.empty) return MMSA_OK;
+  MMSA_TRY(check_ptr(q, "q"));
+  MMSA_TRY(check_ptr(k, "k"));
+  MMSA_TRY(check_ptr(v, "v"));
+  hipStream_t s = (hipStream_t)stream;
+  char* w = (char*)ws;
+  MMSA_TRY(upload(Lo, ws, s));
+  if (Lo.need_seg) MMSA_HIP(launch_seg_tables(Lo.dm, Lo.tb, w, s), "segment tables");
+  if (Lo.gridrow_bytes > 0) {
+    MMSA_HIP(launch_fill_u32(w + Lo.gridrow_off, 0xffffffffu, Lo.gridrow_bytes / 4, s), "row order clear");
+    MMSA_HIP(launch_grid_rows(Lo.dm, Lo.tb, w, s), "grid row order");
+  }
+  MMSA_HIP(launch_gather(Lo.dm, Lo.tb, w, q, k, v, Lo.max_gather_slots, s), "gather");
+  MMSA_HIP(launch_plan(Lo.dm, Lo.tb, w, Lo.max_tiles, Lo.max_bm_words, s), "plan");
+  return MMSA_OK;
+}
+
+mmsa_status mmsa_sparse_prefill(const mmsa_layer_desc* desc, const void* q, const void* k, const void* v, void* ws,
+                                size_t ws_bytes, void* o, float* lse, void* stream) {
+  Layout Lo;
+  MMSA_TRY(prepare(desc, ws, ws_bytes, Lo));
+  if (Lo.empty) return MMSA_OK;
+  MMSA_TRY(check_ptr(q, "q"));
+  MMSA_TRY(check_ptr(k, "k"));
+  MMSA_TRY(check_ptr(v, "v"));
+  MMSA_TRY(check_ptr(o, "o"));
+  hipStream_t s = (hipStream_t)stream;
+  MMSA_TRY(upload(Lo, ws, s));
+  MMSA_HIP(launch_attention(Lo.dm, Lo.tb, (char*)ws, q, k, v, o, lse, Lo.max_items, s), "attention");
+  return MMSA_OK;
+}
+
+mmsa_status mmsa_unpermute(const mmsa_layer_desc* desc, void* ws, size_t ws_bytes, void* o, void* stream) {
+  Layout Lo;
+  MMSA_TRY(prepare(desc, ws, ws_bytes, Lo));
+  if (Lo.empty) return MMSA_OK;
+  MMSA_TRY(check_ptr(o, "o"));
+  hipStream_t s = (hipStream_t)stream;
+  MMSA_TRY(upload(Lo, ws, s));
+  MMSA_HIP(launch_unpermute(Lo.dm, Lo.tb, (char*)ws, o, Lo.max_unperm_slots, s), "unpermute");
+  return MMSA_OK;
+}
+
+}  // extern "C"

@@ -33,7 +33,8 @@
  *    a thread-local message.  No C++ exception crosses this interface.
  *  - Budgets above the number of candidates are clamped, not errors.
  *  - NaN or Inf in Q/K/V give undefined (but memory-safe) results.
- *  - Limits: L < 2^22 tokens (tile indices are packed in 16 bits), B*Hq <= 4096.
+ *  - Limits: L < 2^22 tokens (tile indices are packed in 16 bits), B*Hq <= 4096;
+ *    BLOCK heads need L <= 2^20 (one pooled-logit row per query block in LDS).
  */
 #ifndef MMSA_H
 #define MMSA_H
@@ -73,8 +74,7 @@ enum {
 };
 enum { MMSA_TEXT = 0, MMSA_VIDEO = 1 };
 
-/* Flags of mmsa_layer_desc.flags */
-#define MMSA_FLAG_EXPORT_SCORES 1u /* keep the block-score matrix of BLOCK heads in the workspace */
+/* mmsa_layer_desc.flags: reserved, must be 0 */
 
 typedef struct {
   int32_t pattern;      /* MMSA_ASHAPE / VS / BLOCK / GRID                          */
@@ -85,8 +85,8 @@ typedef struct {
   int32_t k_slash;      /* VS: slash diagonals kept (per index set)                  */
   int32_t k_blocks;     /* BLOCK: key blocks kept per query block                    */
   int32_t grid_phases;  /* GRID: number of phases w kept at the winning stride (>=1) */
-  int32_t stride_lo;    /* GRID: smallest stride searched (>= 1)                     */
-  int32_t stride_hi;    /* GRID: largest stride searched (>= stride_lo, <= 4096)     */
+  int32_t stride_lo;    /* GRID: smallest stride searched (>= 16)                    */
+  int32_t stride_hi;    /* GRID: largest stride searched (>= stride_lo, <= 1024)     */
   int32_t grid_clip;    /* GRID: clip constant C of the line score (1..64; 0 -> 8)   */
 } mmsa_head_cfg;
 
@@ -102,7 +102,7 @@ typedef struct {
   int32_t _pad0;
   int64_t q_strides[3], k_strides[3], v_strides[3], o_strides[3]; /* elements: batch, head, row */
   float scale;                      /* softmax scale; 0 -> 1/sqrt(d)                 */
-  uint32_t flags;                   /* MMSA_FLAG_*                                   */
+  uint32_t flags;                   /* reserved: 0                                   */
   const int32_t* kv_head_of;        /* host [Hq] or NULL -> h / (Hq / Hkv)           */
   const mmsa_head_cfg* heads;       /* host [Hq]                                     */
   const mmsa_segment* segs;         /* host [n_segs]; NULL / 0 -> one text segment   */
@@ -117,27 +117,37 @@ size_t mmsa_workspace_bytes(const mmsa_layer_desc* desc);
 
 /* Where a named intermediate of one (batch*Hq + head) `bh` lives in the
  * workspace, so a caller can read it after the stream has drained.
- * `part` selects the index set (0/1: query modality text/video for boundary
- * heads; for 2D heads part = 2*query_modality + key_modality).  On success
- * *offset_bytes and *count (elements) are set; a buffer that does not exist
- * for that head gives count 0.  Buffers: */
+ * `part` selects the index set: 0 for plain heads; the query modality for
+ * Q-boundary heads; 2*query_modality + key_modality for 2D-boundary heads.
+ * On success *offset_bytes and *count (elements) are set; a buffer that does
+ * not exist for that head gives count 0.  Buffers: */
 enum {
-  MMSA_BUF_V_SCORES = 0,   /* float[count]  vertical (column) scores                     */
-  MMSA_BUF_S_SCORES = 1,   /* float[count]  slash (diagonal) scores                      */
-  MMSA_BUF_V_INDEX = 2,    /* int32[count]  selected vertical indices, ascending         */
-  MMSA_BUF_S_INDEX = 3,    /* int32[count]  selected slash indices, ascending            */
-  MMSA_BUF_NSEL = 4,       /* int32[2]      number selected (vertical, slash)            */
-  MMSA_BUF_GRID = 5,       /* int32[2+w]    stride, w, then w ascending phases           */
-  MMSA_BUF_BLOCK_INDEX = 6,/* int32[nB*kb]  per query block, kb key blocks (-1 unused)   */
-  MMSA_BUF_BLOCK_SCORES = 7,/* float[nB*nB] pooled logits (only with EXPORT_SCORES)      */
-  MMSA_BUF_ROW_ORDER = 8,  /* int32[count]  original position of each permuted row, -1 pad */
-  MMSA_BUF_TILE_PAIRS = 9, /* int64[count]  selected (query, key) pairs per query tile    */
-  MMSA_BUF_TILE_WORK = 10, /* int32[count]  64x64 key tiles computed per query tile       */
-  MMSA_BUF_EST_STATS = 11, /* float[2*64*count] row max / row sum of the estimation rows  */
-  MMSA_BUF_SCORE_META = 12 /* int32[4]  vertical candidates [0,a), slash candidates [b,c), slash index shift */
+  MMSA_BUF_V_SCORES = 0,    /* float[count]  vertical (column) scores; grid heads: line scores
+                               per grid coordinate                                          */
+  MMSA_BUF_S_SCORES = 1,    /* float[count]  slash (diagonal) scores                         */
+  MMSA_BUF_V_INDEX = 2,     /* int32[count]  selected vertical indices, ascending            */
+  MMSA_BUF_S_INDEX = 3,     /* int32[count]  selected slash indices, ascending               */
+  MMSA_BUF_NSEL = 4,        /* int32[2]      number selected (vertical, slash)               */
+  MMSA_BUF_GRID = 5,        /* int32[3+w]    stride, w, number of line positions, w phases   */
+  MMSA_BUF_BLOCK_INDEX = 6, /* int32[nB*kb]  per query block, kb key blocks ascending, -1 pad */
+  MMSA_BUF_BLOCK_SCORES = 7,/* float[nB*nB]  pooled logits, row b valid for columns 0..b     */
+  MMSA_BUF_ROW_ORDER = 8,   /* int32[count]  original position of each permuted row, -1 pad  */
+  MMSA_BUF_TILE_PAIRS = 9,  /* int64[count]  selected (query, key) pairs per query tile       */
+  MMSA_BUF_TILE_INFO = 10,  /* int32[4*count] per query tile: key tiles, gathered columns,
+                               cost, rows                                                    */
+  MMSA_BUF_EST_STATS = 11   /* float[2*64]   per estimation row: max of scale*log2(e)*q.k and
+                               the sum of 2^(x - max) over its causal keys                   */
 };
 mmsa_status mmsa_workspace_view(const mmsa_layer_desc* desc, int32_t buf, int32_t bh, int32_t part,
                                 int64_t* offset_bytes, int64_t* count);
+
+/* Host-side facts of one index set (same `bh` / `part` as above), all int32:
+ * out[0..1] vertical candidates [lo, hi); out[2..3] slash candidates [lo, hi);
+ * out[4] vertical budget after clamping; out[5] slash budget after clamping;
+ * out[6] slash index shift (2D: keys of the key modality - 1; else 0);
+ * out[7] number of estimation rows.  For grid heads out[0..1] is the grid
+ * coordinate range [0, D) the stride rule reads. */
+mmsa_status mmsa_index_meta(const mmsa_layer_desc* desc, int32_t bh, int32_t part, int32_t out[8]);
 
 /* 1. Vertical-slash, boundary and grid estimation (MInference summary page,
  *    "Approach": last-64-query attention for vertical/slash lines; MMInference
