@@ -436,7 +436,9 @@ __global__ __launch_bounds__(256) void k_plan(Dims dm, Tables tb, char* ws) {
     const int cost = ntiles + (g_cnt + 63) / 64;
     *info = make_int4(ntiles, g_cnt, cost, nrows);
     *pairs_out = pred[0];
-    if (cost > 0) atomicAdd(wsp<int32_t>(ws, dm.ws_qhist) + queue_bin(cost), 1);
+    // every tile with rows is queued: rows without any selected key still get
+    // their zero output and -inf LSE from the attention kernel
+    atomicAdd(wsp<int32_t>(ws, dm.ws_qhist) + queue_bin(cost), 1);
   }
 }
 
@@ -458,14 +460,15 @@ __global__ __launch_bounds__(1024) void k_queue_scan(Dims dm, char* ws) {
   if (t == QUEUE_BINS - 1) hist[QUEUE_BINS] = incl;
 }
 
-// Place every non-empty (head, tile) in cost order.  grid (tiles, heads).
+// Place every (head, tile) that has rows in cost order.  grid (tiles, heads).
 __global__ __launch_bounds__(64) void k_queue_scatter(Dims dm, Tables tb, char* ws) {
   const int bh = blockIdx.y;
   const HeadDev& H = wsp<const HeadDev>(ws, tb.off_heads)[bh];
   const int t = blockIdx.x * 64 + threadIdx.x;
   if (t >= H.nT_rows) return;
-  const int cost = wsp<const int4>(ws, H.ws_info)[t].z;
-  if (cost <= 0) return;
+  const int4 inf = wsp<const int4>(ws, H.ws_info)[t];
+  if (inf.w <= 0) return;
+  const int cost = inf.z;
   const int pos = atomicAdd(wsp<int32_t>(ws, dm.ws_qhist) + queue_bin(cost), 1);
   wsp<int32_t>(ws, dm.ws_queue)[pos] = (bh << 16) | t;
 }
