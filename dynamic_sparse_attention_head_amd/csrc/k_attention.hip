@@ -19,7 +19,7 @@
 namespace mmsa {
 
 template <int D>
-struct AttnSmem {
+struct AttnSmem {  // 2 stages of K (row-major), V^T (d-major) and key positions
   static constexpr int KS = D + 8;    // K row stride (elements)
   static constexpr int VS = 64 + 8;   // V^T row stride (elements)
   bf16_t K[2][64 * KS];
@@ -33,18 +33,18 @@ __device__ __forceinline__ int vt_slot(int kq) {
   return 32 * c + (q < 4 ? 8 * q : 8 * (q - 4) + 4);
 }
 
+// One (head, query tile) work item.  Ends with a workgroup barrier, so the
+// next item may reuse the LDS at once.
 template <int D>
-__global__ __launch_bounds__(256, 2) void k_attn(Dims dm, Tables tb, char* ws, const bf16_t* __restrict__ q,
-                                                 const bf16_t* __restrict__ k, const bf16_t* __restrict__ v,
-                                                 bf16_t* __restrict__ o, float* __restrict__ lse) {
+__device__ __forceinline__ void attn_item(AttnSmem<D>& sm, const Dims& dm, const Tables& tb, char* ws,
+                                          const bf16_t* __restrict__ q, const bf16_t* __restrict__ k,
+                                          const bf16_t* __restrict__ v, bf16_t* __restrict__ o,
+                                          float* __restrict__ lse, uint32_t item) {
   constexpr int KS = AttnSmem<D>::KS, VS = AttnSmem<D>::VS, NC = D / 32, ND = D / 16;
-  __shared__ AttnSmem<D> sm;
-  const int n_items = wsp<const int32_t>(ws, dm.ws_qhist)[QUEUE_BINS];
-  if ((int)blockIdx.x >= n_items) return;
-  const uint32_t item = wsp<const uint32_t>(ws, dm.ws_queue)[blockIdx.x];
   const int bh = (int)(item >> 16), t = (int)(item & 0xffff);
   const HeadDev& H = wsp<const HeadDev>(ws, tb.off_heads)[bh];
   const int tid = threadIdx.x, w = tid >> 6, lane = tid & 63, qc = lane & 15, g4 = lane >> 4;
+  if (wsp<const int4>(ws, H.ws_info)[t].w <= 0) return;   // a tile of padding rows only (uniform)
 
   // ---- query rows of this wave (B operand of S^T) ----
   const int slot = 64 * t + 16 * w + qc;
@@ -79,75 +79,80 @@ __global__ __launch_bounds__(256, 2) void k_attn(Dims dm, Tables tb, char* ws, c
   const bf16_t* vview = grouped_view ? wsp<const bf16_t>(ws, H.ws_vgrp) : v + H.v_off;
   const int64_t kv_sl = grouped_view ? D : dm.k_sl;
   const int64_t vv_sl = grouped_view ? D : dm.v_sl;
+  const int view_rows = 64 * H.nT_view;
   const int32_t* pgrp = wsp<const int32_t>(ws, dm.ws_pgrp);
   const bf16_t* kg = k + H.k_off;
   const bf16_t* vg = v + H.v_off;
   const bool ashape = H.pattern == MMSA_ASHAPE;
   const int sink = H.sink, window = H.window;
   const int n_chunks = n_tiles + (g_cnt + 63) / 64;
-
-  // chunk descriptor -> (source row, key position) of staged row r
-  // kind 0: view tile `idx`; kind 1: gathered chunk `idx`
-  auto row_src = [&](int kind, int idx, int r, const bf16_t*& kb, const bf16_t*& vb, int64_t& krow,
-                     int64_t& vrow) -> int {
-    if (kind == 0) {
-      const int vr = idx < 0 ? 0 : 64 * idx + r;
-      int pos;
-      if (idx < 0 || vr >= 64 * H.nT_view) pos = -1;
-      else if (grouped_view) pos = pgrp[vr];
-      else pos = vr < dm.L ? vr : -1;
-      kb = kview;
-      vb = vview;
-      krow = (int64_t)vr * kv_sl;
-      vrow = (int64_t)vr * vv_sl;
-      return pos;
-    }
-    const int e = 64 * idx + r;
-    const int pos = e < g_cnt ? glist[e] : -1;
-    kb = kg;
-    vb = vg;
-    krow = (int64_t)(pos < 0 ? 0 : pos) * dm.k_sl;
-    vrow = (int64_t)(pos < 0 ? 0 : pos) * dm.v_sl;
-    return pos;
-  };
+  const int last_row = dm.L - 1;
 
   // ---- staging registers ----
-  constexpr int KCH = D / 32;           // 16-byte K chunks per thread (row r = tid/4)
+  // K: a thread moves 16-byte chunk kc of rows kr0 + j*KRP (coalesced row reads,
+  //    bank-conflict-free row-major LDS stores).
+  // V: a thread moves d-chunk vdc of key quad vkq (4 rows), transposes the 4x8
+  //    block in registers and stores 8-byte runs of 4 keys; lanes of one store
+  //    instruction vary over 16 key quads x 2 d-rows, which hit distinct banks.
+  // Loads are unconditional: a row without a token reads a real (finite) row
+  // through a clamped address and is masked by its key position.
+  constexpr int VDC = D / 8;            // 16-byte d-chunks per row
+  constexpr int KRP = 256 / VDC;        // rows per K pass
+  constexpr int KCH = 64 / KRP;         // K passes (rows per thread)
   uint4 kreg[KCH];
   uint4 vreg[4];
-  int kpreg = -1;
-  const int kr = tid >> 2, kpart = tid & 3;
-  constexpr int VDC = D / 8;            // d-chunks of 8
-  constexpr int VUNITS = 16 * VDC;      // key-quads x d-chunks
-  const bool v_active = tid < VUNITS;
-  const int vkq = tid / VDC, vdc = tid % VDC;
+  int kpreg = KPOS_NONE;
+  const int kc = tid % VDC, kr0 = tid / VDC;
+  const int vkq = lane & 15, vdc = 4 * w + (lane >> 4);
+  const bool v_active = (D == 128) || w < 2;   // wave-uniform
 
-  auto load_chunk = [&](int kind, int idx) {
-    const bf16_t *kb, *vb;
-    int64_t krow, vrow;
-    const int pos = row_src(kind, idx, kr, kb, vb, krow, vrow);
+  auto load_tile = [&](int c) {          // key tile c of the head's key view
+    const int r0 = 64 * c;
 #pragma unroll
     for (int j = 0; j < KCH; ++j) {
-      kreg[j] = make_uint4(0, 0, 0, 0);
-      if (pos >= 0) kreg[j] = ld16(kb + krow + kpart * (D / 4) + 8 * j);
+      int vr = r0 + kr0 + KRP * j;
+      vr = grouped_view ? vr : min(vr, last_row);
+      kreg[j] = ld16(kview + (int64_t)vr * kv_sl + 8 * kc);
     }
     if (v_active) {
 #pragma unroll
       for (int rr = 0; rr < 4; ++rr) {
-        const int p2 = row_src(kind, idx, 4 * vkq + rr, kb, vb, krow, vrow);
-        vreg[rr] = make_uint4(0, 0, 0, 0);
-        if (p2 >= 0) vreg[rr] = ld16(vb + vrow + 8 * vdc);
+        int vr = r0 + 4 * vkq + rr;
+        vr = grouped_view ? vr : min(vr, last_row);
+        vreg[rr] = ld16(vview + (int64_t)vr * vv_sl + 8 * vdc);
       }
     }
-    if (tid < 64) {
-      const int p3 = row_src(kind, idx, tid, kb, vb, krow, vrow);
-      kpreg = p3 >= 0 ? p3 : KPOS_NONE;
+    if (w == 0) {
+      const int vr = r0 + lane;
+      int pos;
+      if (grouped_view) pos = pgrp[min(vr, view_rows - 1)];
+      else pos = vr < dm.L ? vr : -1;
+      kpreg = pos >= 0 ? pos : KPOS_NONE;
     }
   };
-  auto store_chunk = [&](int buf) {
-    bf16_t* kd = sm.K[buf] + kr * KS + kpart * (D / 4);
+  auto load_gather = [&](int n) {        // gathered key columns 64n .. 64n+63
+    const int e0 = 64 * n, el = g_cnt - 1;
 #pragma unroll
-    for (int j = 0; j < KCH; ++j) st16(kd + 8 * j, kreg[j]);
+    for (int j = 0; j < KCH; ++j) {
+      const int p = glist[min(e0 + kr0 + KRP * j, el)];
+      kreg[j] = ld16(kg + (int64_t)p * dm.k_sl + 8 * kc);
+    }
+    if (v_active) {
+#pragma unroll
+      for (int rr = 0; rr < 4; ++rr) {
+        const int p = glist[min(e0 + 4 * vkq + rr, el)];
+        vreg[rr] = ld16(vg + (int64_t)p * dm.v_sl + 8 * vdc);
+      }
+    }
+    if (w == 0) kpreg = (e0 + lane <= el) ? glist[e0 + lane] : KPOS_NONE;
+  };
+  auto load_chunk = [&](int kind, int idx) {
+    if (kind == 0) load_tile(idx);
+    else load_gather(idx);
+  };
+  auto store_chunk = [&](int buf) {
+#pragma unroll
+    for (int j = 0; j < KCH; ++j) st16(sm.K[buf] + (kr0 + KRP * j) * KS + 8 * kc, kreg[j]);
     if (v_active) {
       const uint32_t w0[4] = {vreg[0].x, vreg[0].y, vreg[0].z, vreg[0].w};
       const uint32_t w1[4] = {vreg[1].x, vreg[1].y, vreg[1].z, vreg[1].w};
@@ -157,23 +162,28 @@ __global__ __launch_bounds__(256, 2) void k_attn(Dims dm, Tables tb, char* ws, c
 #pragma unroll
       for (int m = 0; m < 4; ++m) {
         uint2 lo, hi;
-        lo.x = (w0[m] & 0xffffu) | (w1[m] << 16);
-        lo.y = (w2[m] & 0xffffu) | (w3[m] << 16);
-        hi.x = (w0[m] >> 16) | (w1[m] & 0xffff0000u);
-        hi.y = (w2[m] >> 16) | (w3[m] & 0xffff0000u);
+        lo.x = __builtin_amdgcn_perm(w1[m], w0[m], 0x05040100u);
+        lo.y = __builtin_amdgcn_perm(w3[m], w2[m], 0x05040100u);
+        hi.x = __builtin_amdgcn_perm(w1[m], w0[m], 0x07060302u);
+        hi.y = __builtin_amdgcn_perm(w3[m], w2[m], 0x07060302u);
         *reinterpret_cast<uint2*>(vd + (2 * m) * VS) = lo;
         *reinterpret_cast<uint2*>(vd + (2 * m + 1) * VS) = hi;
       }
     }
-    if (tid < 64) sm.kp[buf][tid] = kpreg;
+    if (w == 0) sm.kp[buf][lane] = kpreg;
   };
 
   // tile iteration over the bitmap (uniform across the workgroup)
+  auto uload64 = [&](int i) -> uint64_t {   // a bitmap word, known uniform
+    const uint64_t x = bmrow[i];
+    return ((uint64_t)__builtin_amdgcn_readfirstlane((int)(x >> 32)) << 32) |
+           (uint32_t)__builtin_amdgcn_readfirstlane((int)(uint32_t)x);
+  };
   int wi = 0;
-  uint64_t bits = W > 0 ? bmrow[0] : 0ull;
+  uint64_t bits = W > 0 ? uload64(0) : 0ull;
   auto next_desc = [&](int ci, int& kind, int& idx) {
     if (ci < n_tiles) {
-      while (bits == 0ull && wi + 1 < W) bits = bmrow[++wi];
+      while (bits == 0ull && wi + 1 < W) bits = uload64(++wi);
       const int b = __ffsll((unsigned long long)bits) - 1;
       bits &= bits - 1;
       kind = 0;
@@ -245,11 +255,13 @@ __global__ __launch_bounds__(256, 2) void k_attn(Dims dm, Tables tb, char* ws, c
     for (int e = 0; e < 16; e += 2) {
       const float p0 = exp2f(s[e] - m_use), p1 = exp2f(s[e + 1] - m_use);
       psum += p0 + p1;
-      pk[e >> 1] = pack_bf2(p0, p1);
+      pk[e >> 1] = pack_bf2_hw(p0, p1);
     }
     l_run = l_run * corr + psum;
+    if (__builtin_amdgcn_read_exec() & __ballot(corr != 1.0f)) {   // some row's max moved (wave-uniform test)
 #pragma unroll
-    for (int db = 0; db < ND; ++db) oacc[db] *= corr;
+      for (int db = 0; db < ND; ++db) oacc[db] *= corr;
+    }
     // ---- O^T += V^T . P^T ----
     const bf16_t* Vb = sm.Vt[buf];
 #pragma unroll
@@ -275,8 +287,8 @@ __global__ __launch_bounds__(256, 2) void k_attn(Dims dm, Tables tb, char* ws, c
 #pragma unroll
     for (int db = 0; db < ND; ++db) {
       uint2 pkd;
-      pkd.x = pack_bf2(oacc[db][0] * inv, oacc[db][1] * inv);
-      pkd.y = pack_bf2(oacc[db][2] * inv, oacc[db][3] * inv);
+      pkd.x = pack_bf2_hw(oacc[db][0] * inv, oacc[db][1] * inv);
+      pkd.y = pack_bf2_hw(oacc[db][2] * inv, oacc[db][3] * inv);
       *reinterpret_cast<uint2*>(orow + 16 * db + 4 * g4) = pkd;
     }
     if (lse != nullptr && g4 == 0) {
@@ -286,15 +298,45 @@ __global__ __launch_bounds__(256, 2) void k_attn(Dims dm, Tables tb, char* ws, c
   }
 }
 
+// Persistent workgroups: workgroup i drains the queue segment of XCD i % 8
+// (items popped with an atomic counter), then helps the other segments.
+// Every workgroup exits once all segments are empty.
+template <int D>
+__global__ __launch_bounds__(256, 2) void k_attn(Dims dm, Tables tb, char* ws, const bf16_t* __restrict__ q,
+                                                 const bf16_t* __restrict__ k, const bf16_t* __restrict__ v,
+                                                 bf16_t* __restrict__ o, float* __restrict__ lse) {
+  __shared__ AttnSmem<D> sm;
+  __shared__ int sh_j;
+  const int64_t* seg = wsp<const int64_t>(ws, dm.ws_seg);
+  int32_t* ctr = reinterpret_cast<int32_t*>(wsp<int64_t>(ws, dm.ws_seg) + N_XCD + 1);
+  const int32_t* items = wsp<const int32_t>(ws, dm.ws_enum_item);
+  const int x0 = blockIdx.x % N_XCD;
+  for (int s = 0; s < N_XCD; ++s) {
+    const int x = (x0 + s) % N_XCD;
+    const int64_t beg = seg[x], end = seg[x + 1];
+    while (true) {
+      if (threadIdx.x == 0) sh_j = atomicAdd(&ctr[x], 1);
+      __syncthreads();
+      // the popped index is the same in every lane; saying so keeps the item's
+      // descriptors in scalar registers and its control flow uniform
+      const int64_t e = beg + __builtin_amdgcn_readfirstlane(sh_j);
+      __syncthreads();
+      if (e >= end) break;
+      const uint32_t item = (uint32_t)__builtin_amdgcn_readfirstlane(items[e]);
+      attn_item<D>(sm, dm, tb, ws, q, k, v, o, lse, item);
+    }
+  }
+}
+
 hipError_t launch_attention(const Dims& dm, const Tables& tb, char* ws, const void* q, const void* k, const void* v,
-                            void* o, float* lse, int64_t max_items, hipStream_t s) {
-  if (max_items <= 0) return hipSuccess;
+                            void* o, float* lse, int n_workgroups, hipStream_t s) {
+  if (dm.n_items <= 0 || n_workgroups <= 0) return hipSuccess;
   if (dm.d == 128)
-    k_attn<128><<<(unsigned)max_items, 256, 0, s>>>(dm, tb, ws, (const bf16_t*)q, (const bf16_t*)k,
-                                                     (const bf16_t*)v, (bf16_t*)o, lse);
+    k_attn<128><<<(unsigned)n_workgroups, 256, 0, s>>>(dm, tb, ws, (const bf16_t*)q, (const bf16_t*)k,
+                                                        (const bf16_t*)v, (bf16_t*)o, lse);
   else
-    k_attn<64><<<(unsigned)max_items, 256, 0, s>>>(dm, tb, ws, (const bf16_t*)q, (const bf16_t*)k,
-                                                    (const bf16_t*)v, (bf16_t*)o, lse);
+    k_attn<64><<<(unsigned)n_workgroups, 256, 0, s>>>(dm, tb, ws, (const bf16_t*)q, (const bf16_t*)k,
+                                                       (const bf16_t*)v, (bf16_t*)o, lse);
   return hipGetLastError();
 }
 

@@ -170,11 +170,6 @@ hipError_t launch_unpermute(const Dims& dm, const Tables& tb, char* ws, void* o,
 // Plan compile: one workgroup per (head, query tile).
 // grid (max query tiles, heads), block 256, dynamic LDS = bitmap words.
 // ---------------------------------------------------------------------------
-__device__ __forceinline__ int queue_bin(int cost) {
-  const int b = cost < 512 ? cost : min(QUEUE_BINS - 1, 512 + ((cost - 512) >> 5));
-  return QUEUE_BINS - 1 - b;   // most expensive first
-}
-
 __device__ __forceinline__ void bm_set(uint64_t* bm, int bit) {
   atomicOr((unsigned long long*)&bm[bit >> 6], 1ull << (bit & 63));
 }
@@ -436,51 +431,92 @@ __global__ __launch_bounds__(256) void k_plan(Dims dm, Tables tb, char* ws) {
     const int cost = ntiles + (g_cnt + 63) / 64;
     *info = make_int4(ntiles, g_cnt, cost, nrows);
     *pairs_out = pred[0];
-    // every tile with rows is queued: rows without any selected key still get
-    // their zero output and -inf LSE from the attention kernel
-    atomicAdd(wsp<int32_t>(ws, dm.ws_qhist) + queue_bin(cost), 1);
   }
 }
 
-// Exclusive scan of the queue histogram (one workgroup of 1024).
-__global__ __launch_bounds__(1024) void k_queue_scan(Dims dm, char* ws) {
-  int32_t* hist = wsp<int32_t>(ws, dm.ws_qhist);
-  __shared__ int sh[QUEUE_BINS];
-  const int t = threadIdx.x;
-  sh[t] = hist[t];
-  __syncthreads();
-  for (int off = 1; off < QUEUE_BINS; off <<= 1) {
-    const int v = t >= off ? sh[t - off] : 0;
-    __syncthreads();
-    sh[t] += v;
-    __syncthreads();
-  }
-  const int incl = sh[t];
-  hist[t] = incl - hist[t];          // exclusive start = cursor
-  if (t == QUEUE_BINS - 1) hist[QUEUE_BINS] = incl;
-}
+// ---------------------------------------------------------------------------
+// Attention work queue.  Items (head, query tile) are ordered by queue group
+// (q heads sharing one b, KV head), then query tile descending, then head; the
+// order is cut into N_XCD contiguous segments of equal total cost, one per XCD,
+// so each XCD's workgroups stream one KV head's keys together through their L2
+// and start with the most expensive tiles.
+// ---------------------------------------------------------------------------
 
-// Place every (head, tile) that has rows in cost order.  grid (tiles, heads).
-__global__ __launch_bounds__(64) void k_queue_scatter(Dims dm, Tables tb, char* ws) {
+// Queue position and cost of every (head, tile).  grid (tiles/64, heads).
+__global__ __launch_bounds__(64) void k_queue_enum(Dims dm, Tables tb, char* ws) {
   const int bh = blockIdx.y;
-  const HeadDev& H = wsp<const HeadDev>(ws, tb.off_heads)[bh];
+  const HeadDev* heads = wsp<const HeadDev>(ws, tb.off_heads);
+  const HeadDev& H = heads[bh];
   const int t = blockIdx.x * 64 + threadIdx.x;
   if (t >= H.nT_rows) return;
+  const QGroup G = wsp<const QGroup>(ws, tb.off_qgroups)[H.qgroup];
+  const int32_t* gh = wsp<const int32_t>(ws, tb.off_qgroup_heads);
+  int64_t e = G.item_base;
+  for (int i = G.head_begin; i < G.head_end; ++i) {
+    const int h2 = gh[i];
+    const int nt2 = heads[h2].nT_rows;
+    e += max(0, nt2 - 1 - t);               // items of larger tiles
+    if (h2 < bh && nt2 > t) e += 1;          // same tile, earlier head
+  }
   const int4 inf = wsp<const int4>(ws, H.ws_info)[t];
-  if (inf.w <= 0) return;
-  const int cost = inf.z;
-  const int pos = atomicAdd(wsp<int32_t>(ws, dm.ws_qhist) + queue_bin(cost), 1);
-  wsp<int32_t>(ws, dm.ws_queue)[pos] = (bh << 16) | t;
+  wsp<int32_t>(ws, dm.ws_enum_item)[e] = (bh << 16) | t;
+  // a tile with rows but no selected key still costs a visit (zero output)
+  wsp<int32_t>(ws, dm.ws_enum_cost)[e] = inf.w > 0 ? max(inf.z, 1) : 0;
+}
+
+// Prefix sums of cost in queue order and the N_XCD segment boundaries.
+// One workgroup of 1024 threads.
+__global__ __launch_bounds__(1024) void k_queue_split(Dims dm, char* ws) {
+  const int32_t* cost = wsp<const int32_t>(ws, dm.ws_enum_cost);
+  int64_t* seg = wsp<int64_t>(ws, dm.ws_seg);
+  __shared__ long long part[1024];
+  __shared__ long long target[N_XCD + 1];
+  const int t = threadIdx.x;
+  const int64_t n = dm.n_items;
+  const int64_t per = (n + 1023) / 1024;
+  const int64_t b0 = min(n, t * per), b1 = min(n, b0 + per);
+  long long s = 0;
+  for (int64_t i = b0; i < b1; ++i) s += cost[i];
+  part[t] = s;
+  __syncthreads();
+  for (int off = 1; off < 1024; off <<= 1) {
+    const long long v = t >= off ? part[t - off] : 0;
+    __syncthreads();
+    part[t] += v;
+    __syncthreads();
+  }
+  const long long total = part[1023];
+  if (t <= N_XCD) target[t] = (total * t + N_XCD - 1) / N_XCD;
+  __syncthreads();
+  // segment x (x >= 1) starts right after the item whose cost crosses target[x]
+  long long run = part[t] - s;
+  for (int64_t i = b0; i < b1; ++i) {
+    const long long c = cost[i];
+    for (int x = 1; x < N_XCD; ++x)
+      if (run < target[x] && run + c >= target[x]) seg[x] = i + 1;
+    run += c;
+  }
+  __syncthreads();
+  if (t == 0) {
+    seg[0] = 0;
+    seg[N_XCD] = n;
+    int64_t last = 0;
+    for (int x = 1; x < N_XCD; ++x) {
+      if (total == 0) seg[x] = n;
+      seg[x] = seg[x] < last ? last : (seg[x] > n ? n : seg[x]);
+      last = seg[x];
+    }
+    int32_t* ctr = reinterpret_cast<int32_t*>(seg + N_XCD + 1);
+    for (int x = 0; x < N_XCD; ++x) ctr[x] = 0;
+  }
 }
 
 hipError_t launch_plan(const Dims& dm, const Tables& tb, char* ws, int max_tiles, int max_bm_words,
                        hipStream_t s) {
-  hipError_t e = launch_fill_u32(ws + dm.ws_qhist, 0, QUEUE_BINS + 1, s);
-  if (e != hipSuccess) return e;
   if (max_tiles > 0 && tb.n_heads > 0) {
     k_plan<<<dim3(max_tiles, (unsigned)tb.n_heads), 256, (size_t)max_bm_words * 8, s>>>(dm, tb, ws);
-    k_queue_scan<<<1, QUEUE_BINS, 0, s>>>(dm, ws);
-    k_queue_scatter<<<dim3((max_tiles + 63) / 64, (unsigned)tb.n_heads), 64, 0, s>>>(dm, tb, ws);
+    k_queue_enum<<<dim3((max_tiles + 63) / 64, (unsigned)tb.n_heads), 64, 0, s>>>(dm, tb, ws);
+    k_queue_split<<<1, 1024, 0, s>>>(dm, ws);
   }
   return hipGetLastError();
 }

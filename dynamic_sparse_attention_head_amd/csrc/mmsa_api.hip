@@ -64,6 +64,8 @@ struct Layout {
   std::vector<BlockTask> blocks;
   std::vector<GatherTask> gathers;
   std::vector<UnpermTask> unperms;
+  std::vector<QGroup> qgroups;
+  std::vector<int32_t> qgroup_heads;
   std::vector<char> blob;
   int64_t ws_total = 0;
   int n_chunks1 = 0, n_chunks2 = 0, max_ds = 0, max_strides = 0, nB = 0, max_tiles = 0, max_bm_words = 0;
@@ -533,6 +535,25 @@ mmsa_status build_layout(const mmsa_layer_desc* desc, Layout& Lo) {
   Lo.n_chunks1 = (L + EST_CK - 1) / EST_CK;
   Lo.n_chunks2 = (std::max(L, dm.L_grp) + EST_CK - 1) / EST_CK;
 
+  // ---- queue groups: q heads sharing one (b, KV head) ----
+  {
+    int64_t base = 0;
+    for (int b = 0; b < D.B; ++b) {
+      for (int g = 0; g < D.Hkv; ++g) {
+        QGroup G{(int32_t)Lo.qgroup_heads.size(), 0, base};
+        for (int h = 0; h < D.Hq; ++h) {
+          if (Lo.kvmap[h] != g) continue;
+          const int bh = b * D.Hq + h;
+          Lo.heads[bh].qgroup = (int32_t)Lo.qgroups.size();
+          Lo.qgroup_heads.push_back(bh);
+          base += Lo.heads[bh].nT_rows;
+        }
+        G.head_end = (int32_t)Lo.qgroup_heads.size();
+        if (G.head_end > G.head_begin) Lo.qgroups.push_back(G);
+      }
+    }
+  }
+
   // ---- sizes of the uploaded tables ----
   Tables& tb = Lo.tb;
   tb.n_heads = Lo.BH;
@@ -564,6 +585,7 @@ mmsa_status build_layout(const mmsa_layer_desc* desc, Layout& Lo) {
   tb.n_block = n_block;
   tb.n_gather = n_perm + 2 * (int64_t)kv_grp.size();
   tb.n_unperm = n_perm;
+  tb.n_qgroups = (int64_t)Lo.qgroups.size();
 
   Bump bp;
   tb.off_heads = bp.take((int64_t)sizeof(HeadDev) * tb.n_heads);
@@ -577,16 +599,20 @@ mmsa_status build_layout(const mmsa_layer_desc* desc, Layout& Lo) {
   tb.off_block = bp.take((int64_t)sizeof(BlockTask) * tb.n_block);
   tb.off_gather = bp.take((int64_t)sizeof(GatherTask) * tb.n_gather);
   tb.off_unperm = bp.take((int64_t)sizeof(UnpermTask) * tb.n_unperm);
+  tb.off_qgroups = bp.take((int64_t)sizeof(QGroup) * tb.n_qgroups);
+  tb.off_qgroup_heads = bp.take((int64_t)sizeof(int32_t) * (int64_t)Lo.qgroup_heads.size());
   const int64_t blob_bytes = pad_to(bp.off, 256);
 
   // ---- device buffers ----
   const int dd = D.d;
   dm.ws_flag = bp.take(256);
-  dm.ws_qhist = bp.take(4 * (QUEUE_BINS + 1));
   dm.ws_pgrp = bp.take(4ll * std::max(dm.L_grp, 1));
   dm.ws_gslot = bp.take(4ll * L);
   for (const HeadDev& H : Lo.heads) Lo.max_items += H.nT_rows;
-  dm.ws_queue = bp.take(4 * Lo.max_items);
+  dm.n_items = Lo.max_items;
+  dm.ws_enum_item = bp.take(4 * Lo.max_items);
+  dm.ws_enum_cost = bp.take(4 * Lo.max_items);
+  dm.ws_seg = bp.take(8 * (N_XCD + 1) + 4 * N_XCD);
   // estimation: stats and partials
   for (EstJob& J : Lo.jobs) {
     J.ws_stats = bp.take(8ll * EST_ROWS);
@@ -710,6 +736,8 @@ mmsa_status build_layout(const mmsa_layer_desc* desc, Layout& Lo) {
   put(tb.off_block, Lo.blocks.data(), sizeof(BlockTask) * Lo.blocks.size());
   put(tb.off_gather, Lo.gathers.data(), sizeof(GatherTask) * Lo.gathers.size());
   put(tb.off_unperm, Lo.unperms.data(), sizeof(UnpermTask) * Lo.unperms.size());
+  put(tb.off_qgroups, Lo.qgroups.data(), sizeof(QGroup) * Lo.qgroups.size());
+  put(tb.off_qgroup_heads, Lo.qgroup_heads.data(), sizeof(int32_t) * Lo.qgroup_heads.size());
   return MMSA_OK;
 }
 
@@ -945,7 +973,11 @@ mmsa_status mmsa_sparse_prefill(const mmsa_layer_desc* desc, const void* q, cons
   MMSA_TRY(check_ptr(o, "o"));
   hipStream_t s = (hipStream_t)stream;
   MMSA_TRY(upload(Lo, ws, s));
-  MMSA_HIP(launch_attention(Lo.dm, Lo.tb, (char*)ws, q, k, v, o, lse, Lo.max_items, s), "attention");
+  int dev = 0, n_cu = 0;
+  MMSA_HIP(hipGetDevice(&dev), "hipGetDevice");
+  MMSA_HIP(hipDeviceGetAttribute(&n_cu, hipDeviceAttributeMultiprocessorCount, dev), "CU count");
+  // two resident workgroups per CU (the kernel's LDS and register budget)
+  MMSA_HIP(launch_attention(Lo.dm, Lo.tb, (char*)ws, q, k, v, o, lse, 2 * std::max(n_cu, 1), s), "attention");
   return MMSA_OK;
 }
 

@@ -36,6 +36,15 @@ __device__ __forceinline__ uint32_t pack_bf2(float lo, float hi) {
   return f2bf_bits(lo) | (f2bf_bits(hi) << 16);
 }
 
+// two floats -> packed bf16 pair with the hardware round-to-nearest-even convert
+typedef __bf16 bf16x2_t __attribute__((ext_vector_type(2)));
+__device__ __forceinline__ uint32_t pack_bf2_hw(float lo, float hi) {
+  bf16x2_t v;
+  v[0] = (__bf16)lo;
+  v[1] = (__bf16)hi;
+  return __builtin_bit_cast(uint32_t, v);
+}
+
 __device__ __forceinline__ float shfl_xor_f(float v, int m) { return __shfl_xor(v, m, 64); }
 
 // Merge two (max, sum-of-exp2) pairs of the same row.

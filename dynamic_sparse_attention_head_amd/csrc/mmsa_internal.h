@@ -14,7 +14,7 @@ constexpr int GRP_PAD = 256;    // modality parts of the grouped order are padde
 constexpr int MAX_PHASES = 16;  // grid phases kept at most
 constexpr int MAX_STRIDE = 1024;// largest grid stride searched
 constexpr int GRID_OUT = 3 + MAX_PHASES;  // stride, w, n_line, phases
-constexpr int QUEUE_BINS = 1024;
+constexpr int N_XCD = 8;          // L2 domains (XCDs); workgroup i runs on XCD i % 8
 constexpr int32_t KPOS_NONE = 0x7fffffff;  // key slot without a token (never causal)
 constexpr double SFIX = 1099511627776.0;   // 2^40: fixed-point scale of slash sums
 
@@ -42,7 +42,7 @@ struct HeadDev {
   int32_t grid_task;         // GRID: index into the grid task table, else -1
   int32_t job[2];            // VS family: estimation job per query modality (or [0] only)
   int32_t n_pairs;           // 2D: key modalities with tokens (index sets per region)
-  int32_t _pad;
+  int32_t qgroup;            // queue group: the q heads sharing this head's (b, KV head)
   int64_t q_off, k_off, v_off, o_off;  // element offsets of (b,h) in Q/O and (b,g) in K/V
   int64_t ws_row_order;      // int32[n_row_slots]
   int64_t ws_qperm, ws_operm;// bf16 [n_row_slots][d]
@@ -127,12 +127,19 @@ struct UnpermTask {
   int32_t n_slots, _pad;
 };
 
+// Q heads sharing one (b, KV head): their query tiles are queued together,
+// tile-descending, so concurrent workgroups stream the same K/V through L2.
+struct QGroup {
+  int32_t head_begin, head_end;   // range in the flat head list
+  int64_t item_base;              // first queue position of the group
+};
+
 // Everything the kernels read, placed at the start of the workspace.
 struct Tables {
   int64_t n_heads, n_jobs, n_groups1, n_groups2, n_topk, n_grid, n_segs;
-  int64_t n_pool, n_block, n_gather, n_unperm;
+  int64_t n_pool, n_block, n_gather, n_unperm, n_qgroups;
   int64_t off_heads, off_jobs, off_groups1, off_groups2, off_topk, off_grid, off_segs;
-  int64_t off_pool, off_block, off_gather, off_unperm;
+  int64_t off_pool, off_block, off_gather, off_unperm, off_qgroups, off_qgroup_heads;
 };
 
 // Shapes shared by every kernel of one call.
@@ -143,8 +150,10 @@ struct Dims {
   int64_t q_sb, q_sh, q_sl, k_sb, k_sh, k_sl, v_sb, v_sh, v_sl, o_sb, o_sh, o_sl;
   int64_t ws_pgrp;           // int32[L_grp]: original position at each grouped slot (-1 pad)
   int64_t ws_gslot;          // int32[L]: grouped slot of each position
-  int64_t ws_queue;          // int32 [max items]
-  int64_t ws_qhist;          // int32 [QUEUE_BINS] then int32 n_items
+  int64_t n_items;           // queue length: every (head, query tile)
+  int64_t ws_enum_item;      // int32 [n_items]: (bh << 16) | tile in queue order
+  int64_t ws_enum_cost;      // int32 [n_items]: cost of each queued item
+  int64_t ws_seg;            // int64 [N_XCD + 1] segment starts, then int32 [N_XCD] counters
   int64_t ws_flag;           // int32 debug / status word
 };
 
@@ -171,7 +180,7 @@ hipError_t launch_plan(const Dims& dm, const Tables& tb, char* ws, int max_tiles
                        hipStream_t s);
 
 hipError_t launch_attention(const Dims& dm, const Tables& tb, char* ws, const void* q, const void* k,
-                            const void* v, void* o, float* lse, int64_t max_items, hipStream_t s);
+                            const void* v, void* o, float* lse, int n_workgroups, hipStream_t s);
 hipError_t launch_unpermute(const Dims& dm, const Tables& tb, char* ws, void* o, int max_slots, hipStream_t s);
 
 }  // namespace mmsa
