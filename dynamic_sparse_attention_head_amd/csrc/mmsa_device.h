@@ -15,6 +15,14 @@ __device__ __forceinline__ T* wsp(char* ws, int64_t off) { return reinterpret_ca
 template <class T>
 __device__ __forceinline__ const T* wsp(const char* ws, int64_t off) { return reinterpret_cast<const T*>(ws + off); }
 
+// Read-only tables through the constant address space: with a uniform address
+// these become scalar loads, and the values stay in scalar registers.
+#define MMSA_CONST __attribute__((address_space(4)))
+template <class T>
+__device__ __forceinline__ const MMSA_CONST T* cptr(const char* ws, int64_t off) {
+  return (const MMSA_CONST T*)(ws + off);
+}
+
 __device__ __forceinline__ bf16x8 as_bf16x8(uint4 u) { return __builtin_bit_cast(bf16x8, u); }
 __device__ __forceinline__ uint4 ld16(const void* p) { return *reinterpret_cast<const uint4*>(p); }
 __device__ __forceinline__ void st16(void* p, uint4 v) { *reinterpret_cast<uint4*>(p) = v; }
