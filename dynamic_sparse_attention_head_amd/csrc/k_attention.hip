@@ -3,20 +3,34 @@
 // load only the permuted blocks and keep matrix-core compute dense; the online
 // softmax is the FlashAttention-2 recurrence those kernels build on).
 //
-// One workgroup = one 64-row query tile of one head, 4 waves x 16 rows.  Key
-// chunks of 64 (a whole view tile, or 64 gathered columns) are staged in LDS:
-// K row-major, V transposed (d-major, keys in MFMA k-slot order), so both
-// products run as bf16 16x16x32 MFMA with fp32 accumulation:
-//   S^T (keys x queries) = K . Q^T     -> each lane holds one query's 16 logits
+// One workgroup = one pair of adjacent 64-row query tiles of one head (128
+// rows), 4 waves x 32 rows.  Key chunks of 64 (a whole view tile, or 64
+// gathered columns) are staged once in LDS for both tiles: K row-major, V
+// transposed (d-major, keys in MFMA k-slot order).  The staged chunks are the
+// union of the two tiles' plans; a wave computes only the chunks its own tile
+// selected.  Both products run as bf16 32x32x16 MFMA with fp32 accumulation:
+//   S^T (keys x queries) = K . Q^T     -> each lane holds one query's 32 logits
 //   O^T (d x queries)   += V^T . P^T   -> each lane holds one query's outputs
-// With these transposed layouts a lane owns one query row throughout, so the
-// online-softmax row max needs only two cross-lane shuffles per chunk and the
-// running rescale is a per-lane scalar.  Staging is double-buffered: the next
-// chunk's global loads are in flight while the current chunk is computed.
-// Masking is element-wise on original positions (causal, A-shape window).
+// With these layouts a lane owns one query row throughout, so the online
+// softmax needs one cross-lane exchange per chunk and its rescale is a per-lane
+// scalar.  32 query rows per wave make every LDS fragment feed two 16-row
+// blocks' worth of MFMA work, and 128 rows per workgroup halve the K/V bytes
+// staged per FLOP.  Staging is double-buffered: the next chunk's global loads
+// are in flight while the current chunk is computed.  Masking is element-wise
+// on original positions (causal, A-shape window) and is skipped for chunks
+// whose keys all precede the wave's first row.
 #include "mmsa_device.h"
 
 namespace mmsa {
+
+typedef float floatx16 __attribute__((ext_vector_type(16)));
+
+// D(32x32 fp32) += A(32x16 bf16) * B(16x32 bf16).  Lane l: A row l%32, k-slots
+// 8*(l/32)..+8; B column l%32, same k-slots; D column l%32, rows 8i+4(l/32)+j
+// held at index 4i+j.
+__device__ __forceinline__ floatx16 mfma32(bf16x8 a, bf16x8 b, floatx16 c) {
+  return __builtin_amdgcn_mfma_f32_32x32x16_bf16(a, b, c, 0, 0, 0);
+}
 
 template <int D>
 struct AttnSmem {  // 2 stages of K (row-major), V^T (d-major), key positions and their max
@@ -28,11 +42,10 @@ struct AttnSmem {  // 2 stages of K (row-major), V^T (d-major), key positions an
   int kmax[2];
 };
 
-// k-slot of the first key of key-quad kq (4 consecutive keys) inside V^T rows
-__device__ __forceinline__ int vt_slot(int kq) {
-  const int c = kq >> 3, q = kq & 7;
-  return 32 * c + (q < 4 ? 8 * q : 8 * (q - 4) + 4);
-}
+// V^T slot of the first key of key quad kq (keys 4kq..4kq+3).  Within each
+// 16-key MFMA step, k-slots 8h..8h+7 of lane half h hold keys {4h..4h+3,
+// 8+4h..8+4h+3}, the keys that half holds in the S^T accumulator.
+__device__ __forceinline__ int vt_slot(int kq) { return 16 * (kq >> 2) + 8 * (kq & 1) + 4 * ((kq >> 1) & 1); }
 
 // Raw buffer resource over [base, base + bytes): loads past the end return 0.
 __device__ __forceinline__ __amdgpu_buffer_rsrc_t make_rsrc(const void* base, uint32_t bytes) {
@@ -45,57 +58,87 @@ __device__ __forceinline__ int uniform(int x) { return __builtin_amdgcn_readfirs
 
 constexpr uint32_t OOB = 0x80000000u;   // a buffer offset past every tensor slice
 
-// One (head, query tile) work item.  Ends with a workgroup barrier, so the
+// One (head, query-tile pair) work item.  Ends with a workgroup barrier, so the
 // next item may reuse the LDS at once.
 template <int D>
-__device__ __forceinline__ void attn_item(AttnSmem<D>& sm, const Dims& dm, const Tables& tb, char* ws,
+__device__ __forceinline__ void attn_pair(AttnSmem<D>& sm, const Dims& dm, const Tables& tb, char* ws,
                                           const bf16_t* __restrict__ q, const bf16_t* __restrict__ k,
                                           const bf16_t* __restrict__ v, bf16_t* __restrict__ o,
                                           float* __restrict__ lse, uint32_t item) {
-  constexpr int KS = AttnSmem<D>::KS, VS = AttnSmem<D>::VS, NC = D / 32, ND = D / 16;
-  const int bh = (int)(item >> 16), t = (int)(item & 0xffff);
+  constexpr int KS = AttnSmem<D>::KS, VS = AttnSmem<D>::VS, NS = D / 16, ND = D / 32;
+  const int bh = (int)(item >> 16), pr = (int)(item & 0xffff);
   const MMSA_CONST HeadDev& H = cptr<HeadDev>(ws, tb.off_heads)[bh];
-  const int tid = threadIdx.x, w = tid >> 6, lane = tid & 63, qc = lane & 15, g4 = lane >> 4;
-  const MMSA_CONST int32_t* info = cptr<int32_t>(ws, H.ws_info) + 4 * t;   // tiles, gathered, cost, rows
-  if (info[3] <= 0) return;   // a tile of padding rows only
+  const int tid = threadIdx.x, w = tid >> 6, lane = tid & 63, qc = lane & 31, hh = lane >> 5;
+  const int t0 = 2 * pr, t1 = 2 * pr + 1;
+  const bool has1 = t1 < H.nT_rows;
+  const MMSA_CONST int32_t* inf0 = cptr<int32_t>(ws, H.ws_info) + 4 * t0;   // tiles, gathered, cost, rows
+  const MMSA_CONST int32_t* inf1 = cptr<int32_t>(ws, H.ws_info) + 4 * (has1 ? t1 : t0);
+  const int rows0 = inf0[3], rows1 = has1 ? inf1[3] : 0;
+  if (rows0 <= 0 && rows1 <= 0) return;   // padding tiles only
 
   // ---- query rows of this wave (B operand of S^T) ----
-  const int slot = 64 * t + 16 * w + qc;
-  int qpos;
-  if (H.row_kind == ROW_IDENTITY) qpos = slot < dm.L ? slot : -1;
-  else qpos = wsp<const int32_t>(ws, H.ws_row_order)[slot];
-  bf16x8 qf[NC];
+  const int myt = w < 2 ? t0 : t1;
+  const bool wave_has = (w < 2) ? rows0 > 0 : rows1 > 0;   // wave-uniform
+  const int slot = 64 * myt + 32 * (w & 1) + qc;
+  int qpos = -1;
+  if (wave_has) {
+    if (H.row_kind == ROW_IDENTITY) qpos = slot < dm.L ? slot : -1;
+    else qpos = wsp<const int32_t>(ws, H.ws_row_order)[slot];
+  }
+  bf16x8 qf[NS];
   {
     const bf16_t* qrow = (H.ws_qperm >= 0) ? wsp<const bf16_t>(ws, H.ws_qperm) + (int64_t)slot * D
                                            : q + H.q_off + (int64_t)(qpos < 0 ? 0 : qpos) * dm.q_sl;
+    uint4 u[NS];
 #pragma unroll
-    for (int c = 0; c < NC; ++c) {
-      uint4 u = make_uint4(0, 0, 0, 0);
-      if (qpos >= 0) u = ld16(qrow + 32 * c + 8 * g4);
-      qf[c] = as_bf16x8(u);
+    for (int s = 0; s < NS; ++s) {
+      u[s] = make_uint4(0, 0, 0, 0);
+      if (qpos >= 0) u[s] = ld16(qrow + 16 * s + 8 * hh);
+    }
+    // Consume the fragments here, once: afterwards they are plain register values,
+    // not loads in flight, so the chunk loop never has to wait for them (a wait
+    // there would also wait for the next chunk's prefetch and serialise it).
+#pragma unroll
+    for (int s = 0; s < NS; ++s) {
+      asm volatile("" : "+v"(u[s].x), "+v"(u[s].y), "+v"(u[s].z), "+v"(u[s].w));
+      qf[s] = as_bf16x8(u[s]);
     }
   }
   // smallest valid query position of the wave: chunks whose keys all precede it need no mask
   int wq = qpos >= 0 ? qpos : 0x7fffffff;
 #pragma unroll
-  for (int m = 1; m < 16; m <<= 1) wq = min(wq, __shfl_xor(wq, m, 64));
+  for (int m = 1; m < 32; m <<= 1) wq = min(wq, __shfl_xor(wq, m, 64));
   const int wave_qmin = uniform(wq);
 
-  // ---- plan of this tile ----
+  // ---- plan of the pair ----
   const int W = H.bm_words;
+  const bool grid = H.pattern == MMSA_GRID;
+  const int g_cap = grid ? dm.L : H.gcap;
   // clamped to the buffers' capacities (a plan that was never built stays in bounds)
-  const int n_tiles = min(max(info[0], 0), 64 * W);
-  const int g_cap = (H.pattern == MMSA_GRID) ? dm.L : H.gcap;
-  const int g_cnt = min(max(info[1], 0), g_cap);
-  const MMSA_CONST uint64_t* bmrow = cptr<uint64_t>(ws, H.ws_bm) + (int64_t)t * W;
-  const int32_t* glist = nullptr;
-  if (H.pattern == MMSA_GRID) glist = wsp<const int32_t>(ws, H.ws_row_order);
-  else if (H.gcap > 0) glist = wsp<const int32_t>(ws, H.ws_gather) + (int64_t)t * H.gcap;
+  const int g0 = rows0 > 0 ? min(max(inf0[1], 0), g_cap) : 0;
+  const int g1 = rows1 > 0 ? min(max(inf1[1], 0), g_cap) : 0;
+  const MMSA_CONST uint64_t* bm0 = cptr<uint64_t>(ws, H.ws_bm) + (int64_t)t0 * W;
+  const MMSA_CONST uint64_t* bm1 = cptr<uint64_t>(ws, H.ws_bm) + (int64_t)(has1 ? t1 : t0) * W;
+  const bool use0 = rows0 > 0, use1 = rows1 > 0;
+  int n_union = 0;
+  for (int i = 0; i < W; ++i) n_union += __popcll((use0 ? bm0[i] : 0ull) | (use1 ? bm1[i] : 0ull));
+  // gathered columns: grid tiles share one ascending list (prefixes of it);
+  // vertical-slash tiles each have their own list
+  const int32_t* gl0 = nullptr;
+  const int32_t* gl1 = nullptr;
+  if (grid) {
+    gl0 = gl1 = wsp<const int32_t>(ws, H.ws_row_order);
+  } else if (H.gcap > 0) {
+    gl0 = wsp<const int32_t>(ws, H.ws_gather) + (int64_t)t0 * H.gcap;
+    gl1 = wsp<const int32_t>(ws, H.ws_gather) + (int64_t)(has1 ? t1 : t0) * H.gcap;
+  }
+  const int nch0 = (g0 + 63) / 64, nch1 = (g1 + 63) / 64;
+  const int n_gath = grid ? max(nch0, nch1) : nch0 + nch1;
+  const int n_chunks = n_union + n_gath;
   const bool grouped_view = H.view_kind == VIEW_GROUPED;
   const int32_t* pgrp = wsp<const int32_t>(ws, dm.ws_pgrp);
   const bool ashape = H.pattern == MMSA_ASHAPE;
   const int sink = H.sink, window = H.window;
-  const int n_chunks = n_tiles + (g_cnt + 63) / 64;
 
   // buffer views: the head's key view (tiles) and its original K/V (gathered columns)
   const uint32_t rb_view = grouped_view ? 2u * D : 2u * (uint32_t)dm.k_sl;
@@ -123,7 +166,7 @@ __device__ __forceinline__ void attn_item(AttnSmem<D>& sm, const Dims& dm, const
   constexpr int KCH = 64 / KRP;         // K passes (rows per thread)
   uint4 kreg[KCH];
   uint4 vreg[4];
-  int kpreg = KPOS_NONE;
+  int kpreg = -1;
   const int kc = tid % VDC, kr0 = tid / VDC;
   const int vkq = lane & 15, vdc = 4 * w + (lane >> 4);
   const bool v_active = (D == 128) || w < 2;   // wave-uniform
@@ -141,17 +184,15 @@ __device__ __forceinline__ void attn_item(AttnSmem<D>& sm, const Dims& dm, const
 #pragma unroll
       for (int rr = 0; rr < 4; ++rr) vreg[rr] = bload16(rv_view, vvoff[rr], sv);
     }
-    if (w == 0) {
+    if (w == 0) {   // raw position; -1 (no token) becomes KPOS_NONE at store time
       const int vr = 64 * c + lane;
-      int pos;
-      if (grouped_view) pos = vr < view_rows ? pgrp[vr] : -1;
-      else pos = vr < dm.L ? vr : -1;
-      kpreg = pos >= 0 ? pos : KPOS_NONE;
+      if (grouped_view) kpreg = pgrp[min(vr, view_rows - 1)];
+      else kpreg = vr < dm.L ? vr : -1;
     }
   };
-  auto load_gather = [&](int n) {        // gathered key columns 64n .. 64n+63
+  auto load_gather = [&](const int32_t* glist, int cnt, int n) {   // gathered columns 64n .. 64n+63
     // indices first (clamped, unconditional, so they issue back to back), then rows
-    const int e0 = 64 * n, el = g_cnt - 1;
+    const int e0 = 64 * n, el = cnt - 1;
     int pk[KCH], pv[4];
 #pragma unroll
     for (int j = 0; j < KCH; ++j) pk[j] = glist[min(e0 + kr0 + KRP * j, el)];
@@ -166,7 +207,7 @@ __device__ __forceinline__ void attn_item(AttnSmem<D>& sm, const Dims& dm, const
       for (int rr = 0; rr < 4; ++rr)
         vreg[rr] = bload16(rv, e0 + 4 * vkq + rr <= el ? (uint32_t)pv[rr] * rbv + 16u * vdc : OOB, 0);
     }
-    if (w == 0) kpreg = (e0 + lane <= el) ? p3 : KPOS_NONE;
+    if (w == 0) kpreg = (e0 + lane <= el) ? p3 : -1;
   };
   auto store_chunk = [&](int buf) {
 #pragma unroll
@@ -189,133 +230,172 @@ __device__ __forceinline__ void attn_item(AttnSmem<D>& sm, const Dims& dm, const
       }
     }
     if (w == 0) {
-      sm.kp[buf][lane] = kpreg;
-      int mx = kpreg;
+      const int kpos = kpreg >= 0 ? kpreg : KPOS_NONE;
+      sm.kp[buf][lane] = kpos;
+      int mx = kpos;
 #pragma unroll
       for (int m = 1; m < 64; m <<= 1) mx = max(mx, __shfl_xor(mx, m, 64));
       if (lane == 0) sm.kmax[buf] = mx;
     }
   };
 
-  // tile iteration over the bitmap (uniform across the workgroup)
-  auto uload64 = [&](int i) -> uint64_t { return bmrow[i]; };
-  int wi = 0;
-  uint64_t bits = W > 0 ? uload64(0) : 0ull;
-  auto load_next = [&](int ci) {
-    if (ci < n_tiles) {
-      while (bits == 0ull && wi + 1 < W) bits = uload64(++wi);
-      const int b = __ffsll((unsigned long long)bits) - 1;
-      bits &= bits - 1;
+  // Chunk sequence (uniform across the workgroup): the union of both tiles'
+  // key tiles, highest first -- workgroups on neighbouring query tiles then
+  // stream the same key tiles at about the same time and share them in L2, and
+  // the diagonal (the only chunk a causal tile needs masked) comes first -- then
+  // the gathered columns.  The returned bits say which tiles (bit 0: first,
+  // bit 1: second) selected the chunk.
+  int wi = W;
+  uint64_t bits = 0, wb0 = 0, wb1 = 0;
+  auto load_next = [&](int ci) -> int {
+    if (ci < n_union) {
+      while (bits == 0ull && wi > 0) {
+        --wi;
+        wb0 = use0 ? bm0[wi] : 0ull;
+        wb1 = use1 ? bm1[wi] : 0ull;
+        bits = wb0 | wb1;
+      }
+      const int b = bits ? 63 - __clzll((long long)bits) : -1;
+      bits &= ~(1ull << (b & 63));
       load_tile(b < 0 ? (view_rows + 63) / 64 : 64 * wi + b);   // (b < 0 only for a corrupt plan)
-    } else {
-      load_gather(ci - n_tiles);
+      return b < 0 ? 0 : (int)(((wb0 >> b) & 1ull) | (((wb1 >> b) & 1ull) << 1));
     }
+    const int n = ci - n_union;
+    if (grid) {
+      load_gather(gl0, max(g0, g1), n);
+      return (64 * n < g0 ? 1 : 0) | (64 * n < g1 ? 2 : 0);
+    }
+    if (n < nch0) {
+      load_gather(gl0, g0, n);
+      return 1;
+    }
+    load_gather(gl1, g1, n - nch0);
+    return 2;
   };
 
-  floatx4 oacc[ND];
+  floatx16 oacc[ND];
 #pragma unroll
-  for (int db = 0; db < ND; ++db) oacc[db] = floatx4{0.f, 0.f, 0.f, 0.f};
+  for (int db = 0; db < ND; ++db)
+#pragma unroll
+    for (int e = 0; e < 16; ++e) oacc[db][e] = 0.f;
   float m_run = -INFINITY, l_run = 0.f;
   const float sl2 = dm.scale_log2;
+  const int wbit = w < 2 ? 1 : 2;
 
+  int memb_cur = 0;
   if (n_chunks > 0) {
-    load_next(0);
+    memb_cur = load_next(0);
     store_chunk(0);
     __syncthreads();
   }
   for (int ci = 0; ci < n_chunks; ++ci) {
     const int buf = ci & 1;
     const bool has_next = ci + 1 < n_chunks;
-    if (has_next) load_next(ci + 1);
-    // ---- S^T = K . Q^T ----
-    const bf16_t* Kb = sm.K[buf];
-    floatx4 sacc[4];
+    int memb_next = 0;
+    if (has_next) memb_next = load_next(ci + 1);
+    if (wave_has && (memb_cur & wbit)) {
+      // ---- S^T = K . Q^T ----
+      const bf16_t* Kb = sm.K[buf];
+      floatx16 sacc[2];
 #pragma unroll
-    for (int kb = 0; kb < 4; ++kb) {
-      sacc[kb] = floatx4{0.f, 0.f, 0.f, 0.f};
+      for (int kb = 0; kb < 2; ++kb) {
 #pragma unroll
-      for (int c = 0; c < NC; ++c) {
-        const bf16x8 a = as_bf16x8(ld16(Kb + (16 * kb + qc) * KS + 32 * c + 8 * g4));
-        sacc[kb] = mfma16(a, qf[c], sacc[kb]);
+        for (int e = 0; e < 16; ++e) sacc[kb][e] = 0.f;
+#pragma unroll
+        for (int s = 0; s < NS; ++s) {
+          const bf16x8 a = as_bf16x8(ld16(Kb + (32 * kb + qc) * KS + 16 * s + 8 * hh));
+          sacc[kb] = mfma32(a, qf[s], sacc[kb]);
+        }
       }
-    }
-    // ---- mask (only chunks crossing the causal edge, or A-shape), online softmax ----
-    const bool full = !ashape && uniform(sm.kmax[buf]) <= wave_qmin;
-    if (!full) {
-      // branch-free selects (bitwise boolean ops, no short-circuit evaluation)
+      // ---- mask (only chunks crossing the causal edge, or A-shape), online softmax ----
+      const bool full = !ashape && uniform(sm.kmax[buf]) <= wave_qmin;
+      if (!full) {
+        // branch-free selects (bitwise boolean ops, no short-circuit evaluation)
 #pragma unroll
-      for (int kb = 0; kb < 4; ++kb) {
-        const int4 kk = *reinterpret_cast<const int4*>(&sm.kp[buf][16 * kb + 4 * g4]);
-        const int kpv[4] = {kk.x, kk.y, kk.z, kk.w};
+        for (int kb = 0; kb < 2; ++kb) {
 #pragma unroll
-        for (int i = 0; i < 4; ++i) {
-          bool ok = kpv[i] <= qpos;
-          if (ashape) ok = ok & ((kpv[i] < sink) | (qpos - kpv[i] < window));
-          sacc[kb][i] = ok ? sacc[kb][i] : -INFINITY;
+          for (int i = 0; i < 4; ++i) {
+            const int4 kk = *reinterpret_cast<const int4*>(&sm.kp[buf][32 * kb + 8 * i + 4 * hh]);
+            const int kpv[4] = {kk.x, kk.y, kk.z, kk.w};
+#pragma unroll
+            for (int j = 0; j < 4; ++j) {
+              bool ok = kpv[j] <= qpos;
+              if (ashape) ok = ok & ((kpv[j] < sink) | (qpos - kpv[j] < window));
+              sacc[kb][4 * i + j] = ok ? sacc[kb][4 * i + j] : -INFINITY;
+            }
+          }
+        }
+      }
+      float mx = -INFINITY;
+#pragma unroll
+      for (int kb = 0; kb < 2; ++kb)
+#pragma unroll
+        for (int e = 0; e < 16; e += 4)
+          mx = fmaxf(fmaxf(mx, fmaxf(sacc[kb][e], sacc[kb][e + 1])), fmaxf(sacc[kb][e + 2], sacc[kb][e + 3]));
+      mx = fmaxf(mx, shfl_xor_f(mx, 32));
+      const float m_new = fmaxf(m_run, mx * sl2);
+      const float m_use = (m_new == -INFINITY) ? 0.f : m_new;
+      const float corr = __builtin_amdgcn_exp2f(m_run - m_use);
+      m_run = m_new;
+      float psum = 0.f;
+      uint32_t pk[16];
+#pragma unroll
+      for (int kb = 0; kb < 2; ++kb) {
+#pragma unroll
+        for (int e = 0; e < 16; e += 2) {
+          const float p0 = __builtin_amdgcn_exp2f(fmaf(sacc[kb][e], sl2, -m_use));
+          const float p1 = __builtin_amdgcn_exp2f(fmaf(sacc[kb][e + 1], sl2, -m_use));
+          psum += p0 + p1;
+          pk[8 * kb + (e >> 1)] = pack_bf2_hw(p0, p1);
+        }
+      }
+      l_run = l_run * corr + psum;
+      if (__ballot(corr != 1.0f)) {   // some row's max moved (wave-uniform test)
+#pragma unroll
+        for (int db = 0; db < ND; ++db) oacc[db] *= corr;
+      }
+      // ---- O^T += V^T . P^T ----
+      const bf16_t* Vb = sm.Vt[buf];
+#pragma unroll
+      for (int st = 0; st < 4; ++st) {   // 16-key steps: accumulator values 8(st&1).. of key block st>>1
+        const bf16x8 pb =
+            as_bf16x8(make_uint4(pk[4 * st], pk[4 * st + 1], pk[4 * st + 2], pk[4 * st + 3]));
+#pragma unroll
+        for (int db = 0; db < ND; ++db) {
+          const bf16x8 a = as_bf16x8(ld16(Vb + (32 * db + qc) * VS + 16 * st + 8 * hh));
+          oacc[db] = mfma32(a, pb, oacc[db]);
         }
       }
     }
-    float mx = -INFINITY;
-#pragma unroll
-    for (int kb = 0; kb < 4; ++kb)
-      mx = fmaxf(fmaxf(fmaxf(mx, sacc[kb][0]), fmaxf(sacc[kb][1], sacc[kb][2])), sacc[kb][3]);
-    mx = fmaxf(mx, shfl_xor_f(mx, 16));
-    mx = fmaxf(mx, shfl_xor_f(mx, 32));
-    const float m_new = fmaxf(m_run, mx * sl2);
-    const float m_use = (m_new == -INFINITY) ? 0.f : m_new;
-    const float corr = __builtin_amdgcn_exp2f(m_run - m_use);
-    m_run = m_new;
-    float psum = 0.f;
-    uint32_t pk[8];
-#pragma unroll
-    for (int e = 0; e < 16; e += 2) {
-      const float p0 = __builtin_amdgcn_exp2f(fmaf(sacc[e >> 2][e & 3], sl2, -m_use));
-      const float p1 = __builtin_amdgcn_exp2f(fmaf(sacc[(e + 1) >> 2][(e + 1) & 3], sl2, -m_use));
-      psum += p0 + p1;
-      pk[e >> 1] = pack_bf2_hw(p0, p1);
-    }
-    l_run = l_run * corr + psum;
-    if (__ballot(corr != 1.0f)) {   // some row's max moved (wave-uniform test)
-#pragma unroll
-      for (int db = 0; db < ND; ++db) oacc[db] *= corr;
-    }
-    // ---- O^T += V^T . P^T ----
-    const bf16_t* Vb = sm.Vt[buf];
-#pragma unroll
-    for (int cc = 0; cc < 2; ++cc) {
-      const bf16x8 pb = as_bf16x8(make_uint4(pk[4 * cc], pk[4 * cc + 1], pk[4 * cc + 2], pk[4 * cc + 3]));
-#pragma unroll
-      for (int db = 0; db < ND; ++db) {
-        const bf16x8 a = as_bf16x8(ld16(Vb + (16 * db + qc) * VS + 32 * cc + 8 * g4));
-        oacc[db] = mfma16(a, pb, oacc[db]);
-      }
-    }
     if (has_next) store_chunk(buf ^ 1);
+    memb_cur = memb_next;
     __syncthreads();
   }
 
   // ---- epilogue ----
-  float l_tot = l_run + shfl_xor_f(l_run, 16);
-  l_tot += shfl_xor_f(l_tot, 32);
+  const float l_tot = l_run + shfl_xor_f(l_run, 32);
   if (qpos >= 0) {
     const float inv = l_tot > 0.f ? 1.0f / l_tot : 0.f;
     bf16_t* orow = (H.ws_operm >= 0) ? wsp<bf16_t>(ws, H.ws_operm) + (int64_t)slot * D
                                      : o + H.o_off + (int64_t)qpos * dm.o_sl;
 #pragma unroll
     for (int db = 0; db < ND; ++db) {
-      uint2 pkd;
-      pkd.x = pack_bf2_hw(oacc[db][0] * inv, oacc[db][1] * inv);
-      pkd.y = pack_bf2_hw(oacc[db][2] * inv, oacc[db][3] * inv);
-      *reinterpret_cast<uint2*>(orow + 16 * db + 4 * g4) = pkd;
+#pragma unroll
+      for (int i = 0; i < 4; ++i) {
+        uint2 pkd;
+        pkd.x = pack_bf2_hw(oacc[db][4 * i] * inv, oacc[db][4 * i + 1] * inv);
+        pkd.y = pack_bf2_hw(oacc[db][4 * i + 2] * inv, oacc[db][4 * i + 3] * inv);
+        *reinterpret_cast<uint2*>(orow + 32 * db + 8 * i + 4 * hh) = pkd;
+      }
     }
-    if (lse != nullptr && g4 == 0) {
+    if (lse != nullptr && hh == 0) {
       const float val = l_tot > 0.f ? (m_run + log2f(l_tot)) * 0.69314718055994531f : -INFINITY;
       lse[((int64_t)H.b * dm.Hq + H.h) * dm.L + qpos] = val;
     }
   }
 }
 
-// Persistent workgroups: workgroup i drains the queue segment of XCD i % 8
+// Persistent workgroups: a workgroup drains the queue segment of its own XCD
 // (items popped with an atomic counter), then helps the other segments.
 // Every workgroup exits once all segments are empty.
 template <int D>
@@ -327,7 +407,8 @@ __global__ __launch_bounds__(256, 2) void k_attn(Dims dm, Tables tb, char* ws, c
   const MMSA_CONST int64_t* seg = cptr<int64_t>(ws, dm.ws_seg);
   int32_t* ctr = reinterpret_cast<int32_t*>(wsp<int64_t>(ws, dm.ws_seg) + N_XCD + 1);
   const int32_t* items = wsp<const int32_t>(ws, dm.ws_enum_item);
-  const int x0 = blockIdx.x % N_XCD;
+  // this workgroup's XCD (hardware XCC id), so its L2 serves its segment
+  const int x0 = (int)(__builtin_amdgcn_s_getreg((3 << 11) | (0 << 6) | 20) & (N_XCD - 1));
   for (int s = 0; s < N_XCD; ++s) {
     const int x = (x0 + s) % N_XCD;
     const int64_t beg = seg[x], end = seg[x + 1];
@@ -340,7 +421,7 @@ __global__ __launch_bounds__(256, 2) void k_attn(Dims dm, Tables tb, char* ws, c
       __syncthreads();
       if (e >= end) break;
       const uint32_t item = (uint32_t)__builtin_amdgcn_readfirstlane(items[e]);
-      attn_item<D>(sm, dm, tb, ws, q, k, v, o, lse, item);
+      attn_pair<D>(sm, dm, tb, ws, q, k, v, o, lse, item);
     }
   }
 }

@@ -435,33 +435,40 @@ __global__ __launch_bounds__(256) void k_plan(Dims dm, Tables tb, char* ws) {
 }
 
 // ---------------------------------------------------------------------------
-// Attention work queue.  Items (head, query tile) are ordered by queue group
-// (q heads sharing one b, KV head), then query tile descending, then head; the
+// Attention work queue.  Items (head, pair of adjacent query tiles) are ordered
+// by queue group (q heads sharing one b, KV head), then pair descending, then
+// head; the
 // order is cut into N_XCD contiguous segments of equal total cost, one per XCD,
 // so each XCD's workgroups stream one KV head's keys together through their L2
 // and start with the most expensive tiles.
 // ---------------------------------------------------------------------------
 
-// Queue position and cost of every (head, tile).  grid (tiles/64, heads).
+// Queue position and cost of every (head, pair of adjacent query tiles).
+// grid (pairs/64, heads).
 __global__ __launch_bounds__(64) void k_queue_enum(Dims dm, Tables tb, char* ws) {
   const int bh = blockIdx.y;
   const HeadDev* heads = wsp<const HeadDev>(ws, tb.off_heads);
   const HeadDev& H = heads[bh];
-  const int t = blockIdx.x * 64 + threadIdx.x;
-  if (t >= H.nT_rows) return;
+  const int np = (H.nT_rows + 1) / 2;
+  const int pr = blockIdx.x * 64 + threadIdx.x;
+  if (pr >= np) return;
   const QGroup G = wsp<const QGroup>(ws, tb.off_qgroups)[H.qgroup];
   const int32_t* gh = wsp<const int32_t>(ws, tb.off_qgroup_heads);
   int64_t e = G.item_base;
   for (int i = G.head_begin; i < G.head_end; ++i) {
     const int h2 = gh[i];
-    const int nt2 = heads[h2].nT_rows;
-    e += max(0, nt2 - 1 - t);               // items of larger tiles
-    if (h2 < bh && nt2 > t) e += 1;          // same tile, earlier head
+    const int np2 = (heads[h2].nT_rows + 1) / 2;
+    e += max(0, np2 - 1 - pr);               // items of larger pairs
+    if (h2 < bh && np2 > pr) e += 1;          // same pair, earlier head
   }
-  const int4 inf = wsp<const int4>(ws, H.ws_info)[t];
-  wsp<int32_t>(ws, dm.ws_enum_item)[e] = (bh << 16) | t;
-  // a tile with rows but no selected key still costs a visit (zero output)
-  wsp<int32_t>(ws, dm.ws_enum_cost)[e] = inf.w > 0 ? max(inf.z, 1) : 0;
+  const int4 i0 = wsp<const int4>(ws, H.ws_info)[2 * pr];
+  const int4 i1 = (2 * pr + 1 < H.nT_rows) ? wsp<const int4>(ws, H.ws_info)[2 * pr + 1] : make_int4(0, 0, 0, 0);
+  const int c0 = i0.w > 0 ? i0.z : 0, c1 = i1.w > 0 ? i1.z : 0;
+  // the union of the two tiles' chunks, estimated; a pair with rows but no
+  // selected key still costs a visit (zero output)
+  const int cost = max(c0, c1) + min(c0, c1) / 2;
+  wsp<int32_t>(ws, dm.ws_enum_item)[e] = (bh << 16) | pr;
+  wsp<int32_t>(ws, dm.ws_enum_cost)[e] = (i0.w > 0 || i1.w > 0) ? max(cost, 1) : 0;
 }
 
 // Prefix sums of cost in queue order and the N_XCD segment boundaries.
@@ -515,7 +522,7 @@ hipError_t launch_plan(const Dims& dm, const Tables& tb, char* ws, int max_tiles
                        hipStream_t s) {
   if (max_tiles > 0 && tb.n_heads > 0) {
     k_plan<<<dim3(max_tiles, (unsigned)tb.n_heads), 256, (size_t)max_bm_words * 8, s>>>(dm, tb, ws);
-    k_queue_enum<<<dim3((max_tiles + 63) / 64, (unsigned)tb.n_heads), 64, 0, s>>>(dm, tb, ws);
+    k_queue_enum<<<dim3((max_tiles / 2 + 64) / 64, (unsigned)tb.n_heads), 64, 0, s>>>(dm, tb, ws);
     k_queue_split<<<1, 1024, 0, s>>>(dm, ws);
   }
   return hipGetLastError();

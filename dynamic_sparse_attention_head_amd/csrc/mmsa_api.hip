@@ -546,7 +546,7 @@ mmsa_status build_layout(const mmsa_layer_desc* desc, Layout& Lo) {
           const int bh = b * D.Hq + h;
           Lo.heads[bh].qgroup = (int32_t)Lo.qgroups.size();
           Lo.qgroup_heads.push_back(bh);
-          base += Lo.heads[bh].nT_rows;
+          base += (Lo.heads[bh].nT_rows + 1) / 2;   // queue items are pairs of query tiles
         }
         G.head_end = (int32_t)Lo.qgroup_heads.size();
         if (G.head_end > G.head_begin) Lo.qgroups.push_back(G);
@@ -608,7 +608,7 @@ mmsa_status build_layout(const mmsa_layer_desc* desc, Layout& Lo) {
   dm.ws_flag = bp.take(256);
   dm.ws_pgrp = bp.take(4ll * std::max(dm.L_grp, 1));
   dm.ws_gslot = bp.take(4ll * L);
-  for (const HeadDev& H : Lo.heads) Lo.max_items += H.nT_rows;
+  for (const HeadDev& H : Lo.heads) Lo.max_items += (H.nT_rows + 1) / 2;
   dm.n_items = Lo.max_items;
   dm.ws_enum_item = bp.take(4 * Lo.max_items);
   dm.ws_enum_cost = bp.take(4 * Lo.max_items);

@@ -150,8 +150,8 @@ struct Dims {
   int64_t q_sb, q_sh, q_sl, k_sb, k_sh, k_sl, v_sb, v_sh, v_sl, o_sb, o_sh, o_sl;
   int64_t ws_pgrp;           // int32[L_grp]: original position at each grouped slot (-1 pad)
   int64_t ws_gslot;          // int32[L]: grouped slot of each position
-  int64_t n_items;           // queue length: every (head, query tile)
-  int64_t ws_enum_item;      // int32 [n_items]: (bh << 16) | tile in queue order
+  int64_t n_items;           // queue length: every (head, pair of adjacent query tiles)
+  int64_t ws_enum_item;      // int32 [n_items]: (bh << 16) | pair in queue order
   int64_t ws_enum_cost;      // int32 [n_items]: cost of each queued item
   int64_t ws_seg;            // int64 [N_XCD + 1] segment starts, then int32 [N_XCD] counters
   int64_t ws_flag;           // int32 debug / status word
