@@ -27,6 +27,12 @@ HIPCC_FLAGS = [
     "-Xclang", "-target-feature", "-Xclang", "-packed-fp32-ops",
     "-Wno-unused-result",
 ]
+# Per-source additions.  The attention kernel never sees a NaN (masked logits are
+# -inf, never NaN), so its max/min need no NaN quieting: IEEE mode off lets them
+# map to single v_max/v_max3 instructions.
+FILE_FLAGS = {
+    "k_attention.hip": ["-fno-honor-nans", "-mno-amdgpu-ieee"],
+}
 
 
 def hipcc():
@@ -35,7 +41,7 @@ def hipcc():
 
 
 def _compile(src, obj, extra):
-    cmd = [hipcc(), *HIPCC_FLAGS, *extra, "-c", src, "-o", obj]
+    cmd = [hipcc(), *HIPCC_FLAGS, *FILE_FLAGS.get(os.path.basename(src), []), *extra, "-c", src, "-o", obj]
     r = subprocess.run(cmd, capture_output=True, text=True)
     if r.returncode != 0:
         raise RuntimeError(f"hipcc failed for {src}:\n{r.stdout}\n{r.stderr}")

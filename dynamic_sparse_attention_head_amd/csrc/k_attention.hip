@@ -57,6 +57,8 @@ __device__ __forceinline__ uint4 bload16(__amdgpu_buffer_rsrc_t r, uint32_t voff
 __device__ __forceinline__ int uniform(int x) { return __builtin_amdgcn_readfirstlane(x); }
 
 constexpr uint32_t OOB = 0x80000000u;   // a buffer offset past every tensor slice
+constexpr float LAZY_LOG2 = 8.0f;       // stale-max slack of the online softmax (log2 units)
+__device__ constexpr bf16x2_t ONES_BF2 = {(__bf16)1.0f, (__bf16)1.0f};
 
 // One (head, query-tile pair) work item.  Ends with a workgroup barrier, so the
 // next item may reuse the LDS at once.
@@ -176,10 +178,12 @@ __device__ __forceinline__ void attn_pair(AttnSmem<D>& sm, const Dims& dm, const
 #pragma unroll
   for (int rr = 0; rr < 4; ++rr) vvoff[rr] = (uint32_t)(4 * vkq + rr) * rbv_view + 16u * vdc;
 
-  auto load_tile = [&](int c) {          // key tile c of the head's key view
-    const uint32_t sk = (uint32_t)(64 * c) * rb_view, sv = (uint32_t)(64 * c) * rbv_view;
-#pragma unroll
-    for (int j = 0; j < KCH; ++j) kreg[j] = bload16(rk_view, kvoff[j], sk);
+  // A chunk is staged in two halves so that only one half's registers are live
+  // at a time: V (and the key positions) are loaded when the chunk is chosen and
+  // stored at the end of the iteration; K is loaded after the current chunk's
+  // S^T products and stored right after them.
+  auto loadv_tile = [&](int c) {         // key tile c of the head's key view
+    const uint32_t sv = (uint32_t)(64 * c) * rbv_view;
     if (v_active) {
 #pragma unroll
       for (int rr = 0; rr < 4; ++rr) vreg[rr] = bload16(rv_view, vvoff[rr], sv);
@@ -190,18 +194,19 @@ __device__ __forceinline__ void attn_pair(AttnSmem<D>& sm, const Dims& dm, const
       else kpreg = vr < dm.L ? vr : -1;
     }
   };
-  auto load_gather = [&](const int32_t* glist, int cnt, int n) {   // gathered columns 64n .. 64n+63
-    // indices first (clamped, unconditional, so they issue back to back), then rows
-    const int e0 = 64 * n, el = cnt - 1;
-    int pk[KCH], pv[4];
+  auto loadk_tile = [&](int c) {
+    const uint32_t sk = (uint32_t)(64 * c) * rb_view;
 #pragma unroll
-    for (int j = 0; j < KCH; ++j) pk[j] = glist[min(e0 + kr0 + KRP * j, el)];
+    for (int j = 0; j < KCH; ++j) kreg[j] = bload16(rk_view, kvoff[j], sk);
+  };
+  // gathered columns 64n .. 64n+63 of a list: indices first (clamped,
+  // unconditional, so they issue back to back), then rows
+  auto loadv_gather = [&](const int32_t* glist, int cnt, int n) {
+    const int e0 = 64 * n, el = cnt - 1;
+    int pv[4];
 #pragma unroll
     for (int rr = 0; rr < 4; ++rr) pv[rr] = glist[min(e0 + 4 * vkq + rr, el)];
     const int p3 = glist[min(e0 + lane, el)];
-#pragma unroll
-    for (int j = 0; j < KCH; ++j)
-      kreg[j] = bload16(rk, e0 + kr0 + KRP * j <= el ? (uint32_t)pk[j] * rbk + 16u * kc : OOB, 0);
     if (v_active) {
 #pragma unroll
       for (int rr = 0; rr < 4; ++rr)
@@ -209,9 +214,20 @@ __device__ __forceinline__ void attn_pair(AttnSmem<D>& sm, const Dims& dm, const
     }
     if (w == 0) kpreg = (e0 + lane <= el) ? p3 : -1;
   };
-  auto store_chunk = [&](int buf) {
+  auto loadk_gather = [&](const int32_t* glist, int cnt, int n) {
+    const int e0 = 64 * n, el = cnt - 1;
+    int pk[KCH];
+#pragma unroll
+    for (int j = 0; j < KCH; ++j) pk[j] = glist[min(e0 + kr0 + KRP * j, el)];
+#pragma unroll
+    for (int j = 0; j < KCH; ++j)
+      kreg[j] = bload16(rk, e0 + kr0 + KRP * j <= el ? (uint32_t)pk[j] * rbk + 16u * kc : OOB, 0);
+  };
+  auto storek = [&](int buf) {
 #pragma unroll
     for (int j = 0; j < KCH; ++j) st16(sm.K[buf] + (kr0 + KRP * j) * KS + 8 * kc, kreg[j]);
+  };
+  auto storev = [&](int buf) {
     if (v_active) {
       const uint32_t w0[4] = {vreg[0].x, vreg[0].y, vreg[0].z, vreg[0].w};
       const uint32_t w1[4] = {vreg[1].x, vreg[1].y, vreg[1].z, vreg[1].w};
@@ -247,7 +263,8 @@ __device__ __forceinline__ void attn_pair(AttnSmem<D>& sm, const Dims& dm, const
   // bit 1: second) selected the chunk.
   int wi = W;
   uint64_t bits = 0, wb0 = 0, wb1 = 0;
-  auto load_next = [&](int ci) -> int {
+  // chunk ci -> (source: -1 tile / 0 first list / 1 second list, index, membership bits)
+  auto next_chunk = [&](int ci, int& src, int& idx) -> int {
     if (ci < n_union) {
       while (bits == 0ull && wi > 0) {
         --wi;
@@ -257,20 +274,35 @@ __device__ __forceinline__ void attn_pair(AttnSmem<D>& sm, const Dims& dm, const
       }
       const int b = bits ? 63 - __clzll((long long)bits) : -1;
       bits &= ~(1ull << (b & 63));
-      load_tile(b < 0 ? (view_rows + 63) / 64 : 64 * wi + b);   // (b < 0 only for a corrupt plan)
+      src = -1;
+      idx = b < 0 ? (view_rows + 63) / 64 : 64 * wi + b;   // (b < 0 only for a corrupt plan)
       return b < 0 ? 0 : (int)(((wb0 >> b) & 1ull) | (((wb1 >> b) & 1ull) << 1));
     }
     const int n = ci - n_union;
     if (grid) {
-      load_gather(gl0, max(g0, g1), n);
+      src = 0;
+      idx = n;
       return (64 * n < g0 ? 1 : 0) | (64 * n < g1 ? 2 : 0);
     }
     if (n < nch0) {
-      load_gather(gl0, g0, n);
+      src = 0;
+      idx = n;
       return 1;
     }
-    load_gather(gl1, g1, n - nch0);
+    src = 1;
+    idx = n - nch0;
     return 2;
+  };
+  const int gcnt0 = grid ? max(g0, g1) : g0;
+  auto loadv = [&](int src, int idx) {
+    if (src < 0) loadv_tile(idx);
+    else if (src == 0) loadv_gather(gl0, gcnt0, idx);
+    else loadv_gather(gl1, g1, idx);
+  };
+  auto loadk = [&](int src, int idx) {
+    if (src < 0) loadk_tile(idx);
+    else if (src == 0) loadk_gather(gl0, gcnt0, idx);
+    else loadk_gather(gl1, g1, idx);
   };
 
   floatx16 oacc[ND];
@@ -284,29 +316,58 @@ __device__ __forceinline__ void attn_pair(AttnSmem<D>& sm, const Dims& dm, const
 
   int memb_cur = 0;
   if (n_chunks > 0) {
-    memb_cur = load_next(0);
-    store_chunk(0);
+    int src, idx;
+    memb_cur = next_chunk(0, src, idx);
+    loadv(src, idx);
+    loadk(src, idx);
+    storek(0);
+    storev(0);
     __syncthreads();
   }
+  // LDS fragment reads are software-pipelined PF ahead of the MFMAs that use
+  // them; scheduling barriers pin that order (the scheduler would otherwise
+  // pair each read with its MFMA and expose every read's latency).
+  constexpr int PF = 4, NK = 2 * NS, NV = 4 * ND;
   for (int ci = 0; ci < n_chunks; ++ci) {
     const int buf = ci & 1;
     const bool has_next = ci + 1 < n_chunks;
     int memb_next = 0;
-    if (has_next) memb_next = load_next(ci + 1);
-    if (wave_has && (memb_cur & wbit)) {
-      // ---- S^T = K . Q^T ----
-      const bf16_t* Kb = sm.K[buf];
-      floatx16 sacc[2];
+    if (has_next) {
+      int nsrc, nidx;
+      memb_next = next_chunk(ci + 1, nsrc, nidx);
+      loadv(nsrc, nidx);
+      loadk(nsrc, nidx);
+    }
+    const bool mine = wave_has && (memb_cur & wbit);
+    floatx16 sacc[2];
+    if (mine) {
+      // ---- S^T = K . Q^T (fragment i: key block i&1, d-step i>>1) ----
+      const bf16_t* Kb = sm.K[buf] + qc * KS + 8 * hh;
+      auto kfrag = [&](int i) { return as_bf16x8(ld16(Kb + 32 * (i & 1) * KS + 16 * (i >> 1))); };
 #pragma unroll
-      for (int kb = 0; kb < 2; ++kb) {
+      for (int kb = 0; kb < 2; ++kb)
 #pragma unroll
         for (int e = 0; e < 16; ++e) sacc[kb][e] = 0.f;
+      bf16x8 af[NK];
 #pragma unroll
-        for (int s = 0; s < NS; ++s) {
-          const bf16x8 a = as_bf16x8(ld16(Kb + (32 * kb + qc) * KS + 16 * s + 8 * hh));
-          sacc[kb] = mfma32(a, qf[s], sacc[kb]);
-        }
+      for (int i = 0; i < PF; ++i) af[i] = kfrag(i);
+#pragma unroll
+      for (int i = 0; i < NK; ++i) {
+        __builtin_amdgcn_sched_barrier(0);
+        if (i + PF < NK) af[i + PF] = kfrag(i + PF);
+        sacc[i & 1] = mfma32(af[i], qf[i >> 1], sacc[i & 1]);
       }
+      __builtin_amdgcn_sched_barrier(0);
+    }
+    if (has_next) storek(buf ^ 1);
+    if (mine) {
+      // first V^T fragments in flight during the softmax (fragment i: d-block i%ND, key step i/ND)
+      const bf16_t* Vb = sm.Vt[buf] + qc * VS + 8 * hh;
+      auto vfrag = [&](int i) { return as_bf16x8(ld16(Vb + 32 * (i % ND) * VS + 16 * (i / ND))); };
+      bf16x8 vf[NV];
+#pragma unroll
+      for (int i = 0; i < PF; ++i) vf[i] = vfrag(i);
+      __builtin_amdgcn_sched_barrier(0);
       // ---- mask (only chunks crossing the causal edge, or A-shape), online softmax ----
       const bool full = !ashape && uniform(sm.kmax[buf]) <= wave_qmin;
       if (!full) {
@@ -330,14 +391,21 @@ __device__ __forceinline__ void attn_pair(AttnSmem<D>& sm, const Dims& dm, const
 #pragma unroll
       for (int kb = 0; kb < 2; ++kb)
 #pragma unroll
-        for (int e = 0; e < 16; e += 4)
-          mx = fmaxf(fmaxf(mx, fmaxf(sacc[kb][e], sacc[kb][e + 1])), fmaxf(sacc[kb][e + 2], sacc[kb][e + 3]));
+        for (int e = 0; e < 16; e += 2) mx = fmaxf(mx, fmaxf(sacc[kb][e], sacc[kb][e + 1]));
       mx = fmaxf(mx, shfl_xor_f(mx, 32));
-      const float m_new = fmaxf(m_run, mx * sl2);
-      const float m_use = (m_new == -INFINITY) ? 0.f : m_new;
-      const float corr = __builtin_amdgcn_exp2f(m_run - m_use);
-      m_run = m_new;
-      float psum = 0.f;
+      // Lazy rescale: the running max moves (and O, l are rescaled) only when
+      // some row's max grows by more than 2^LAZY; otherwise probabilities are
+      // taken against the stale max and stay below 2^LAZY.
+      const float m_cand = fmaxf(m_run, mx * sl2);
+      if (__ballot(m_cand > m_run + LAZY_LOG2)) {
+        const float m_use = (m_cand == -INFINITY) ? 0.f : m_cand;
+        const float corr = __builtin_amdgcn_exp2f(m_run - m_use);
+        m_run = m_cand;
+        l_run *= corr;
+#pragma unroll
+        for (int db = 0; db < ND; ++db) oacc[db] *= corr;
+      }
+      const float m_use = (m_run == -INFINITY) ? 0.f : m_run;
       uint32_t pk[16];
 #pragma unroll
       for (int kb = 0; kb < 2; ++kb) {
@@ -345,29 +413,28 @@ __device__ __forceinline__ void attn_pair(AttnSmem<D>& sm, const Dims& dm, const
         for (int e = 0; e < 16; e += 2) {
           const float p0 = __builtin_amdgcn_exp2f(fmaf(sacc[kb][e], sl2, -m_use));
           const float p1 = __builtin_amdgcn_exp2f(fmaf(sacc[kb][e + 1], sl2, -m_use));
-          psum += p0 + p1;
           pk[8 * kb + (e >> 1)] = pack_bf2_hw(p0, p1);
         }
       }
-      l_run = l_run * corr + psum;
-      if (__ballot(corr != 1.0f)) {   // some row's max moved (wave-uniform test)
+      // row sum of the bf16-rounded probabilities, the values the MFMA consumes
+      float psum = 0.f;
 #pragma unroll
-        for (int db = 0; db < ND; ++db) oacc[db] *= corr;
-      }
+      for (int e = 0; e < 16; ++e)
+        psum = __builtin_amdgcn_fdot2_f32_bf16(__builtin_bit_cast(bf16x2_t, pk[e]), ONES_BF2, psum, false);
+      l_run += psum;
+      __builtin_amdgcn_sched_barrier(0);
       // ---- O^T += V^T . P^T ----
-      const bf16_t* Vb = sm.Vt[buf];
 #pragma unroll
-      for (int st = 0; st < 4; ++st) {   // 16-key steps: accumulator values 8(st&1).. of key block st>>1
-        const bf16x8 pb =
-            as_bf16x8(make_uint4(pk[4 * st], pk[4 * st + 1], pk[4 * st + 2], pk[4 * st + 3]));
-#pragma unroll
-        for (int db = 0; db < ND; ++db) {
-          const bf16x8 a = as_bf16x8(ld16(Vb + (32 * db + qc) * VS + 16 * st + 8 * hh));
-          oacc[db] = mfma32(a, pb, oacc[db]);
-        }
+      for (int i = 0; i < NV; ++i) {
+        __builtin_amdgcn_sched_barrier(0);
+        if (i + PF < NV) vf[i + PF] = vfrag(i + PF);
+        const int st = i / ND;   // 16-key step: accumulator values 8(st&1).. of key block st>>1
+        const bf16x8 pb = as_bf16x8(make_uint4(pk[4 * st], pk[4 * st + 1], pk[4 * st + 2], pk[4 * st + 3]));
+        oacc[i % ND] = mfma32(vf[i], pb, oacc[i % ND]);
       }
+      __builtin_amdgcn_sched_barrier(0);
     }
-    if (has_next) store_chunk(buf ^ 1);
+    if (has_next) storev(buf ^ 1);
     memb_cur = memb_next;
     __syncthreads();
   }
