@@ -1,6 +1,7 @@
 """Benchmark of one sparse-prefill layer on one MI355X.
 
     python bench.py [--gpus 1] [--steps K] [--warmup W] [--config 2] [--no-cpu]
+    python bench.py --copy-calibration     # plain copy of known size, for counter scaling
 
 A step is one pass of the whole path (estimate_vs, estimate_blocks, permute,
 sparse_prefill, unpermute) over one layer of synthetic bf16 inputs resident in
@@ -14,6 +15,7 @@ CPU oracle timed on a bounded sample of the same layer.
 from __future__ import annotations
 
 import argparse
+import hashlib
 import json
 import math
 import os
@@ -30,6 +32,10 @@ from dynamic_sparse_attention_head_amd import mmsa, synth  # noqa: E402
 
 PEAK_BF16_TFLOPS = 2500.0     # MI355X dense bf16 MFMA
 PEAK_HBM_GBPS = 8000.0
+CSRC = os.path.join(ROOT, "dynamic_sparse_attention_head_amd", "csrc")
+ATTN_SOURCES = ("k_attention.hip", "mmsa_device.h", "mmsa_internal.h")
+PROFILES = os.path.join(ROOT, "profiles")
+COPY_BYTES = 1 << 30
 
 
 def log(*a):
@@ -56,7 +62,55 @@ def est_bytes(spec):
     return 2 * len(kvs) * spec.L * spec.d * 2
 
 
-def cpu_baseline(spec, lay, seed=0, rows_per_head=48):
+def attn_source_digest():
+    """sha256 over the attention kernel's sources: counter figures taken on
+    another version of the kernel are not reported."""
+    h = hashlib.sha256()
+    for f in ATTN_SOURCES:
+        with open(os.path.join(CSRC, f), "rb") as fh:
+            h.update(fh.read())
+    return h.hexdigest()
+
+
+def read_traffic(workload):
+    """HBM bytes per attention launch from the committed counter summary of
+    this workload, or None when it is missing or was taken on other sources."""
+    path = os.path.join(PROFILES, f"k_attn_{workload}_traffic.md")
+    if not os.path.exists(path):
+        return None
+    kv = {}
+    with open(path) as f:
+        for line in f:
+            if line.startswith("- ") and ":" in line:
+                k, v = line[2:].split(":", 1)
+                kv[k.strip()] = v.strip().strip("`")
+    if kv.get("attention sources sha256") != attn_source_digest():
+        return None
+    try:
+        return int(float(kv["traffic bytes per launch"]))
+    except (KeyError, ValueError):
+        return None
+
+
+def copy_calibration(steps):
+    """A plain streaming kernel of known size: y = x * 1 over COPY_BYTES of bf16
+    (reads and writes COPY_BYTES each per launch)."""
+    n = COPY_BYTES // 2
+    x = torch.ones(n, dtype=torch.bfloat16, device="cuda")
+    y = torch.empty_like(x)
+    torch.cuda.synchronize()
+    ev = [torch.cuda.Event(enable_timing=True) for _ in range(2)]
+    ev[0].record()
+    for _ in range(steps):
+        torch.mul(x, 1.0, out=y)
+    ev[1].record()
+    torch.cuda.synchronize()
+    ms = ev[0].elapsed_time(ev[1]) / steps
+    print(json.dumps({"copy_bytes_read": COPY_BYTES, "copy_bytes_written": COPY_BYTES, "launches": steps,
+                      "ms_per_launch": round(ms, 4), "gbps": round(2 * COPY_BYTES / ms / 1e6, 1)}), flush=True)
+
+
+def cpu_baseline(spec, lay, seed=0, rows_per_head=768):
     """The CPU oracle, as written, on a bounded sample: for one head of each
     pattern present, full index estimation plus attention on sampled rows.
     Returns effective TFLOP/s of the sample (4 d |selected pairs| / time)."""
@@ -104,12 +158,16 @@ def main():
     ap.add_argument("--warmup", type=int, default=2)
     ap.add_argument("--config", type=int, default=2)
     ap.add_argument("--no-cpu", action="store_true")
-    ap.add_argument("--cpu-rows", type=int, default=48)
+    ap.add_argument("--cpu-rows", type=int, default=768)
+    ap.add_argument("--copy-calibration", action="store_true")
     args = ap.parse_args()
     if args.gpus != 1:
         print(f"bench.py runs on one GPU only (asked for --gpus {args.gpus}); the path shards by KV head "
               f"without collectives but multi-GPU runs are not part of this build.", file=sys.stderr)
         sys.exit(2)
+    if args.copy_calibration:
+        copy_calibration(max(args.steps, 1))
+        return
     dev = torch.device("cuda")
     spec = synth.config(args.config)
     log(f"[bench] generating {spec.name}: L={spec.L} Hq={spec.Hq} Hkv={spec.Hkv} d={spec.d}")
@@ -188,7 +246,8 @@ def main():
                    "heads": "16 vertical-slash (1000/4096), 8 block (top-100), 8 A-shape (128, 4096)"
                    if args.config == 2 else str([h["pattern"] for h in spec.heads])},
         "roofline": {"bound": "mfma", "achieved": round(achieved, 2), "peak": PEAK_BF16_TFLOPS,
-                     "unit": "TFLOP/s", "frac": round(achieved / PEAK_BF16_TFLOPS, 4), "traffic": None,
+                     "unit": "TFLOP/s", "frac": round(achieved / PEAK_BF16_TFLOPS, 4),
+                     "traffic": read_traffic(spec.name),
                      "kernel": "k_attn (mmsa_sparse_prefill)", "launch_ms": round(attn_ms, 3)},
         "effective_pct_mfma_peak": round(100 * eff_tflops / PEAK_BF16_TFLOPS, 2),
         "selected_pairs": pairs,
