@@ -5,25 +5,33 @@
 //
 // One workgroup = one pair of adjacent 64-row query tiles of one head (128
 // rows), 4 waves x 32 rows.  Key chunks of 64 (a whole view tile, or 64
-// gathered columns) are staged once in LDS for both tiles: K row-major, V
-// transposed (d-major, keys in MFMA k-slot order).  The staged chunks are the
-// union of the two tiles' plans; a wave computes only the chunks its own tile
-// selected.  Both products run as bf16 32x32x16 MFMA with fp32 accumulation:
+// gathered columns) are staged once in LDS for both tiles; the staged chunks
+// are the union of the two tiles' plans and a wave computes only the chunks
+// its own tile selected.  Both products run as bf16 32x32x16 MFMA with fp32
+// accumulation:
 //   S^T (keys x queries) = K . Q^T     -> each lane holds one query's 32 logits
 //   O^T (d x queries)   += V^T . P^T   -> each lane holds one query's outputs
-// With these layouts a lane owns one query row throughout, so the online
-// softmax needs one cross-lane exchange per chunk and its rescale is a per-lane
-// scalar.  32 query rows per wave make every LDS fragment feed two 16-row
-// blocks' worth of MFMA work, and 128 rows per workgroup halve the K/V bytes
-// staged per FLOP.  Staging is double-buffered: the next chunk's global loads
-// are in flight while the current chunk is computed.  Masking is element-wise
-// on original positions (causal, A-shape window) and is skipped for chunks
-// whose keys all precede the wave's first row.
+// so a lane owns one query row throughout: the online softmax needs one
+// cross-lane exchange per chunk and its rescale is a per-lane scalar.
+//
+// Staging goes straight from HBM to LDS (buffer loads with the LDS bit, 16
+// bytes per lane) -- no registers, no LDS stores.  K and V stay row-major with
+// their 16-byte chunks XOR-swizzled per row; the V^T operand is read with the
+// LDS transpose read (ds_read_b64_tr_b16), which hands each lane 4 keys of one
+// d column.  The pipeline runs K one chunk ahead of V: while chunk n's softmax
+// and P.V run, S^T of chunk n+1 is computed (its MFMAs interleaved with the
+// softmax arithmetic), and the copies of K for chunk n+2 and V for chunk n+1
+// are in flight.  Masking is element-wise on original positions (causal,
+// A-shape window) and runs only for chunks whose keys may follow the wave's
+// first row.  The running max moves only when a row's max grows by more than
+// 2^LAZY, so rescales of O are rare.
 #include "mmsa_device.h"
 
 namespace mmsa {
 
 typedef float floatx16 __attribute__((ext_vector_type(16)));
+typedef __bf16 bf16x4_t __attribute__((ext_vector_type(4)));
+#define MMSA_LDS __attribute__((address_space(3)))
 
 // D(32x32 fp32) += A(32x16 bf16) * B(16x32 bf16).  Lane l: A row l%32, k-slots
 // 8*(l/32)..+8; B column l%32, same k-slots; D column l%32, rows 8i+4(l/32)+j
@@ -33,32 +41,58 @@ __device__ __forceinline__ floatx16 mfma32(bf16x8 a, bf16x8 b, floatx16 c) {
 }
 
 template <int D>
-struct AttnSmem {  // 2 stages of K (row-major), V^T (d-major), key positions and their max
-  static constexpr int KS = D + 8;    // K row stride (elements)
-  static constexpr int VS = 64 + 8;   // V^T row stride (elements)
-  bf16_t K[2][64 * KS];
-  bf16_t Vt[2][D * VS];
+struct AttnSmem {   // 2 stages of K and V (row-major, swizzled), key positions and their max
+  bf16_t K[2][64 * D];
+  bf16_t V[2][64 * D];
   int kp[2][64];
   int kmax[2];
 };
 
-// V^T slot of the first key of key quad kq (keys 4kq..4kq+3).  Within each
-// 16-key MFMA step, k-slots 8h..8h+7 of lane half h hold keys {4h..4h+3,
-// 8+4h..8+4h+3}, the keys that half holds in the S^T accumulator.
-__device__ __forceinline__ int vt_slot(int kq) { return 16 * (kq >> 2) + 8 * (kq & 1) + 4 * ((kq >> 1) & 1); }
+// Swizzle of the 16-byte chunks of row r: physical chunk = logical ^ swz(r).
+// It permutes the low three chunk bits with row bits (2, 0, 1), so that
+//  * 8 consecutive rows read at one logical chunk (a K fragment) hit 8
+//    different 16-byte bank groups, and
+//  * 4 consecutive rows x 2 adjacent chunks (one transpose read of V by 16
+//    lanes) hit 8 different bank groups.
+__device__ __forceinline__ int swz(int r) { return ((r >> 2) & 1) | ((r & 1) << 1) | (((r >> 1) & 1) << 2); }
 
 // Raw buffer resource over [base, base + bytes): loads past the end return 0.
 __device__ __forceinline__ __amdgpu_buffer_rsrc_t make_rsrc(const void* base, uint32_t bytes) {
   return __builtin_amdgcn_make_buffer_rsrc(const_cast<void*>(base), (short)0, (int)bytes, 0x00020000);
 }
-__device__ __forceinline__ uint4 bload16(__amdgpu_buffer_rsrc_t r, uint32_t voff, uint32_t soff) {
-  return __builtin_bit_cast(uint4, __builtin_amdgcn_raw_buffer_load_b128(r, (int)voff, (int)soff, 0));
+// 16 bytes per lane from the buffer straight into LDS at dst + 16 * lane.
+__device__ __forceinline__ void dma16(__amdgpu_buffer_rsrc_t r, void* dst, uint32_t voff, uint32_t soff) {
+  __builtin_amdgcn_raw_ptr_buffer_load_lds(r, (MMSA_LDS void*)dst, 16, (int)voff, (int)soff, 0, 0);
 }
 __device__ __forceinline__ int uniform(int x) { return __builtin_amdgcn_readfirstlane(x); }
+// Transpose read: within each 16-lane group, lane i receives element i%4 of the
+// 8 bytes addressed by lanes 4j + i/4 (j = 0..3) as its elements j.
+__device__ __forceinline__ uint2 ld_tr(const void* p) {
+  return __builtin_bit_cast(uint2, __builtin_amdgcn_ds_read_tr16_b64_v4bf16((MMSA_LDS bf16x4_t*)p));
+}
+
+// (x[l], x[l ^ 32]) as a pair, in registers: v_permlane32_swap exchanges the
+// upper half-wave of one copy with the lower half-wave of the other, so the
+// two results hold, lane by lane, x and its partner in some order.
+__device__ __forceinline__ float max_xor32(float x) {
+  const auto r = __builtin_amdgcn_permlane32_swap(__float_as_uint(x), __float_as_uint(x), false, false);
+  return fmaxf(__uint_as_float(r[0]), __uint_as_float(r[1]));
+}
+__device__ __forceinline__ float sum_xor32(float x) {
+  const auto r = __builtin_amdgcn_permlane32_swap(__float_as_uint(x), __float_as_uint(x), false, false);
+  return __uint_as_float(r[0]) + __uint_as_float(r[1]);
+}
 
 constexpr uint32_t OOB = 0x80000000u;   // a buffer offset past every tensor slice
 constexpr float LAZY_LOG2 = 8.0f;       // stale-max slack of the online softmax (log2 units)
 __device__ constexpr bf16x2_t ONES_BF2 = {(__bf16)1.0f, (__bf16)1.0f};
+
+// Descriptor of one staged chunk: source (-1 view tile, 0 first list, 1 second
+// list), index (tile, or 64-column chunk of the list) and which tiles of the
+// pair selected it (bit 0: first, bit 1: second).
+struct Chunk {
+  int src, idx, memb;
+};
 
 // One (head, query-tile pair) work item.  Ends with a workgroup barrier, so the
 // next item may reuse the LDS at once.
@@ -67,7 +101,10 @@ __device__ __forceinline__ void attn_pair(AttnSmem<D>& sm, const Dims& dm, const
                                           const bf16_t* __restrict__ q, const bf16_t* __restrict__ k,
                                           const bf16_t* __restrict__ v, bf16_t* __restrict__ o,
                                           float* __restrict__ lse, uint32_t item) {
-  constexpr int KS = AttnSmem<D>::KS, VS = AttnSmem<D>::VS, NS = D / 16, ND = D / 32;
+  constexpr int NS = D / 16, ND = D / 32;
+  constexpr int CPR = D / 8;          // 16-byte chunks per row
+  constexpr int RPI = 64 / CPR;       // rows per staging instruction (64 lanes x 16 bytes)
+  constexpr int PPW = CPR / 4;        // staging instructions per wave per tile
   const int bh = (int)(item >> 16), pr = (int)(item & 0xffff);
   const MMSA_CONST HeadDev& H = cptr<HeadDev>(ws, tb.off_heads)[bh];
   const int tid = threadIdx.x, w = tid >> 6, lane = tid & 63, qc = lane & 31, hh = lane >> 5;
@@ -98,8 +135,7 @@ __device__ __forceinline__ void attn_pair(AttnSmem<D>& sm, const Dims& dm, const
       if (qpos >= 0) u[s] = ld16(qrow + 16 * s + 8 * hh);
     }
     // Consume the fragments here, once: afterwards they are plain register values,
-    // not loads in flight, so the chunk loop never has to wait for them (a wait
-    // there would also wait for the next chunk's prefetch and serialise it).
+    // not loads in flight, so the chunk loop never has to wait for them.
 #pragma unroll
     for (int s = 0; s < NS; ++s) {
       asm volatile("" : "+v"(u[s].x), "+v"(u[s].y), "+v"(u[s].z), "+v"(u[s].w));
@@ -137,6 +173,7 @@ __device__ __forceinline__ void attn_pair(AttnSmem<D>& sm, const Dims& dm, const
   const int nch0 = (g0 + 63) / 64, nch1 = (g1 + 63) / 64;
   const int n_gath = grid ? max(nch0, nch1) : nch0 + nch1;
   const int n_chunks = n_union + n_gath;
+  const int gcnt0 = grid ? max(g0, g1) : g0;
   const bool grouped_view = H.view_kind == VIEW_GROUPED;
   const int32_t* pgrp = wsp<const int32_t>(ws, dm.ws_pgrp);
   const bool ashape = H.pattern == MMSA_ASHAPE;
@@ -156,115 +193,89 @@ __device__ __forceinline__ void attn_pair(AttnSmem<D>& sm, const Dims& dm, const
   const __amdgpu_buffer_rsrc_t rk = make_rsrc(k + H.k_off, (uint32_t)(dm.L - 1) * rbk + 2u * D);
   const __amdgpu_buffer_rsrc_t rv = make_rsrc(v + H.v_off, (uint32_t)(dm.L - 1) * rbv + 2u * D);
 
-  // ---- staging ----
-  // K: a thread moves 16-byte chunk kc of rows kr0 + j*KRP (coalesced row reads,
-  //    bank-conflict-free row-major LDS stores).
-  // V: a thread moves d-chunk vdc of key quad vkq (4 rows), transposes the 4x8
-  //    block in registers and stores 8-byte runs of 4 keys; lanes of one store
-  //    instruction vary over 16 key quads x 2 d-rows, which hit distinct banks.
-  // Rows past the end of a view read zeros (buffer bounds) and carry no position.
-  constexpr int VDC = D / 8;            // 16-byte d-chunks per row
-  constexpr int KRP = 256 / VDC;        // rows per K pass
-  constexpr int KCH = 64 / KRP;         // K passes (rows per thread)
-  uint4 kreg[KCH];
-  uint4 vreg[4];
-  int kpreg = -1;
-  const int kc = tid % VDC, kr0 = tid / VDC;
-  const int vkq = lane & 15, vdc = 4 * w + (lane >> 4);
-  const bool v_active = (D == 128) || w < 2;   // wave-uniform
-  uint32_t kvoff[KCH], vvoff[4];
+  // ---- staging: instruction p of wave w fills chunk rows (w*PPW + p)*RPI .. +RPI-1;
+  // the lane writes row srow0 + p*RPI, physical chunk lane % CPR, which holds
+  // logical chunk (lane % CPR) ^ swz(row).  swz only sees row bits 0-2, and
+  // p*RPI changes them only through the parity of p, so two chunk offsets
+  // (p even / odd) serve every p; the rest of the row offset is uniform.
+  const int srow0 = w * PPW * RPI + lane / CPR;
+  uint32_t lchk16[2], kdo[2], vdo[2];
 #pragma unroll
-  for (int j = 0; j < KCH; ++j) kvoff[j] = (uint32_t)(kr0 + KRP * j) * rb_view + 16u * kc;
+  for (int e = 0; e < 2; ++e) {
+    lchk16[e] = 16u * (uint32_t)((lane % CPR) ^ swz(srow0 + e * RPI));
+    kdo[e] = (uint32_t)srow0 * rb_view + lchk16[e];
+    vdo[e] = (uint32_t)srow0 * rbv_view + lchk16[e];
+  }
+  char* const kbuf0 = reinterpret_cast<char*>(sm.K[0]);
+  char* const vbuf0 = reinterpret_cast<char*>(sm.V[0]);
+  constexpr uint32_t BUFB = 64u * D * 2u;   // bytes of one K or V stage
+  auto dma_k = [&](const Chunk& c, int par) {
+    char* dst = kbuf0 + par * BUFB + (w * PPW) * 1024;
+    if (c.src < 0) {
+      const uint32_t s0 = (uint32_t)(64 * c.idx) * rb_view;
 #pragma unroll
-  for (int rr = 0; rr < 4; ++rr) vvoff[rr] = (uint32_t)(4 * vkq + rr) * rbv_view + 16u * vdc;
-
-  // A chunk is staged in two halves so that only one half's registers are live
-  // at a time: V (and the key positions) are loaded when the chunk is chosen and
-  // stored at the end of the iteration; K is loaded after the current chunk's
-  // S^T products and stored right after them.
-  auto loadv_tile = [&](int c) {         // key tile c of the head's key view
-    const uint32_t sv = (uint32_t)(64 * c) * rbv_view;
-    if (v_active) {
+      for (int p = 0; p < PPW; ++p) dma16(rk_view, dst + p * 1024, kdo[p & 1], s0 + (uint32_t)(p * RPI) * rb_view);
+    } else {
+      const int32_t* gl = c.src == 0 ? gl0 : gl1;
+      const int e0 = 64 * c.idx, el = (c.src == 0 ? gcnt0 : g1) - 1;
+      int gi[PPW];
 #pragma unroll
-      for (int rr = 0; rr < 4; ++rr) vreg[rr] = bload16(rv_view, vvoff[rr], sv);
-    }
-    if (w == 0) {   // raw position; -1 (no token) becomes KPOS_NONE at store time
-      const int vr = 64 * c + lane;
-      if (grouped_view) kpreg = pgrp[min(vr, view_rows - 1)];
-      else kpreg = vr < dm.L ? vr : -1;
+      for (int p = 0; p < PPW; ++p) gi[p] = gl[min(e0 + srow0 + p * RPI, el)];
+#pragma unroll
+      for (int p = 0; p < PPW; ++p)
+        dma16(rk, dst + p * 1024, e0 + srow0 + p * RPI <= el ? (uint32_t)gi[p] * rbk + lchk16[p & 1] : OOB, 0);
     }
   };
-  auto loadk_tile = [&](int c) {
-    const uint32_t sk = (uint32_t)(64 * c) * rb_view;
+  auto dma_v = [&](const Chunk& c, int par) {
+    char* dst = vbuf0 + par * BUFB + (w * PPW) * 1024;
+    if (c.src < 0) {
+      const uint32_t s0 = (uint32_t)(64 * c.idx) * rbv_view;
 #pragma unroll
-    for (int j = 0; j < KCH; ++j) kreg[j] = bload16(rk_view, kvoff[j], sk);
-  };
-  // gathered columns 64n .. 64n+63 of a list: indices first (clamped,
-  // unconditional, so they issue back to back), then rows
-  auto loadv_gather = [&](const int32_t* glist, int cnt, int n) {
-    const int e0 = 64 * n, el = cnt - 1;
-    int pv[4];
+      for (int p = 0; p < PPW; ++p) dma16(rv_view, dst + p * 1024, vdo[p & 1], s0 + (uint32_t)(p * RPI) * rbv_view);
+    } else {
+      const int32_t* gl = c.src == 0 ? gl0 : gl1;
+      const int e0 = 64 * c.idx, el = (c.src == 0 ? gcnt0 : g1) - 1;
+      int gi[PPW];
 #pragma unroll
-    for (int rr = 0; rr < 4; ++rr) pv[rr] = glist[min(e0 + 4 * vkq + rr, el)];
-    const int p3 = glist[min(e0 + lane, el)];
-    if (v_active) {
+      for (int p = 0; p < PPW; ++p) gi[p] = gl[min(e0 + srow0 + p * RPI, el)];
 #pragma unroll
-      for (int rr = 0; rr < 4; ++rr)
-        vreg[rr] = bload16(rv, e0 + 4 * vkq + rr <= el ? (uint32_t)pv[rr] * rbv + 16u * vdc : OOB, 0);
+      for (int p = 0; p < PPW; ++p)
+        dma16(rv, dst + p * 1024, e0 + srow0 + p * RPI <= el ? (uint32_t)gi[p] * rbv + lchk16[p & 1] : OOB, 0);
     }
-    if (w == 0) kpreg = (e0 + lane <= el) ? p3 : -1;
   };
-  auto loadk_gather = [&](const int32_t* glist, int cnt, int n) {
-    const int e0 = 64 * n, el = cnt - 1;
-    int pk[KCH];
-#pragma unroll
-    for (int j = 0; j < KCH; ++j) pk[j] = glist[min(e0 + kr0 + KRP * j, el)];
-#pragma unroll
-    for (int j = 0; j < KCH; ++j)
-      kreg[j] = bload16(rk, e0 + kr0 + KRP * j <= el ? (uint32_t)pk[j] * rbk + 16u * kc : OOB, 0);
-  };
-  auto storek = [&](int buf) {
-#pragma unroll
-    for (int j = 0; j < KCH; ++j) st16(sm.K[buf] + (kr0 + KRP * j) * KS + 8 * kc, kreg[j]);
-  };
-  auto storev = [&](int buf) {
-    if (v_active) {
-      const uint32_t w0[4] = {vreg[0].x, vreg[0].y, vreg[0].z, vreg[0].w};
-      const uint32_t w1[4] = {vreg[1].x, vreg[1].y, vreg[1].z, vreg[1].w};
-      const uint32_t w2[4] = {vreg[2].x, vreg[2].y, vreg[2].z, vreg[2].w};
-      const uint32_t w3[4] = {vreg[3].x, vreg[3].y, vreg[3].z, vreg[3].w};
-      bf16_t* vd = sm.Vt[buf] + (8 * vdc) * VS + vt_slot(vkq);
-#pragma unroll
-      for (int m = 0; m < 4; ++m) {
-        uint2 lo, hi;
-        lo.x = __builtin_amdgcn_perm(w1[m], w0[m], 0x05040100u);
-        lo.y = __builtin_amdgcn_perm(w3[m], w2[m], 0x05040100u);
-        hi.x = __builtin_amdgcn_perm(w1[m], w0[m], 0x07060302u);
-        hi.y = __builtin_amdgcn_perm(w3[m], w2[m], 0x07060302u);
-        *reinterpret_cast<uint2*>(vd + (2 * m) * VS) = lo;
-        *reinterpret_cast<uint2*>(vd + (2 * m + 1) * VS) = hi;
-      }
+  // key positions of a chunk (wave 0, one per lane): the raw value, and whether
+  // the slot holds a token; they are combined only when stored, so the load
+  // stays in flight until then
+  auto load_kp = [&](const Chunk& c, bool& valid) -> int {
+    if (c.src < 0) {
+      const int vr = 64 * c.idx + lane;
+      valid = true;
+      if (grouped_view) return pgrp[min(vr, view_rows - 1)];
+      return vr < dm.L ? vr : -1;
     }
-    if (w == 0) {
-      const int kpos = kpreg >= 0 ? kpreg : KPOS_NONE;
-      sm.kp[buf][lane] = kpos;
-      int mx = kpos;
+    const int32_t* gl = c.src == 0 ? gl0 : gl1;
+    const int e0 = 64 * c.idx, el = (c.src == 0 ? gcnt0 : g1) - 1;
+    valid = e0 + lane <= el;
+    return gl[min(e0 + lane, el)];
+  };
+  auto store_kp = [&](int kpr, bool valid, int par) {
+    const int kpos = (valid & (kpr >= 0)) ? kpr : KPOS_NONE;
+    sm.kp[par][lane] = kpos;
+    int mx = kpos;
 #pragma unroll
-      for (int m = 1; m < 64; m <<= 1) mx = max(mx, __shfl_xor(mx, m, 64));
-      if (lane == 0) sm.kmax[buf] = mx;
-    }
+    for (int m = 1; m < 64; m <<= 1) mx = max(mx, __shfl_xor(mx, m, 64));
+    if (lane == 0) sm.kmax[par] = mx;
   };
 
   // Chunk sequence (uniform across the workgroup): the union of both tiles'
   // key tiles, highest first -- workgroups on neighbouring query tiles then
   // stream the same key tiles at about the same time and share them in L2, and
-  // the diagonal (the only chunk a causal tile needs masked) comes first -- then
-  // the gathered columns.  The returned bits say which tiles (bit 0: first,
-  // bit 1: second) selected the chunk.
+  // the diagonal comes first -- then the gathered columns.
   int wi = W;
   uint64_t bits = 0, wb0 = 0, wb1 = 0;
-  // chunk ci -> (source: -1 tile / 0 first list / 1 second list, index, membership bits)
-  auto next_chunk = [&](int ci, int& src, int& idx) -> int {
+  auto next_chunk = [&](int ci) -> Chunk {
+    Chunk c{0, 0, 0};
+    if (ci >= n_chunks) return c;
     if (ci < n_union) {
       while (bits == 0ull && wi > 0) {
         --wi;
@@ -274,35 +285,58 @@ __device__ __forceinline__ void attn_pair(AttnSmem<D>& sm, const Dims& dm, const
       }
       const int b = bits ? 63 - __clzll((long long)bits) : -1;
       bits &= ~(1ull << (b & 63));
-      src = -1;
-      idx = b < 0 ? (view_rows + 63) / 64 : 64 * wi + b;   // (b < 0 only for a corrupt plan)
-      return b < 0 ? 0 : (int)(((wb0 >> b) & 1ull) | (((wb1 >> b) & 1ull) << 1));
+      c.src = -1;
+      c.idx = b < 0 ? (view_rows + 63) / 64 : 64 * wi + b;   // (b < 0 only for a corrupt plan)
+      c.memb = b < 0 ? 0 : (int)(((wb0 >> b) & 1ull) | (((wb1 >> b) & 1ull) << 1));
+      return c;
     }
     const int n = ci - n_union;
     if (grid) {
-      src = 0;
-      idx = n;
-      return (64 * n < g0 ? 1 : 0) | (64 * n < g1 ? 2 : 0);
+      c.src = 0;
+      c.idx = n;
+      c.memb = (64 * n < g0 ? 1 : 0) | (64 * n < g1 ? 2 : 0);
+    } else if (n < nch0) {
+      c.src = 0;
+      c.idx = n;
+      c.memb = 1;
+    } else {
+      c.src = 1;
+      c.idx = n - nch0;
+      c.memb = 2;
     }
-    if (n < nch0) {
-      src = 0;
-      idx = n;
-      return 1;
-    }
-    src = 1;
-    idx = n - nch0;
-    return 2;
+    return c;
   };
-  const int gcnt0 = grid ? max(g0, g1) : g0;
-  auto loadv = [&](int src, int idx) {
-    if (src < 0) loadv_tile(idx);
-    else if (src == 0) loadv_gather(gl0, gcnt0, idx);
-    else loadv_gather(gl1, g1, idx);
+
+  // ---- per-lane LDS addresses of the MFMA operands ----
+  // K fragment (key block kb, d-step s): row 32kb + qc, logical chunk 2s + hh.
+  // The swizzle touches chunk bits 0-2 only, so 4 bases (s & 3) serve all s.
+  const int fq = swz(qc);
+  uint32_t kaddr[4];
+#pragma unroll
+  for (int j = 0; j < 4; ++j) kaddr[j] = (uint32_t)qc * (2u * D) + 16u * (uint32_t)(((2 * j) | hh) ^ fq);
+  // V^T fragment (d-block db, key step st): two transpose reads of 16-lane
+  // groups; group g = lane/16 covers d 32db + 16(g&1) + 0..15 and keys
+  // 16st + 4(g>>1) + 0..3 (+8 for the second read).  Source lane i of a group
+  // addresses row (4(g>>1) + i/4), d 32db + 16(g&1) + 4(i%4).
+  const int vg = lane >> 4, vi = lane & 15;
+  const int vrow = 4 * (vg >> 1) + (vi >> 2);
+  const int vcl = 2 * (vg & 1) + ((vi & 3) >> 1);     // chunk within the 4-chunk d block
+  const int fv = swz(vrow);
+  uint32_t vaddr[2];
+#pragma unroll
+  for (int e = 0; e < 2; ++e)
+    vaddr[e] = (uint32_t)vrow * (2u * D) + 16u * (uint32_t)((vcl ^ (fv & 3)) + 4 * (e ^ (fv >> 2))) + 8u * (vi & 1);
+
+  auto kfrag = [&](int par, int i) -> bf16x8 {   // i: key block i&1, d-step i>>1
+    const int s = i >> 1, kb = i & 1;
+    const char* p = kbuf0 + par * BUFB + kaddr[s & 3] + 128 * (s >> 2) + kb * 32 * (2 * D);
+    return as_bf16x8(ld16(p));
   };
-  auto loadk = [&](int src, int idx) {
-    if (src < 0) loadk_tile(idx);
-    else if (src == 0) loadk_gather(gl0, gcnt0, idx);
-    else loadk_gather(gl1, g1, idx);
+  auto vfrag = [&](int par, int i) -> bf16x8 {   // i: d-block i%ND, key step i/ND
+    const int db = i % ND, st = i / ND;
+    const char* p = vbuf0 + par * BUFB + vaddr[db & 1] + 128 * (db >> 1) + st * 16 * (2 * D);
+    const uint2 lo = ld_tr(p), hi = ld_tr(p + 8 * (2 * D));
+    return as_bf16x8(make_uint4(lo.x, lo.y, hi.x, hi.y));
   };
 
   floatx16 oacc[ND];
@@ -313,134 +347,182 @@ __device__ __forceinline__ void attn_pair(AttnSmem<D>& sm, const Dims& dm, const
   float m_run = -INFINITY, l_run = 0.f;
   const float sl2 = dm.scale_log2;
   const int wbit = w < 2 ? 1 : 2;
-
-  int memb_cur = 0;
-  if (n_chunks > 0) {
-    int src, idx;
-    memb_cur = next_chunk(0, src, idx);
-    loadv(src, idx);
-    loadk(src, idx);
-    storek(0);
-    storev(0);
-    __syncthreads();
-  }
-  // LDS fragment reads are software-pipelined PF ahead of the MFMAs that use
-  // them; scheduling barriers pin that order (the scheduler would otherwise
-  // pair each read with its MFMA and expose every read's latency).
   constexpr int PF = 4, NK = 2 * NS, NV = 4 * ND;
-  for (int ci = 0; ci < n_chunks; ++ci) {
-    const int buf = ci & 1;
-    const bool has_next = ci + 1 < n_chunks;
-    int memb_next = 0;
-    if (has_next) {
-      int nsrc, nidx;
-      memb_next = next_chunk(ci + 1, nsrc, nidx);
-      loadv(nsrc, nidx);
-      loadk(nsrc, nidx);
-    }
-    const bool mine = wave_has && (memb_cur & wbit);
-    floatx16 sacc[2];
-    if (mine) {
-      // ---- S^T = K . Q^T (fragment i: key block i&1, d-step i>>1) ----
-      const bf16_t* Kb = sm.K[buf] + qc * KS + 8 * hh;
-      auto kfrag = [&](int i) { return as_bf16x8(ld16(Kb + 32 * (i & 1) * KS + 16 * (i >> 1))); };
+
+  // S^T of one chunk into sa (fragment reads run PF ahead of their MFMAs)
+  auto s_chunk = [&](floatx16 (&sa)[2], int par) {
 #pragma unroll
-      for (int kb = 0; kb < 2; ++kb)
+    for (int kb = 0; kb < 2; ++kb)
 #pragma unroll
-        for (int e = 0; e < 16; ++e) sacc[kb][e] = 0.f;
-      bf16x8 af[NK];
+      for (int e = 0; e < 16; ++e) sa[kb][e] = 0.f;
+    bf16x8 af[NK];
 #pragma unroll
-      for (int i = 0; i < PF; ++i) af[i] = kfrag(i);
+    for (int i = 0; i < PF; ++i) af[i] = kfrag(par, i);
 #pragma unroll
-      for (int i = 0; i < NK; ++i) {
-        __builtin_amdgcn_sched_barrier(0);
-        if (i + PF < NK) af[i + PF] = kfrag(i + PF);
-        sacc[i & 1] = mfma32(af[i], qf[i >> 1], sacc[i & 1]);
-      }
+    for (int i = 0; i < NK; ++i) {
       __builtin_amdgcn_sched_barrier(0);
+      if (i + PF < NK) af[i + PF] = kfrag(par, i + PF);
+      sa[i & 1] = mfma32(af[i], qf[i >> 1], sa[i & 1]);
     }
-    if (has_next) storek(buf ^ 1);
-    if (mine) {
-      // first V^T fragments in flight during the softmax (fragment i: d-block i%ND, key step i/ND)
-      const bf16_t* Vb = sm.Vt[buf] + qc * VS + 8 * hh;
-      auto vfrag = [&](int i) { return as_bf16x8(ld16(Vb + 32 * (i % ND) * VS + 16 * (i / ND))); };
-      bf16x8 vf[NV];
-#pragma unroll
-      for (int i = 0; i < PF; ++i) vf[i] = vfrag(i);
-      __builtin_amdgcn_sched_barrier(0);
-      // ---- mask (only chunks crossing the causal edge, or A-shape), online softmax ----
-      const bool full = !ashape && uniform(sm.kmax[buf]) <= wave_qmin;
-      if (!full) {
-        // branch-free selects (bitwise boolean ops, no short-circuit evaluation)
-#pragma unroll
-        for (int kb = 0; kb < 2; ++kb) {
-#pragma unroll
-          for (int i = 0; i < 4; ++i) {
-            const int4 kk = *reinterpret_cast<const int4*>(&sm.kp[buf][32 * kb + 8 * i + 4 * hh]);
-            const int kpv[4] = {kk.x, kk.y, kk.z, kk.w};
-#pragma unroll
-            for (int j = 0; j < 4; ++j) {
-              bool ok = kpv[j] <= qpos;
-              if (ashape) ok = ok & ((kpv[j] < sink) | (qpos - kpv[j] < window));
-              sacc[kb][4 * i + j] = ok ? sacc[kb][4 * i + j] : -INFINITY;
-            }
-          }
-        }
-      }
-      float mx = -INFINITY;
-#pragma unroll
-      for (int kb = 0; kb < 2; ++kb)
-#pragma unroll
-        for (int e = 0; e < 16; e += 2) mx = fmaxf(mx, fmaxf(sacc[kb][e], sacc[kb][e + 1]));
-      mx = fmaxf(mx, shfl_xor_f(mx, 32));
-      // Lazy rescale: the running max moves (and O, l are rescaled) only when
-      // some row's max grows by more than 2^LAZY; otherwise probabilities are
-      // taken against the stale max and stay below 2^LAZY.
-      const float m_cand = fmaxf(m_run, mx * sl2);
-      if (__ballot(m_cand > m_run + LAZY_LOG2)) {
-        const float m_use = (m_cand == -INFINITY) ? 0.f : m_cand;
-        const float corr = __builtin_amdgcn_exp2f(m_run - m_use);
-        m_run = m_cand;
-        l_run *= corr;
-#pragma unroll
-        for (int db = 0; db < ND; ++db) oacc[db] *= corr;
-      }
-      const float m_use = (m_run == -INFINITY) ? 0.f : m_run;
-      uint32_t pk[16];
+    __builtin_amdgcn_sched_barrier(0);
+  };
+  // mask and running-max update of one chunk's logits (the part of the softmax
+  // that may branch); returns the max to subtract
+  auto soft_a = [&](floatx16 (&sa)[2], int par) -> float {
+    const bool full = !ashape && uniform(sm.kmax[par]) <= wave_qmin;
+    if (!full) {
+      // one lane-dependent base, constant offsets per (kb, i)
+      const char* kpb = reinterpret_cast<const char*>(sm.kp[0]) + par * 256 + 16 * hh;
 #pragma unroll
       for (int kb = 0; kb < 2; ++kb) {
 #pragma unroll
-        for (int e = 0; e < 16; e += 2) {
-          const float p0 = __builtin_amdgcn_exp2f(fmaf(sacc[kb][e], sl2, -m_use));
-          const float p1 = __builtin_amdgcn_exp2f(fmaf(sacc[kb][e + 1], sl2, -m_use));
-          pk[8 * kb + (e >> 1)] = pack_bf2_hw(p0, p1);
+        for (int i = 0; i < 4; ++i) {
+          const int4 kk = *reinterpret_cast<const int4*>(kpb + 4 * (32 * kb + 8 * i));
+          const int kpv[4] = {kk.x, kk.y, kk.z, kk.w};
+#pragma unroll
+          for (int j = 0; j < 4; ++j) {
+            bool ok = kpv[j] <= qpos;
+            if (ashape) ok = ok & ((kpv[j] < sink) | (qpos - kpv[j] < window));
+            sa[kb][4 * i + j] = ok ? sa[kb][4 * i + j] : -INFINITY;
+          }
         }
       }
-      // row sum of the bf16-rounded probabilities, the values the MFMA consumes
-      float psum = 0.f;
-#pragma unroll
-      for (int e = 0; e < 16; ++e)
-        psum = __builtin_amdgcn_fdot2_f32_bf16(__builtin_bit_cast(bf16x2_t, pk[e]), ONES_BF2, psum, false);
-      l_run += psum;
-      __builtin_amdgcn_sched_barrier(0);
-      // ---- O^T += V^T . P^T ----
-#pragma unroll
-      for (int i = 0; i < NV; ++i) {
-        __builtin_amdgcn_sched_barrier(0);
-        if (i + PF < NV) vf[i + PF] = vfrag(i + PF);
-        const int st = i / ND;   // 16-key step: accumulator values 8(st&1).. of key block st>>1
-        const bf16x8 pb = as_bf16x8(make_uint4(pk[4 * st], pk[4 * st + 1], pk[4 * st + 2], pk[4 * st + 3]));
-        oacc[i % ND] = mfma32(vf[i], pb, oacc[i % ND]);
-      }
-      __builtin_amdgcn_sched_barrier(0);
     }
-    if (has_next) storev(buf ^ 1);
-    memb_cur = memb_next;
+    float mx = -INFINITY;
+#pragma unroll
+    for (int kb = 0; kb < 2; ++kb)
+#pragma unroll
+      for (int e = 0; e < 16; e += 2) mx = fmaxf(mx, fmaxf(sa[kb][e], sa[kb][e + 1]));
+    mx = max_xor32(mx);
+    const float m_cand = fmaxf(m_run, mx * sl2);
+    if (__ballot(m_cand > m_run + LAZY_LOG2)) {
+      const float m_use = (m_cand == -INFINITY) ? 0.f : m_cand;
+      const float corr = __builtin_amdgcn_exp2f(m_run - m_use);
+      m_run = m_cand;
+      l_run *= corr;
+#pragma unroll
+      for (int db = 0; db < ND; ++db) oacc[db] *= corr;
+    }
+    return (m_run == -INFINITY) ? 0.f : m_run;
+  };
+  // probabilities of the 2 logits e = 2i, 2i+1 (bf16, packed in MFMA k-slot order)
+  auto soft_pair = [&](const floatx16 (&sa)[2], float m_use, int i) -> uint32_t {
+    const int kb = i >> 3, e = 2 * (i & 7);
+    const float p0 = __builtin_amdgcn_exp2f(fmaf(sa[kb][e], sl2, -m_use));
+    const float p1 = __builtin_amdgcn_exp2f(fmaf(sa[kb][e + 1], sl2, -m_use));
+    return pack_bf2_hw(p0, p1);
+  };
+  // row sum of the bf16-rounded probabilities, the values the MFMA consumes
+  auto row_sum = [&](const uint32_t (&pk)[16]) {
+    float psum = 0.f;
+#pragma unroll
+    for (int e = 0; e < 16; ++e)
+      psum = __builtin_amdgcn_fdot2_f32_bf16(__builtin_bit_cast(bf16x2_t, pk[e]), ONES_BF2, psum, false);
+    l_run += psum;
+  };
+  auto soft_b = [&](const floatx16 (&sa)[2], float m_use, uint32_t (&pk)[16]) {
+#pragma unroll
+    for (int i = 0; i < 16; ++i) pk[i] = soft_pair(sa, m_use, i);
+    row_sum(pk);
+  };
+  // S^T of the next chunk into sn, interleaved step by step with the
+  // probabilities of the current chunk (one MFMA per 2 exponentials)
+  auto s_and_soft = [&](floatx16 (&sn)[2], int par, const floatx16 (&sc)[2], float m_use, uint32_t (&pk)[16]) {
+#pragma unroll
+    for (int kb = 0; kb < 2; ++kb)
+#pragma unroll
+      for (int e = 0; e < 16; ++e) sn[kb][e] = 0.f;
+    bf16x8 af[NK];
+#pragma unroll
+    for (int i = 0; i < PF; ++i) af[i] = kfrag(par, i);
+#pragma unroll
+    for (int i = 0; i < NK; ++i) {
+      __builtin_amdgcn_sched_barrier(0);
+      if (i + PF < NK) af[i + PF] = kfrag(par, i + PF);
+      sn[i & 1] = mfma32(af[i], qf[i >> 1], sn[i & 1]);
+      if (NK == 16) {
+        pk[i] = soft_pair(sc, m_use, i);
+      } else {   // 8 MFMAs: 4 exponentials each
+        pk[2 * i] = soft_pair(sc, m_use, 2 * i);
+        pk[2 * i + 1] = soft_pair(sc, m_use, 2 * i + 1);
+      }
+    }
+    __builtin_amdgcn_sched_barrier(0);
+    row_sum(pk);
+  };
+  auto pv_chunk = [&](const uint32_t (&pk)[16], int par) {
+    bf16x8 vf[NV];
+#pragma unroll
+    for (int i = 0; i < PF; ++i) vf[i] = vfrag(par, i);
+#pragma unroll
+    for (int i = 0; i < NV; ++i) {
+      __builtin_amdgcn_sched_barrier(0);
+      if (i + PF < NV) vf[i + PF] = vfrag(par, i + PF);
+      const int st = i / ND;   // 16-key step: accumulator values 8(st&1).. of key block st>>1
+      const bf16x8 pb = as_bf16x8(make_uint4(pk[4 * st], pk[4 * st + 1], pk[4 * st + 2], pk[4 * st + 3]));
+      oacc[i % ND] = mfma32(vf[i], pb, oacc[i % ND]);
+    }
+    __builtin_amdgcn_sched_barrier(0);
+  };
+
+  // ---- prologue: K, V, positions of chunk 0; K, positions of chunk 1 ----
+  Chunk c0 = next_chunk(0), c1 = next_chunk(1), c2 = next_chunk(2);
+  int kpreg = -1;
+  bool kpval = false;
+  floatx16 sA[2], sB[2];
+  if (n_chunks > 0) {
+    dma_k(c0, 0);
+    dma_v(c0, 0);
+    if (n_chunks > 1) dma_k(c1, 1);
+    if (w == 0) {
+      bool va;
+      const int a = load_kp(c0, va);
+      store_kp(a, va, 0);
+      if (n_chunks > 1) {
+        bool vb;
+        const int b = load_kp(c1, vb);
+        store_kp(b, vb, 1);
+      }
+    }
+    asm volatile("s_waitcnt vmcnt(0)" ::: "memory");
     __syncthreads();
+    if (wave_has && (c0.memb & wbit)) s_chunk(sA, 0);
+  }
+
+  // ---- chunk n (parity par): S^T of n+1 while n's softmax and P.V run ----
+  auto step = [&](floatx16 (&scur)[2], floatx16 (&snxt)[2], int n, int par) {
+    const bool has_n1 = n + 1 < n_chunks, has_n2 = n + 2 < n_chunks;
+    // positions of chunk n+1 (loaded during the previous step) into their slot
+    if (n >= 1 && has_n1 && w == 0) store_kp(kpreg, kpval, par ^ 1);
+    if (has_n2) {
+      dma_k(c2, par);   // K of n+2 replaces K of n (read by the previous step)
+      if (w == 0) kpreg = load_kp(c2, kpval);
+    }
+    if (has_n1) dma_v(c1, par ^ 1);   // V of n+1 replaces V of n-1
+    const bool doS = wave_has && has_n1 && (c1.memb & wbit);
+    const bool doP = wave_has && (c0.memb & wbit);
+    if (doP) {
+      const float m_use = soft_a(scur, par);
+      uint32_t pk[16];
+      if (doS) s_and_soft(snxt, par ^ 1, scur, m_use, pk);
+      else soft_b(scur, m_use, pk);
+      pv_chunk(pk, par);
+    } else if (doS) {
+      s_chunk(snxt, par ^ 1);
+    }
+    asm volatile("s_waitcnt vmcnt(0)" ::: "memory");
+    __syncthreads();
+    c0 = c1;
+    c1 = c2;
+    c2 = next_chunk(n + 3);
+  };
+  for (int n = 0; n < n_chunks; n += 2) {
+    step(sA, sB, n, 0);
+    if (n + 1 < n_chunks) step(sB, sA, n + 1, 1);
   }
 
   // ---- epilogue ----
-  const float l_tot = l_run + shfl_xor_f(l_run, 32);
+  const float l_tot = sum_xor32(l_run);
   if (qpos >= 0) {
     const float inv = l_tot > 0.f ? 1.0f / l_tot : 0.f;
     bf16_t* orow = (H.ws_operm >= 0) ? wsp<bf16_t>(ws, H.ws_operm) + (int64_t)slot * D

@@ -870,6 +870,7 @@ mmsa_status mmsa_workspace_view(const mmsa_layer_desc* desc, int32_t buf, int32_
     case MMSA_BUF_EST_STATS:
       if (J) *offset_bytes = J->ws_stats, *count = 2 * EST_ROWS;
       break;
+    case MMSA_BUF_TILE_BITMAP: *offset_bytes = H.ws_bm, *count = (int64_t)H.nT_rows * H.bm_words; break;
     default: set_err("unknown buffer %d", buf); return MMSA_INVALID_ARGUMENT;
   }
   return MMSA_OK;

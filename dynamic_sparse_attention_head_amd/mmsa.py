@@ -20,10 +20,11 @@ OK, INVALID_ARGUMENT, UNSUPPORTED, WORKSPACE_TOO_SMALL, HIP_ERROR = range(5)
 PATTERNS = {"ashape": 0, "vs": 1, "block": 2, "grid": 3}
 LAYOUTS = {"plain": 0, "q_boundary": 1, "boundary_2d": 2, "modality_grouped": 3}
 BUF = dict(v_scores=0, s_scores=1, v_index=2, s_index=3, nsel=4, grid=5, block_index=6, block_scores=7,
-           row_order=8, tile_pairs=9, tile_info=10, est_stats=11)
+           row_order=8, tile_pairs=9, tile_info=10, est_stats=11, tile_bitmap=12)
 BUF_DTYPE = dict(v_scores=torch.float32, s_scores=torch.float32, v_index=torch.int32, s_index=torch.int32,
                  nsel=torch.int32, grid=torch.int32, block_index=torch.int32, block_scores=torch.float32,
-                 row_order=torch.int32, tile_pairs=torch.int64, tile_info=torch.int32, est_stats=torch.float32)
+                 row_order=torch.int32, tile_pairs=torch.int64, tile_info=torch.int32, est_stats=torch.float32,
+                 tile_bitmap=torch.int64)
 
 
 class HeadCfg(ctypes.Structure):

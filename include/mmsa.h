@@ -135,8 +135,11 @@ enum {
   MMSA_BUF_TILE_PAIRS = 9,  /* int64[count]  selected (query, key) pairs per query tile       */
   MMSA_BUF_TILE_INFO = 10,  /* int32[4*count] per query tile: key tiles, gathered columns,
                                cost, rows                                                    */
-  MMSA_BUF_EST_STATS = 11   /* float[2*64]   per estimation row: max of scale*log2(e)*q.k and
+  MMSA_BUF_EST_STATS = 11,  /* float[2*64]   per estimation row: max of scale*log2(e)*q.k and
                                the sum of 2^(x - max) over its causal keys                   */
+  MMSA_BUF_TILE_BITMAP = 12 /* uint64[count] per query tile, words of a bitmap over the key
+                               tiles of the head's key view (bit c of word w: key tile 64w+c);
+                               count = tiles * words per tile                                */
 };
 mmsa_status mmsa_workspace_view(const mmsa_layer_desc* desc, int32_t buf, int32_t bh, int32_t part,
                                 int64_t* offset_bytes, int64_t* count);
