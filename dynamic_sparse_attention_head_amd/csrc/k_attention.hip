@@ -49,12 +49,18 @@ struct AttnSmem {   // 2 stages of K and V (row-major, swizzled), key positions 
 };
 
 // Swizzle of the 16-byte chunks of row r: physical chunk = logical ^ swz(r).
-// It permutes the low three chunk bits with row bits (2, 0, 1), so that
-//  * 8 consecutive rows read at one logical chunk (a K fragment) hit 8
-//    different 16-byte bank groups, and
-//  * 4 consecutive rows x 2 adjacent chunks (one transpose read of V by 16
-//    lanes) hit 8 different bank groups.
-__device__ __forceinline__ int swz(int r) { return ((r >> 2) & 1) | ((r & 1) << 1) | (((r >> 1) & 1) << 2); }
+// It is XOR-linear in the row bits and maps, for the 64 LDS banks,
+//  * 16 consecutive rows read at one logical chunk (the lanes of one K
+//    fragment read) to 16 different 16-byte bank groups, and
+//  * 4 consecutive rows x 4 adjacent chunks (two 16-lane transpose reads of V)
+//    to 16 different bank groups.
+// d = 128 (256-byte rows): chunk bits (0,1,2,3) <- row bits (2,3,0,1).
+// d = 64 (128-byte rows, two per bank window): chunk bits (0,1,2) <- row bits (2,3,1).
+template <int D>
+__device__ __forceinline__ int swz(int r) {
+  if (D == 128) return ((r >> 2) & 1) | (((r >> 3) & 1) << 1) | ((r & 1) << 2) | (((r >> 1) & 1) << 3);
+  return ((r >> 2) & 1) | (((r >> 3) & 1) << 1) | (((r >> 1) & 1) << 2);
+}
 
 // Raw buffer resource over [base, base + bytes): loads past the end return 0.
 __device__ __forceinline__ __amdgpu_buffer_rsrc_t make_rsrc(const void* base, uint32_t bytes) {
@@ -195,17 +201,12 @@ __device__ __forceinline__ void attn_pair(AttnSmem<D>& sm, const Dims& dm, const
 
   // ---- staging: instruction p of wave w fills chunk rows (w*PPW + p)*RPI .. +RPI-1;
   // the lane writes row srow0 + p*RPI, physical chunk lane % CPR, which holds
-  // logical chunk (lane % CPR) ^ swz(row).  swz only sees row bits 0-2, and
-  // p*RPI changes them only through the parity of p, so two chunk offsets
-  // (p even / odd) serve every p; the rest of the row offset is uniform.
+  // logical chunk (lane % CPR) ^ swz(row) = lchk0 ^ swz(p*RPI) (swz is linear
+  // and p*RPI shares no bits with srow0's low bits).
   const int srow0 = w * PPW * RPI + lane / CPR;
-  uint32_t lchk16[2], kdo[2], vdo[2];
-#pragma unroll
-  for (int e = 0; e < 2; ++e) {
-    lchk16[e] = 16u * (uint32_t)((lane % CPR) ^ swz(srow0 + e * RPI));
-    kdo[e] = (uint32_t)srow0 * rb_view + lchk16[e];
-    vdo[e] = (uint32_t)srow0 * rbv_view + lchk16[e];
-  }
+  const uint32_t lchk0 = 16u * (uint32_t)((lane % CPR) ^ swz<D>(srow0));
+  auto lchk = [&](int p) -> uint32_t { return lchk0 ^ (16u * (uint32_t)swz<D>(p * RPI)); };
+  const uint32_t kro = (uint32_t)srow0 * rb_view, vro = (uint32_t)srow0 * rbv_view;
   char* const kbuf0 = reinterpret_cast<char*>(sm.K[0]);
   char* const vbuf0 = reinterpret_cast<char*>(sm.V[0]);
   constexpr uint32_t BUFB = 64u * D * 2u;   // bytes of one K or V stage
@@ -214,7 +215,7 @@ __device__ __forceinline__ void attn_pair(AttnSmem<D>& sm, const Dims& dm, const
     if (c.src < 0) {
       const uint32_t s0 = (uint32_t)(64 * c.idx) * rb_view;
 #pragma unroll
-      for (int p = 0; p < PPW; ++p) dma16(rk_view, dst + p * 1024, kdo[p & 1], s0 + (uint32_t)(p * RPI) * rb_view);
+      for (int p = 0; p < PPW; ++p) dma16(rk_view, dst + p * 1024, kro + lchk(p), s0 + (uint32_t)(p * RPI) * rb_view);
     } else {
       const int32_t* gl = c.src == 0 ? gl0 : gl1;
       const int e0 = 64 * c.idx, el = (c.src == 0 ? gcnt0 : g1) - 1;
@@ -223,7 +224,7 @@ __device__ __forceinline__ void attn_pair(AttnSmem<D>& sm, const Dims& dm, const
       for (int p = 0; p < PPW; ++p) gi[p] = gl[min(e0 + srow0 + p * RPI, el)];
 #pragma unroll
       for (int p = 0; p < PPW; ++p)
-        dma16(rk, dst + p * 1024, e0 + srow0 + p * RPI <= el ? (uint32_t)gi[p] * rbk + lchk16[p & 1] : OOB, 0);
+        dma16(rk, dst + p * 1024, e0 + srow0 + p * RPI <= el ? (uint32_t)gi[p] * rbk + lchk(p) : OOB, 0);
     }
   };
   auto dma_v = [&](const Chunk& c, int par) {
@@ -231,7 +232,7 @@ __device__ __forceinline__ void attn_pair(AttnSmem<D>& sm, const Dims& dm, const
     if (c.src < 0) {
       const uint32_t s0 = (uint32_t)(64 * c.idx) * rbv_view;
 #pragma unroll
-      for (int p = 0; p < PPW; ++p) dma16(rv_view, dst + p * 1024, vdo[p & 1], s0 + (uint32_t)(p * RPI) * rbv_view);
+      for (int p = 0; p < PPW; ++p) dma16(rv_view, dst + p * 1024, vro + lchk(p), s0 + (uint32_t)(p * RPI) * rbv_view);
     } else {
       const int32_t* gl = c.src == 0 ? gl0 : gl1;
       const int e0 = 64 * c.idx, el = (c.src == 0 ? gcnt0 : g1) - 1;
@@ -240,7 +241,7 @@ __device__ __forceinline__ void attn_pair(AttnSmem<D>& sm, const Dims& dm, const
       for (int p = 0; p < PPW; ++p) gi[p] = gl[min(e0 + srow0 + p * RPI, el)];
 #pragma unroll
       for (int p = 0; p < PPW; ++p)
-        dma16(rv, dst + p * 1024, e0 + srow0 + p * RPI <= el ? (uint32_t)gi[p] * rbv + lchk16[p & 1] : OOB, 0);
+        dma16(rv, dst + p * 1024, e0 + srow0 + p * RPI <= el ? (uint32_t)gi[p] * rbv + lchk(p) : OOB, 0);
     }
   };
   // key positions of a chunk (wave 0, one per lane): the raw value, and whether
@@ -308,34 +309,40 @@ __device__ __forceinline__ void attn_pair(AttnSmem<D>& sm, const Dims& dm, const
   };
 
   // ---- per-lane LDS addresses of the MFMA operands ----
-  // K fragment (key block kb, d-step s): row 32kb + qc, logical chunk 2s + hh.
-  // The swizzle touches chunk bits 0-2 only, so 4 bases (s & 3) serve all s.
-  const int fq = swz(qc);
-  uint32_t kaddr[4];
-#pragma unroll
-  for (int j = 0; j < 4; ++j) kaddr[j] = (uint32_t)qc * (2u * D) + 16u * (uint32_t)(((2 * j) | hh) ^ fq);
-  // V^T fragment (d-block db, key step st): two transpose reads of 16-lane
+  // Within a stage, rows start at multiples of 2D bytes and the chunk bits sit
+  // above them untouched, so a swizzled address is a lane base XOR a constant.
+  // K fragment (key block kb, d-step s): row 32kb + qc, logical chunk 2s ^ hh.
+  const uint32_t ka = (uint32_t)qc * (2u * D) + 16u * (uint32_t)(hh ^ swz<D>(qc));
+  // V^T fragment (d-block db, key step st): two transpose reads by 16-lane
   // groups; group g = lane/16 covers d 32db + 16(g&1) + 0..15 and keys
   // 16st + 4(g>>1) + 0..3 (+8 for the second read).  Source lane i of a group
-  // addresses row (4(g>>1) + i/4), d 32db + 16(g&1) + 4(i%4).
+  // addresses row 4(g>>1) + i/4, d 32db + 16(g&1) + 4(i%4), i.e. logical chunk
+  // 4db ^ vcl and byte 8(i&1) within it.
   const int vg = lane >> 4, vi = lane & 15;
   const int vrow = 4 * (vg >> 1) + (vi >> 2);
-  const int vcl = 2 * (vg & 1) + ((vi & 3) >> 1);     // chunk within the 4-chunk d block
-  const int fv = swz(vrow);
-  uint32_t vaddr[2];
+  const int vcl = 2 * (vg & 1) + ((vi & 3) >> 1);
+  uint32_t va[2];
 #pragma unroll
   for (int e = 0; e < 2; ++e)
-    vaddr[e] = (uint32_t)vrow * (2u * D) + 16u * (uint32_t)((vcl ^ (fv & 3)) + 4 * (e ^ (fv >> 2))) + 8u * (vi & 1);
+    va[e] = (uint32_t)(vrow + 8 * e) * (2u * D) + 16u * (uint32_t)(vcl ^ swz<D>(vrow + 8 * e)) + 8u * (vi & 1);
 
+  // The bases pass through an empty asm once per chunk: the per-fragment XORs
+  // are then recomputed (one VALU each) instead of hoisted into 24 live
+  // registers.
+  uint32_t ka_l = ka, va_l[2] = {va[0], va[1]};
+  auto launder = [&]() {
+    asm volatile("" : "+v"(ka_l));
+    asm volatile("" : "+v"(va_l[0]), "+v"(va_l[1]));
+  };
   auto kfrag = [&](int par, int i) -> bf16x8 {   // i: key block i&1, d-step i>>1
     const int s = i >> 1, kb = i & 1;
-    const char* p = kbuf0 + par * BUFB + kaddr[s & 3] + 128 * (s >> 2) + kb * 32 * (2 * D);
+    const char* p = kbuf0 + par * BUFB + kb * 32 * (2 * D) + (ka_l ^ (32u * s));
     return as_bf16x8(ld16(p));
   };
   auto vfrag = [&](int par, int i) -> bf16x8 {   // i: d-block i%ND, key step i/ND
     const int db = i % ND, st = i / ND;
-    const char* p = vbuf0 + par * BUFB + vaddr[db & 1] + 128 * (db >> 1) + st * 16 * (2 * D);
-    const uint2 lo = ld_tr(p), hi = ld_tr(p + 8 * (2 * D));
+    const char* b = vbuf0 + par * BUFB + st * 16 * (2 * D);
+    const uint2 lo = ld_tr(b + (va_l[0] ^ (64u * db))), hi = ld_tr(b + (va_l[1] ^ (64u * db)));
     return as_bf16x8(make_uint4(lo.x, lo.y, hi.x, hi.y));
   };
 
@@ -486,12 +493,16 @@ __device__ __forceinline__ void attn_pair(AttnSmem<D>& sm, const Dims& dm, const
     }
     asm volatile("s_waitcnt vmcnt(0)" ::: "memory");
     __syncthreads();
+    launder();
     if (wave_has && (c0.memb & wbit)) s_chunk(sA, 0);
+    // step 0 copies K of chunk 2 over stage 0, which S^T of chunk 0 just read
+    __syncthreads();
   }
 
   // ---- chunk n (parity par): S^T of n+1 while n's softmax and P.V run ----
   auto step = [&](floatx16 (&scur)[2], floatx16 (&snxt)[2], int n, int par) {
     const bool has_n1 = n + 1 < n_chunks, has_n2 = n + 2 < n_chunks;
+    launder();
     // positions of chunk n+1 (loaded during the previous step) into their slot
     if (n >= 1 && has_n1 && w == 0) store_kp(kpreg, kpval, par ^ 1);
     if (has_n2) {
@@ -544,31 +555,33 @@ __device__ __forceinline__ void attn_pair(AttnSmem<D>& sm, const Dims& dm, const
   }
 }
 
-// Persistent workgroups: a workgroup drains the queue segment of its own XCD
-// (items popped with an atomic counter), then helps the other segments.
-// Every workgroup exits once all segments are empty.
+// Persistent workgroups.  The queue (heads sharing a KV head together, most
+// expensive pairs first) is dealt round-robin to the 8 XCDs: a workgroup pops
+// items x, x+8, x+16, ... of its own XCD x (atomic counter per XCD), then
+// helps the other XCDs.  All XCDs thus work on the same KV head at the same
+// time, and its K/V stream through the shared last-level cache once for all of
+// them.  Every workgroup exits once all counters have passed the end.
 template <int D>
 __global__ __launch_bounds__(256, 2) void k_attn(Dims dm, Tables tb, char* ws, const bf16_t* __restrict__ q,
                                                  const bf16_t* __restrict__ k, const bf16_t* __restrict__ v,
                                                  bf16_t* __restrict__ o, float* __restrict__ lse) {
   __shared__ AttnSmem<D> sm;
   __shared__ int sh_j;
-  const MMSA_CONST int64_t* seg = cptr<int64_t>(ws, dm.ws_seg);
-  int32_t* ctr = reinterpret_cast<int32_t*>(wsp<int64_t>(ws, dm.ws_seg) + N_XCD + 1);
+  int32_t* ctr = wsp<int32_t>(ws, dm.ws_ctr);
   const int32_t* items = wsp<const int32_t>(ws, dm.ws_enum_item);
-  // this workgroup's XCD (hardware XCC id), so its L2 serves its segment
+  const int64_t n_items = dm.n_items;
+  // this workgroup's XCD (hardware XCC id)
   const int x0 = (int)(__builtin_amdgcn_s_getreg((3 << 11) | (0 << 6) | 20) & (N_XCD - 1));
   for (int s = 0; s < N_XCD; ++s) {
     const int x = (x0 + s) % N_XCD;
-    const int64_t beg = seg[x], end = seg[x + 1];
     while (true) {
       if (threadIdx.x == 0) sh_j = atomicAdd(&ctr[x], 1);
       __syncthreads();
       // the popped index is the same in every lane; saying so keeps the item's
       // descriptors in scalar registers and its control flow uniform
-      const int64_t e = beg + __builtin_amdgcn_readfirstlane(sh_j);
+      const int64_t e = x + (int64_t)N_XCD * __builtin_amdgcn_readfirstlane(sh_j);
       __syncthreads();
-      if (e >= end) break;
+      if (e >= n_items) break;
       const uint32_t item = (uint32_t)__builtin_amdgcn_readfirstlane(items[e]);
       attn_pair<D>(sm, dm, tb, ws, q, k, v, o, lse, item);
     }

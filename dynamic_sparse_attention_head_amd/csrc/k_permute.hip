@@ -437,10 +437,8 @@ __global__ __launch_bounds__(256) void k_plan(Dims dm, Tables tb, char* ws) {
 // ---------------------------------------------------------------------------
 // Attention work queue.  Items (head, pair of adjacent query tiles) are ordered
 // by queue group (q heads sharing one b, KV head), then pair descending, then
-// head; the
-// order is cut into N_XCD contiguous segments of equal total cost, one per XCD,
-// so each XCD's workgroups stream one KV head's keys together through their L2
-// and start with the most expensive tiles.
+// head: the most expensive pairs of a KV head come first, and the attention
+// kernel deals the order round-robin to the XCDs.
 // ---------------------------------------------------------------------------
 
 // Queue position and cost of every (head, pair of adjacent query tiles).
@@ -471,51 +469,10 @@ __global__ __launch_bounds__(64) void k_queue_enum(Dims dm, Tables tb, char* ws)
   wsp<int32_t>(ws, dm.ws_enum_cost)[e] = (i0.w > 0 || i1.w > 0) ? max(cost, 1) : 0;
 }
 
-// Prefix sums of cost in queue order and the N_XCD segment boundaries.
-// One workgroup of 1024 threads.
-__global__ __launch_bounds__(1024) void k_queue_split(Dims dm, char* ws) {
-  const int32_t* cost = wsp<const int32_t>(ws, dm.ws_enum_cost);
-  int64_t* seg = wsp<int64_t>(ws, dm.ws_seg);
-  __shared__ long long part[1024];
-  __shared__ long long target[N_XCD + 1];
-  const int t = threadIdx.x;
-  const int64_t n = dm.n_items;
-  const int64_t per = (n + 1023) / 1024;
-  const int64_t b0 = min(n, t * per), b1 = min(n, b0 + per);
-  long long s = 0;
-  for (int64_t i = b0; i < b1; ++i) s += cost[i];
-  part[t] = s;
-  __syncthreads();
-  for (int off = 1; off < 1024; off <<= 1) {
-    const long long v = t >= off ? part[t - off] : 0;
-    __syncthreads();
-    part[t] += v;
-    __syncthreads();
-  }
-  const long long total = part[1023];
-  if (t <= N_XCD) target[t] = (total * t + N_XCD - 1) / N_XCD;
-  __syncthreads();
-  // segment x (x >= 1) starts right after the item whose cost crosses target[x]
-  long long run = part[t] - s;
-  for (int64_t i = b0; i < b1; ++i) {
-    const long long c = cost[i];
-    for (int x = 1; x < N_XCD; ++x)
-      if (run < target[x] && run + c >= target[x]) seg[x] = i + 1;
-    run += c;
-  }
-  __syncthreads();
-  if (t == 0) {
-    seg[0] = 0;
-    seg[N_XCD] = n;
-    int64_t last = 0;
-    for (int x = 1; x < N_XCD; ++x) {
-      if (total == 0) seg[x] = n;
-      seg[x] = seg[x] < last ? last : (seg[x] > n ? n : seg[x]);
-      last = seg[x];
-    }
-    int32_t* ctr = reinterpret_cast<int32_t*>(seg + N_XCD + 1);
-    for (int x = 0; x < N_XCD; ++x) ctr[x] = 0;
-  }
+// Per-XCD pop counters of the attention kernel back to zero.
+__global__ __launch_bounds__(64) void k_queue_reset(Dims dm, char* ws) {
+  int32_t* ctr = wsp<int32_t>(ws, dm.ws_ctr);
+  if (threadIdx.x < N_XCD) ctr[threadIdx.x] = 0;
 }
 
 hipError_t launch_plan(const Dims& dm, const Tables& tb, char* ws, int max_tiles, int max_bm_words,
@@ -523,7 +480,7 @@ hipError_t launch_plan(const Dims& dm, const Tables& tb, char* ws, int max_tiles
   if (max_tiles > 0 && tb.n_heads > 0) {
     k_plan<<<dim3(max_tiles, (unsigned)tb.n_heads), 256, (size_t)max_bm_words * 8, s>>>(dm, tb, ws);
     k_queue_enum<<<dim3((max_tiles / 2 + 64) / 64, (unsigned)tb.n_heads), 64, 0, s>>>(dm, tb, ws);
-    k_queue_split<<<1, 1024, 0, s>>>(dm, ws);
+    k_queue_reset<<<1, 64, 0, s>>>(dm, ws);
   }
   return hipGetLastError();
 }

@@ -612,7 +612,7 @@ mmsa_status build_layout(const mmsa_layer_desc* desc, Layout& Lo) {
   dm.n_items = Lo.max_items;
   dm.ws_enum_item = bp.take(4 * Lo.max_items);
   dm.ws_enum_cost = bp.take(4 * Lo.max_items);
-  dm.ws_seg = bp.take(8 * (N_XCD + 1) + 4 * N_XCD);
+  dm.ws_ctr = bp.take(4 * N_XCD);
   // estimation: stats and partials
   for (EstJob& J : Lo.jobs) {
     J.ws_stats = bp.take(8ll * EST_ROWS);

@@ -153,7 +153,7 @@ struct Dims {
   int64_t n_items;           // queue length: every (head, pair of adjacent query tiles)
   int64_t ws_enum_item;      // int32 [n_items]: (bh << 16) | pair in queue order
   int64_t ws_enum_cost;      // int32 [n_items]: cost of each queued item
-  int64_t ws_seg;            // int64 [N_XCD + 1] segment starts, then int32 [N_XCD] counters
+  int64_t ws_ctr;            // int32 [N_XCD] pop counters of the attention queue
   int64_t ws_flag;           // int32 debug / status word
 };
 
