@@ -18,6 +18,14 @@
 
 namespace mmsa {
 
+// Merge two (max, sum of 2^(x - max)) pairs of one row (hardware exp2).
+__device__ __forceinline__ float2 lse2_merge_hw(float2 a, float2 b) {
+  if (a.x == -INFINITY) return b;
+  if (b.x == -INFINITY) return a;
+  const float m = fmaxf(a.x, b.x);
+  return make_float2(m, a.y * __builtin_amdgcn_exp2f(a.x - m) + b.y * __builtin_amdgcn_exp2f(b.x - m));
+}
+
 // ---------------------------------------------------------------------------
 // Fragments of 64 keys x D dims of K for the A operand (rows = keys).
 // ---------------------------------------------------------------------------
@@ -104,13 +112,13 @@ __global__ __launch_bounds__(256) void k_est_pass1(Dims dm, Tables tb, char* ws,
       float sm = 0.f;
       if (mx != -INFINITY) {
 #pragma unroll
-        for (int e = 0; e < 16; ++e) sm += exp2f(xs[e] - mx);
+        for (int e = 0; e < 16; ++e) sm += __builtin_amdgcn_exp2f(xs[e] - mx);
       }
       float2 st = make_float2(mx, sm);
 #pragma unroll
       for (int m = 16; m <= 32; m <<= 1) {
         float2 o = make_float2(shfl_xor_f(st.x, m), shfl_xor_f(st.y, m));
-        st = lse2_merge(st, o);
+        st = lse2_merge_hw(st, o);
       }
       if (g4 == 0) red[par][w][row] = st;
     }
@@ -118,21 +126,29 @@ __global__ __launch_bounds__(256) void k_est_pass1(Dims dm, Tables tb, char* ws,
     if (tid < 64) {
       float2 st = red[par][0][tid];
 #pragma unroll
-      for (int ww = 1; ww < 4; ++ww) st = lse2_merge(st, red[par][ww][tid]);
+      for (int ww = 1; ww < 4; ++ww) st = lse2_merge_hw(st, red[par][ww][tid]);
       wsp<float2>(ws, J.ws_part)[(int64_t)blockIdx.x * 64 + tid] = st;
     }
   }
 }
 
-// Final (max, sum) per estimation row, merging chunk partials in order.
-__global__ __launch_bounds__(64) void k_est_combine(Tables tb, char* ws) {
+// Final (max, sum) per estimation row: 16 waves each merge a contiguous range
+// of chunk partials (lane = row), then the 16 results are merged.
+__global__ __launch_bounds__(1024) void k_est_combine(Tables tb, char* ws) {
   const EstJob& J = wsp<const EstJob>(ws, tb.off_jobs)[blockIdx.x];
-  const int r = threadIdx.x;
+  const int r = threadIdx.x & 63, wv = threadIdx.x >> 6;
   const float2* part = wsp<const float2>(ws, J.ws_part);
   const int last = J.imax / EST_CK + 1;
+  const int per = (last + 15) / 16, c0 = wv * per, c1 = min(last, c0 + per);
   float2 st = make_float2(-INFINITY, 0.f);
-  for (int c = 0; c < last; ++c) st = lse2_merge(st, part[(int64_t)c * 64 + r]);
-  wsp<float2>(ws, J.ws_stats)[r] = st;
+  for (int c = c0; c < c1; ++c) st = lse2_merge_hw(st, part[(int64_t)c * 64 + r]);
+  __shared__ float2 red[16][64];
+  red[wv][r] = st;
+  __syncthreads();
+  if (wv == 0) {
+    for (int w2 = 1; w2 < 16; ++w2) st = lse2_merge_hw(st, red[w2][r]);
+    wsp<float2>(ws, J.ws_stats)[r] = st;
+  }
 }
 
 // ---------------------------------------------------------------------------
@@ -202,7 +218,7 @@ __global__ __launch_bounds__(256) void k_est_pass2(Dims dm, Tables tb, char* ws,
 #pragma unroll
         for (int i = 0; i < 4; ++i) {
           const bool valid = rv && kk[i] >= 0 && kk[i] <= pos;
-          pp[i] = valid ? exp2f(acc[i] * dm.scale_log2 - st.x) * inv_l : 0.f;
+          pp[i] = valid ? __builtin_amdgcn_exp2f(acc[i] * dm.scale_log2 - st.x) * inv_l : 0.f;
         }
         *reinterpret_cast<float4*>(&P[row][64 * w + 16 * kb + 4 * g4]) = pv;
       }
@@ -278,14 +294,40 @@ __global__ __launch_bounds__(256) void k_s_finalize(Tables tb, char* ws) {
 // key (4 rounds of 8 bits), then one compaction pass in index order.
 // grid (tasks), block 1024.
 // ---------------------------------------------------------------------------
+// Workgroup-wide exclusive prefix sum of v in thread order (1024 threads);
+// sets *total.  red: 17 ints of LDS.  Two barriers.
+__device__ __forceinline__ int block_excl_sum(int v, int* red, int* total) {
+  const int lane = threadIdx.x & 63, wv = threadIdx.x >> 6, nw = blockDim.x >> 6;
+  int inc = v;
+#pragma unroll
+  for (int m = 1; m < 64; m <<= 1) {
+    const int o = __shfl_up(inc, m, 64);
+    if (lane >= m) inc += o;
+  }
+  if (lane == 63) red[wv] = inc;
+  __syncthreads();
+  int before = 0, tot = 0;
+  for (int i = 0; i < nw; ++i) {
+    const int c = red[i];
+    before += (i < wv) ? c : 0;
+    tot += c;
+  }
+  __syncthreads();
+  *total = tot;
+  return before + inc - v;
+}
+
 __global__ __launch_bounds__(1024) void k_topk(Tables tb, char* ws) {
+  constexpr int E = 8;   // elements per thread per pass step (index order: thread-major)
   const TopkTask T = wsp<const TopkTask>(ws, tb.off_topk)[blockIdx.x];
   const float* __restrict__ x = wsp<const float>(ws, T.ws_x);
   int32_t* out = wsp<int32_t>(ws, T.ws_out);
-  const int tid = threadIdx.x, nthr = blockDim.x;
+  const int tid = threadIdx.x, nthr = blockDim.x, wv = tid >> 6;
   const int lo = T.lo, hi = T.hi, n = hi - lo;
   const int k = min(T.k, n);
-  __shared__ uint32_t hist[256];
+  // one histogram per wave: scores cluster in a few exponent bins, and 16
+  // waves incrementing one shared counter would serialise on it
+  __shared__ uint32_t hist[16][256];
   __shared__ uint32_t sh_pref, sh_mask, sh_krem;
   __shared__ int red[17];
   if (k <= 0) {
@@ -295,19 +337,34 @@ __global__ __launch_bounds__(1024) void k_topk(Tables tb, char* ws) {
   uint32_t pref = 0, pmask = 0, krem = (uint32_t)k;
   if (k < n) {
     for (int shift = 24; shift >= 0; shift -= 8) {
-      for (int i = tid; i < 256; i += nthr) hist[i] = 0;
+      for (int i = tid; i < 16 * 256; i += nthr) (&hist[0][0])[i] = 0;
       __syncthreads();
-      for (int i = lo + tid; i < hi; i += nthr) {
-        const uint32_t key = order_key(x[i]);
-        if ((key & pmask) == pref) atomicAdd(&hist[(key >> shift) & 255u], 1u);
+      for (int s0 = lo; s0 < hi; s0 += E * nthr) {
+        uint32_t key[E];
+#pragma unroll
+        for (int j = 0; j < E; ++j) {
+          const int i = s0 + j * nthr + tid;
+          key[j] = i < hi ? order_key(x[i]) : 0u;
+        }
+#pragma unroll
+        for (int j = 0; j < E; ++j) {
+          const int i = s0 + j * nthr + tid;
+          if (i < hi && (key[j] & pmask) == pref) atomicAdd(&hist[wv][(key[j] >> shift) & 255u], 1u);
+        }
+      }
+      __syncthreads();
+      if (tid < 256) {
+        uint32_t c = 0;
+        for (int ww = 0; ww < nthr / 64; ++ww) c += hist[ww][tid];
+        hist[0][tid] = c;
       }
       __syncthreads();
       if (tid == 0) {
         uint32_t cum = 0;
         int b = 255;
         for (; b > 0; --b) {
-          if (cum + hist[b] >= krem) break;
-          cum += hist[b];
+          if (cum + hist[0][b] >= krem) break;
+          cum += hist[0][b];
         }
         sh_krem = krem - cum;
         sh_pref = pref | ((uint32_t)b << shift);
@@ -323,20 +380,36 @@ __global__ __launch_bounds__(1024) void k_topk(Tables tb, char* ws) {
     pref = 0;
     krem = (uint32_t)n;
   }
+  // Compaction in index order: thread t owns elements s0 + E*t .. + E-1 of each
+  // E*nthr block; keys above the threshold are taken, equal keys by rank.
   const uint32_t thr = pref;
   const int need = (int)krem;
   int base = 0, eqb = 0;
-  for (int s0 = lo; s0 < hi; s0 += nthr) {
-    const int i = s0 + tid;
-    const bool in = i < hi;
-    const uint32_t key = in ? order_key(x[i]) : 0u;
-    const bool eq = in && key == thr;
-    const bool gt = in && key > thr;
+  for (int s0 = lo; s0 < hi; s0 += E * nthr) {
+    uint32_t key[E];
+    int n_eq = 0;
+#pragma unroll
+    for (int j = 0; j < E; ++j) {
+      const int i = s0 + E * tid + j;
+      key[j] = i < hi ? order_key(x[i]) : 0u;
+      n_eq += (i < hi && key[j] == thr) ? 1 : 0;
+    }
     int eq_tot, sel_tot;
-    const int eq_rank = eqb + block_excl_count(eq, red, &eq_tot);
-    const bool sel = gt || (eq && eq_rank < need);
-    const int r = base + block_excl_count(sel, red, &sel_tot);
-    if (sel) out[r] = i;
+    int er = eqb + block_excl_sum(n_eq, red, &eq_tot);
+    uint32_t selm = 0;
+#pragma unroll
+    for (int j = 0; j < E; ++j) {
+      const int i = s0 + E * tid + j;
+      const bool in = i < hi;
+      const bool eq = in && key[j] == thr;
+      const bool sel = (in && key[j] > thr) || (eq && er < need);
+      er += eq ? 1 : 0;
+      selm |= sel ? (1u << j) : 0u;
+    }
+    int r = base + block_excl_sum(__popc(selm), red, &sel_tot);
+#pragma unroll
+    for (int j = 0; j < E; ++j)
+      if (selm & (1u << j)) out[r++] = s0 + E * tid + j;
     base += sel_tot;
     eqb += eq_tot;
   }
@@ -351,12 +424,19 @@ __device__ __forceinline__ int64_t grid_u(float v, int64_t cap) {
   return u < cap ? u : cap;
 }
 
+// Clipped fixed-point scores u (kept for the stride scan; u <= 64 * 2^24 since
+// a score sums at most 64 probabilities) and their total U.
 __global__ __launch_bounds__(1024) void k_grid_sum(Tables tb, char* ws) {
   const GridTask T = wsp<const GridTask>(ws, tb.off_grid)[blockIdx.x];
   const float* v = wsp<const float>(ws, T.ws_v);
+  int32_t* u = wsp<int32_t>(ws, T.ws_u);
   __shared__ long long part[1024];
   long long s = 0;
-  for (int x = threadIdx.x; x < T.D; x += blockDim.x) s += grid_u(v[x], T.cap);
+  for (int x = threadIdx.x; x < T.D; x += blockDim.x) {
+    const int64_t ux = grid_u(v[x], T.cap);
+    u[x] = (int32_t)ux;
+    s += ux;
+  }
   part[threadIdx.x] = s;
   __syncthreads();
   for (int st = 512; st > 0; st >>= 1) {
@@ -384,15 +464,25 @@ __global__ __launch_bounds__(1024) void k_grid_scan(Tables tb, char* ws) {
   const GridTask T = wsp<const GridTask>(ws, tb.off_grid)[blockIdx.y];
   const int sig = T.s_lo + blockIdx.x;
   if (sig > T.s_hi) return;
-  const float* v = wsp<const float>(ws, T.ws_v);
+  const int32_t* u = wsp<const int32_t>(ws, T.ws_u);
   const long long U = *wsp<const long long>(ws, T.ws_U);
   __shared__ GridCand c[MAX_STRIDE];
   __shared__ int idx[MAX_STRIDE];
+  __shared__ long long part[MAX_STRIDE];
   const int f = threadIdx.x;
+  // every thread works: phase t % sig over every S-th line position, S = slices
+  {
+    const int S = MAX_STRIDE / sig, ph = f % sig, sl = f / sig;
+    long long F = 0;
+    if (sl < S)
+      for (int64_t x = ph + (int64_t)sl * sig; x < T.D; x += (int64_t)S * sig) F += u[x];
+    part[f] = F;
+  }
+  __syncthreads();
   GridCand me{0, 0, -1};
   if (f < sig) {
     long long F = 0;
-    for (int x = f; x < T.D; x += sig) F += grid_u(v[x], T.cap);
+    for (int sl = 0; sl < MAX_STRIDE / sig; ++sl) F += part[sl * sig + f];
     const int cnt = (T.D - f + sig - 1) / sig;
     me.X = (long long)T.D * F - (long long)cnt * U;
     me.cnt = cnt;
@@ -487,7 +577,7 @@ hipError_t launch_est_pass1(const Dims& dm, const Tables& tb, char* ws, const vo
     k_est_pass1<128><<<grid, 256, 0, s>>>(dm, tb, ws, (const bf16_t*)q, (const bf16_t*)k);
   else
     k_est_pass1<64><<<grid, 256, 0, s>>>(dm, tb, ws, (const bf16_t*)q, (const bf16_t*)k);
-  k_est_combine<<<(unsigned)tb.n_jobs, 64, 0, s>>>(tb, ws);
+  k_est_combine<<<(unsigned)tb.n_jobs, 1024, 0, s>>>(tb, ws);
   return hipGetLastError();
 }
 

@@ -649,6 +649,7 @@ mmsa_status build_layout(const mmsa_layer_desc* desc, Layout& Lo) {
   for (GridTask& T : Lo.grids) {
     T.ws_v = Lo.jobs[T.job].pair[0].ws_v;
     T.ws_U = bp.take(8);
+    T.ws_u = bp.take(4ll * std::max(T.D, 1));
     T.ws_cand = bp.take(16ll * MAX_PHASES * std::max(T.s_hi - T.s_lo + 1, 1));
     T.ws_out = bp.take(4ll * GRID_OUT);
   }

@@ -99,6 +99,7 @@ struct GridTask {
   int64_t cap;               // clip level of the fixed-point scores
   int64_t ws_v;              // float [L] vertical scores in grid coordinates
   int64_t ws_U;              // int64 sum of clipped scores
+  int64_t ws_u;              // int32 [D] clipped fixed-point scores
   int64_t ws_cand;           // per stride: MAX_PHASES x (X, cnt, phase)
   int64_t ws_out;            // int32 [GRID_OUT]: stride, w, n_line, phases
 };
