@@ -160,6 +160,9 @@ def main():
     ap.add_argument("--no-cpu", action="store_true")
     ap.add_argument("--cpu-rows", type=int, default=768)
     ap.add_argument("--copy-calibration", action="store_true")
+    ap.add_argument("--materialize", action="store_true",
+                    help="explicit gathers of permuted Q / grouped K,V and an output scatter "
+                         "instead of index-based loads and stores in the attention call")
     args = ap.parse_args()
     if args.gpus != 1:
         print(f"bench.py runs on one GPU only (asked for --gpus {args.gpus}); the path shards by KV head "
@@ -173,7 +176,7 @@ def main():
     log(f"[bench] generating {spec.name}: L={spec.L} Hq={spec.Hq} Hkv={spec.Hkv} d={spec.d}")
     lay = synth.make_layer(spec, dev)
     q, k, v = lay["q"], lay["k"], lay["v"]
-    L = mmsa.Layer(q, k, v, spec.heads, segs=spec.segs)
+    L = mmsa.Layer(q, k, v, spec.heads, segs=spec.segs, materialize=args.materialize)
     L.alloc_workspace()
     o = torch.empty((1, spec.Hq, spec.L, spec.d), dtype=torch.bfloat16, device=dev)
     lse = torch.empty((1, spec.Hq, spec.L), dtype=torch.float32, device=dev)
@@ -243,6 +246,7 @@ def main():
         "data": "synthetic",
         "config": {"workload": f"{spec.name}: one causal prefill layer, L={spec.L}, {spec.Hq} q / {spec.Hkv} kv "
                                f"heads, d={spec.d}", "batch": 1, "seq_len": spec.L,
+                   "permutation": "materialised" if args.materialize else "index-based",
                    "heads": "16 vertical-slash (1000/4096), 8 block (top-100), 8 A-shape (128, 4096)"
                    if args.config == 2 else str([h["pattern"] for h in spec.heads])},
         "roofline": {"bound": "mfma", "achieved": round(achieved, 2), "peak": PEAK_BF16_TFLOPS,

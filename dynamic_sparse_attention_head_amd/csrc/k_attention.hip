@@ -41,11 +41,11 @@ __device__ __forceinline__ floatx16 mfma32(bf16x8 a, bf16x8 b, floatx16 c) {
 }
 
 template <int D>
-struct AttnSmem {   // 2 stages of K and V (row-major, swizzled), key positions and their max
+struct AttnSmem {   // 2 stages of K and V (row-major, swizzled); key positions and their max, 4 slots
   bf16_t K[2][64 * D];
   bf16_t V[2][64 * D];
-  int kp[2][64];
-  int kmax[2];
+  int kp[4][64];
+  int kmax[4];
 };
 
 // Swizzle of the 16-byte chunks of row r: physical chunk = logical ^ swz(r).
@@ -181,21 +181,26 @@ __device__ __forceinline__ void attn_pair(AttnSmem<D>& sm, const Dims& dm, const
   const int n_chunks = n_union + n_gath;
   const int gcnt0 = grid ? max(g0, g1) : g0;
   const bool grouped_view = H.view_kind == VIEW_GROUPED;
+  // grouped view without a grouped copy of K/V: its tiles are read row by row
+  // through the grouped-slot map, like gathered columns
+  const bool grouped_idx = grouped_view && H.ws_kgrp < 0;
   const int32_t* pgrp = wsp<const int32_t>(ws, dm.ws_pgrp);
   const bool ashape = H.pattern == MMSA_ASHAPE;
   const int sink = H.sink, window = H.window;
 
   // buffer views: the head's key view (tiles) and its original K/V (gathered columns)
-  const uint32_t rb_view = grouped_view ? 2u * D : 2u * (uint32_t)dm.k_sl;
-  const uint32_t rbv_view = grouped_view ? 2u * D : 2u * (uint32_t)dm.v_sl;
+  const bool grouped_copy = grouped_view && !grouped_idx;
+  const uint32_t rb_view = grouped_copy ? 2u * D : 2u * (uint32_t)dm.k_sl;
+  const uint32_t rbv_view = grouped_copy ? 2u * D : 2u * (uint32_t)dm.v_sl;
   const uint32_t rbk = 2u * (uint32_t)dm.k_sl, rbv = 2u * (uint32_t)dm.v_sl;
   const int view_rows = grouped_view ? dm.L_grp : dm.L;
+  const int copy_rows = grouped_copy ? dm.L_grp : dm.L;
   const __amdgpu_buffer_rsrc_t rk_view =
-      make_rsrc(grouped_view ? (const void*)wsp<const bf16_t>(ws, H.ws_kgrp) : (const void*)(k + H.k_off),
-                (uint32_t)(view_rows - 1) * rb_view + 2u * D);
+      make_rsrc(grouped_copy ? (const void*)wsp<const bf16_t>(ws, H.ws_kgrp) : (const void*)(k + H.k_off),
+                (uint32_t)(copy_rows - 1) * rb_view + 2u * D);
   const __amdgpu_buffer_rsrc_t rv_view =
-      make_rsrc(grouped_view ? (const void*)wsp<const bf16_t>(ws, H.ws_vgrp) : (const void*)(v + H.v_off),
-                (uint32_t)(view_rows - 1) * rbv_view + 2u * D);
+      make_rsrc(grouped_copy ? (const void*)wsp<const bf16_t>(ws, H.ws_vgrp) : (const void*)(v + H.v_off),
+                (uint32_t)(copy_rows - 1) * rbv_view + 2u * D);
   const __amdgpu_buffer_rsrc_t rk = make_rsrc(k + H.k_off, (uint32_t)(dm.L - 1) * rbk + 2u * D);
   const __amdgpu_buffer_rsrc_t rv = make_rsrc(v + H.v_off, (uint32_t)(dm.L - 1) * rbv + 2u * D);
 
@@ -210,38 +215,38 @@ __device__ __forceinline__ void attn_pair(AttnSmem<D>& sm, const Dims& dm, const
   char* const kbuf0 = reinterpret_cast<char*>(sm.K[0]);
   char* const vbuf0 = reinterpret_cast<char*>(sm.V[0]);
   constexpr uint32_t BUFB = 64u * D * 2u;   // bytes of one K or V stage
-  auto dma_k = [&](const Chunk& c, int par) {
+  // Copies of this wave's rows of chunk c (key positions in LDS slot ks).
+  // View tiles are contiguous rows of the view; gathered columns, and tiles of
+  // an index-read grouped view, are rows listed by original position, read
+  // from the chunk's key positions (KPOS_NONE: no token, copied as zeros).
+  auto dma_k = [&](const Chunk& c, int par, int ks) {
     char* dst = kbuf0 + par * BUFB + (w * PPW) * 1024;
-    if (c.src < 0) {
+    if (c.src < 0 && !grouped_idx) {
       const uint32_t s0 = (uint32_t)(64 * c.idx) * rb_view;
 #pragma unroll
       for (int p = 0; p < PPW; ++p) dma16(rk_view, dst + p * 1024, kro + lchk(p), s0 + (uint32_t)(p * RPI) * rb_view);
     } else {
-      const int32_t* gl = c.src == 0 ? gl0 : gl1;
-      const int e0 = 64 * c.idx, el = (c.src == 0 ? gcnt0 : g1) - 1;
       int gi[PPW];
 #pragma unroll
-      for (int p = 0; p < PPW; ++p) gi[p] = gl[min(e0 + srow0 + p * RPI, el)];
+      for (int p = 0; p < PPW; ++p) gi[p] = sm.kp[ks][srow0 + p * RPI];
 #pragma unroll
       for (int p = 0; p < PPW; ++p)
-        dma16(rk, dst + p * 1024, e0 + srow0 + p * RPI <= el ? (uint32_t)gi[p] * rbk + lchk(p) : OOB, 0);
+        dma16(rk, dst + p * 1024, gi[p] != KPOS_NONE ? (uint32_t)gi[p] * rbk + lchk(p) : OOB, 0);
     }
   };
-  auto dma_v = [&](const Chunk& c, int par) {
+  auto dma_v = [&](const Chunk& c, int par, int ks) {
     char* dst = vbuf0 + par * BUFB + (w * PPW) * 1024;
-    if (c.src < 0) {
+    if (c.src < 0 && !grouped_idx) {
       const uint32_t s0 = (uint32_t)(64 * c.idx) * rbv_view;
 #pragma unroll
       for (int p = 0; p < PPW; ++p) dma16(rv_view, dst + p * 1024, vro + lchk(p), s0 + (uint32_t)(p * RPI) * rbv_view);
     } else {
-      const int32_t* gl = c.src == 0 ? gl0 : gl1;
-      const int e0 = 64 * c.idx, el = (c.src == 0 ? gcnt0 : g1) - 1;
       int gi[PPW];
 #pragma unroll
-      for (int p = 0; p < PPW; ++p) gi[p] = gl[min(e0 + srow0 + p * RPI, el)];
+      for (int p = 0; p < PPW; ++p) gi[p] = sm.kp[ks][srow0 + p * RPI];
 #pragma unroll
       for (int p = 0; p < PPW; ++p)
-        dma16(rv, dst + p * 1024, e0 + srow0 + p * RPI <= el ? (uint32_t)gi[p] * rbv + lchk(p) : OOB, 0);
+        dma16(rv, dst + p * 1024, gi[p] != KPOS_NONE ? (uint32_t)gi[p] * rbv + lchk(p) : OOB, 0);
     }
   };
   // key positions of a chunk (wave 0, one per lane): the raw value, and whether
@@ -375,11 +380,11 @@ __device__ __forceinline__ void attn_pair(AttnSmem<D>& sm, const Dims& dm, const
   };
   // mask and running-max update of one chunk's logits (the part of the softmax
   // that may branch); returns the max to subtract
-  auto soft_a = [&](floatx16 (&sa)[2], int par) -> float {
-    const bool full = !ashape && uniform(sm.kmax[par]) <= wave_qmin;
+  auto soft_a = [&](floatx16 (&sa)[2], int ks) -> float {
+    const bool full = !ashape && uniform(sm.kmax[ks]) <= wave_qmin;
     if (!full) {
       // one lane-dependent base, constant offsets per (kb, i)
-      const char* kpb = reinterpret_cast<const char*>(sm.kp[0]) + par * 256 + 16 * hh;
+      const char* kpb = reinterpret_cast<const char*>(sm.kp[0]) + ks * 256 + 16 * hh;
 #pragma unroll
       for (int kb = 0; kb < 2; ++kb) {
 #pragma unroll
@@ -472,25 +477,28 @@ __device__ __forceinline__ void attn_pair(AttnSmem<D>& sm, const Dims& dm, const
     __builtin_amdgcn_sched_barrier(0);
   };
 
-  // ---- prologue: K, V, positions of chunk 0; K, positions of chunk 1 ----
-  Chunk c0 = next_chunk(0), c1 = next_chunk(1), c2 = next_chunk(2);
+  // ---- prologue: positions of chunks 0-2; K, V of chunk 0; K of chunk 1 ----
+  // Key positions of chunk m live in LDS slot m % 4 from the end of step m-3
+  // (chunks 0-2: the prologue) until step m: the copies of K (step m-2) and V
+  // (step m-1) read their rows there, so no copy waits on a global load.
+  Chunk c0 = next_chunk(0), c1 = next_chunk(1), c2 = next_chunk(2), c3 = next_chunk(3);
   int kpreg = -1;
   bool kpval = false;
   floatx16 sA[2], sB[2];
   if (n_chunks > 0) {
-    dma_k(c0, 0);
-    dma_v(c0, 0);
-    if (n_chunks > 1) dma_k(c1, 1);
     if (w == 0) {
-      bool va;
+      bool va, vb, vc;
       const int a = load_kp(c0, va);
+      const int b = n_chunks > 1 ? load_kp(c1, vb) : -1;
+      const int cc = n_chunks > 2 ? load_kp(c2, vc) : -1;
       store_kp(a, va, 0);
-      if (n_chunks > 1) {
-        bool vb;
-        const int b = load_kp(c1, vb);
-        store_kp(b, vb, 1);
-      }
+      if (n_chunks > 1) store_kp(b, vb, 1);
+      if (n_chunks > 2) store_kp(cc, vc, 2);
     }
+    __syncthreads();
+    dma_k(c0, 0, 0);
+    dma_v(c0, 0, 0);
+    if (n_chunks > 1) dma_k(c1, 1, 1);
     asm volatile("s_waitcnt vmcnt(0)" ::: "memory");
     __syncthreads();
     launder();
@@ -501,19 +509,17 @@ __device__ __forceinline__ void attn_pair(AttnSmem<D>& sm, const Dims& dm, const
 
   // ---- chunk n (parity par): S^T of n+1 while n's softmax and P.V run ----
   auto step = [&](floatx16 (&scur)[2], floatx16 (&snxt)[2], int n, int par) {
-    const bool has_n1 = n + 1 < n_chunks, has_n2 = n + 2 < n_chunks;
+    const bool has_n1 = n + 1 < n_chunks, has_n2 = n + 2 < n_chunks, has_n3 = n + 3 < n_chunks;
     launder();
-    // positions of chunk n+1 (loaded during the previous step) into their slot
-    if (n >= 1 && has_n1 && w == 0) store_kp(kpreg, kpval, par ^ 1);
-    if (has_n2) {
-      dma_k(c2, par);   // K of n+2 replaces K of n (read by the previous step)
-      if (w == 0) kpreg = load_kp(c2, kpval);
-    }
-    if (has_n1) dma_v(c1, par ^ 1);   // V of n+1 replaces V of n-1
+    // positions of chunk n+3, stored at the end of this step into the slot of
+    // chunk n-1 (read for the last time in the previous step)
+    if (has_n3 && w == 0) kpreg = load_kp(c3, kpval);
+    if (has_n2) dma_k(c2, par, (n + 2) & 3);       // K of n+2 replaces K of n (read by the previous step)
+    if (has_n1) dma_v(c1, par ^ 1, (n + 1) & 3);   // V of n+1 replaces V of n-1
     const bool doS = wave_has && has_n1 && (c1.memb & wbit);
     const bool doP = wave_has && (c0.memb & wbit);
     if (doP) {
-      const float m_use = soft_a(scur, par);
+      const float m_use = soft_a(scur, n & 3);
       uint32_t pk[16];
       if (doS) s_and_soft(snxt, par ^ 1, scur, m_use, pk);
       else soft_b(scur, m_use, pk);
@@ -522,10 +528,12 @@ __device__ __forceinline__ void attn_pair(AttnSmem<D>& sm, const Dims& dm, const
       s_chunk(snxt, par ^ 1);
     }
     asm volatile("s_waitcnt vmcnt(0)" ::: "memory");
+    if (has_n3 && w == 0) store_kp(kpreg, kpval, (n + 3) & 3);
     __syncthreads();
     c0 = c1;
     c1 = c2;
-    c2 = next_chunk(n + 3);
+    c2 = c3;
+    c3 = next_chunk(n + 4);
   };
   for (int n = 0; n < n_chunks; n += 2) {
     step(sA, sB, n, 0);

@@ -75,6 +75,7 @@ struct Layout {
   int64_t gridrow_off = 0, gridrow_bytes = 0; // grid row orders (filled with -1)
   bool need_seg = false, any_vs_est = false, any_block = false;
   bool empty = false;
+  bool materialize = false;   // explicit gathers and output scatter (MMSA_FLAG_MATERIALIZE)
   // per (bh, part) index-set facts for mmsa_index_meta / views: job index and pair index
   std::vector<std::vector<std::pair<int, int>>> set_of;   // [bh][part] -> (job, pair) or (-1,-1)
 };
@@ -138,8 +139,8 @@ mmsa_status build_layout(const mmsa_layer_desc* desc, Layout& Lo) {
     set_err("head dimension d=%d is not supported (64 or 128)", D.d);
     return MMSA_UNSUPPORTED;
   }
-  if (D.flags != 0) {
-    set_err("flags must be 0");
+  if ((D.flags & ~MMSA_FLAG_MATERIALIZE) != 0) {
+    set_err("flags must be 0 or MMSA_FLAG_MATERIALIZE");
     return MMSA_INVALID_ARGUMENT;
   }
   if (D.L >= (1 << 22)) {
@@ -289,6 +290,7 @@ mmsa_status build_layout(const mmsa_layer_desc* desc, Layout& Lo) {
   dm.o_sl = D.o_strides[2];
 
   Lo.empty = (Lo.BH == 0 || D.L == 0);
+  Lo.materialize = (D.flags & MMSA_FLAG_MATERIALIZE) != 0;
   if (Lo.empty) {
     Lo.ws_total = 256;
     return MMSA_OK;
@@ -573,8 +575,8 @@ mmsa_status build_layout(const mmsa_layer_desc* desc, Layout& Lo) {
       ++n_block;
       kv_pool.push_back(H.b * D.Hkv + H.g);
     }
-    if (H.row_kind != ROW_IDENTITY) ++n_perm;
-    if (H.view_kind == VIEW_GROUPED) kv_grp.push_back(H.b * D.Hkv + H.g);
+    if (Lo.materialize && H.row_kind != ROW_IDENTITY) ++n_perm;
+    if (Lo.materialize && H.view_kind == VIEW_GROUPED) kv_grp.push_back(H.b * D.Hkv + H.g);
   }
   std::sort(kv_pool.begin(), kv_pool.end());
   kv_pool.erase(std::unique(kv_pool.begin(), kv_pool.end()), kv_pool.end());
@@ -692,7 +694,7 @@ mmsa_status build_layout(const mmsa_layer_desc* desc, Layout& Lo) {
     }
     for (HeadDev& H : Lo.heads) {
       if (H.row_kind == ROW_GROUPED) H.ws_row_order = dm.ws_pgrp;
-      if (H.row_kind != ROW_IDENTITY) {
+      if (Lo.materialize && H.row_kind != ROW_IDENTITY) {
         H.ws_qperm = bp.take(2ll * H.n_row_slots * dd);
         H.ws_operm = bp.take(2ll * H.n_row_slots * dd);
         Lo.gathers.push_back(GatherTask{H.q_off, dm.q_sl, H.ws_row_order, H.ws_qperm, H.n_row_slots, 0});
@@ -700,7 +702,7 @@ mmsa_status build_layout(const mmsa_layer_desc* desc, Layout& Lo) {
         Lo.max_gather_slots = std::max(Lo.max_gather_slots, H.n_row_slots);
         Lo.max_unperm_slots = std::max(Lo.max_unperm_slots, H.n_row_slots);
       }
-      if (H.view_kind == VIEW_GROUPED) {
+      if (Lo.materialize && H.view_kind == VIEW_GROUPED) {
         const int key = H.b * D.Hkv + H.g;
         const size_t i = std::lower_bound(kv_grp.begin(), kv_grp.end(), key) - kv_grp.begin();
         H.ws_kgrp = kg_off[i];

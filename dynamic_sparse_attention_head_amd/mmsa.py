@@ -38,6 +38,9 @@ class Segment(ctypes.Structure):
                 ("_pad", ctypes.c_int32)]
 
 
+FLAG_MATERIALIZE = 1   # mmsa_layer_desc.flags: explicit gathers and output scatter
+
+
 class LayerDesc(ctypes.Structure):
     _fields_ = [("B", ctypes.c_int32), ("Hq", ctypes.c_int32), ("Hkv", ctypes.c_int32), ("L", ctypes.c_int32),
                 ("d", ctypes.c_int32), ("_pad0", ctypes.c_int32),
@@ -131,10 +134,13 @@ class Layer:
 
     q: [B, Hq, L, d] bf16, k / v: [B, Hkv, L, d] bf16 (any strides with the
     last dimension contiguous).  heads: list of dicts (pattern, layout and
-    budgets per q head); segs: list of (start, len, modality) or None."""
+    budgets per q head); segs: list of (start, len, modality) or None.
+    materialize: copy permuted Q / grouped K,V into the workspace and scatter
+    O back in unpermute (MMSA_FLAG_MATERIALIZE) instead of index-based loads
+    and stores inside the attention call."""
 
     def __init__(self, q, k, v, heads, segs=None, scale=None, kv_head_of=None, o_strides=None,
-                 shape=None, device=None):
+                 shape=None, device=None, materialize=False):
         if q is not None:
             B, Hq, L, d = q.shape
             Hkv = k.shape[1]
@@ -160,7 +166,7 @@ class Layer:
         desc.v_strides[:] = _strides(v, B, Hkv, L, d)
         desc.o_strides[:] = o_strides if o_strides is not None else (Hq * L * d, L * d, d)
         desc.scale = float(scale) if scale is not None else 0.0
-        desc.flags = 0
+        desc.flags = FLAG_MATERIALIZE if materialize else 0
         desc.kv_head_of = self._kvmap
         desc.heads = self._cfg
         desc.segs = self._segs

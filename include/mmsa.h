@@ -46,7 +46,7 @@
 extern "C" {
 #endif
 
-#define MMSA_ABI_VERSION 1
+#define MMSA_ABI_VERSION 2
 #define MMSA_TILE 64       /* query and key tile (the 64-token blocks)      */
 #define MMSA_EST_ROWS 64   /* estimation rows: the last 64 queries          */
 
@@ -74,7 +74,21 @@ enum {
 };
 enum { MMSA_TEXT = 0, MMSA_VIDEO = 1 };
 
-/* mmsa_layer_desc.flags: reserved, must be 0 */
+/* mmsa_layer_desc.flags (MMInference verdict page, key_machinery: the
+ * permutation is realised as index-based loading inside the attention kernel).
+ *  0 (default): index-based.  mmsa_sparse_prefill reads the Q rows of permuted
+ *    heads at their original positions through the row order and the keys of
+ *    the modality-grouped view through the grouped-slot map, and writes every
+ *    output row at its original position; mmsa_permute copies no tensor and
+ *    mmsa_unpermute has nothing left to move.
+ *  MMSA_FLAG_MATERIALIZE: mmsa_permute also copies the permuted Q rows and the
+ *    grouped K/V into the workspace, mmsa_sparse_prefill reads those copies and
+ *    writes the rows of permuted heads to the workspace, and mmsa_unpermute
+ *    scatters them into o.  The results are bit-identical; the workspace is
+ *    larger (2*d bytes per row slot of each permuted head, twice, and 4*d
+ *    bytes per grouped slot of each KV head a 2D-boundary head uses).
+ * Any other bit is an error. */
+#define MMSA_FLAG_MATERIALIZE 1u
 
 typedef struct {
   int32_t pattern;      /* MMSA_ASHAPE / VS / BLOCK / GRID                          */
@@ -102,7 +116,7 @@ typedef struct {
   int32_t _pad0;
   int64_t q_strides[3], k_strides[3], v_strides[3], o_strides[3]; /* elements: batch, head, row */
   float scale;                      /* softmax scale; 0 -> 1/sqrt(d)                 */
-  uint32_t flags;                   /* reserved: 0                                   */
+  uint32_t flags;                   /* 0 or MMSA_FLAG_MATERIALIZE                    */
   const int32_t* kv_head_of;        /* host [Hq] or NULL -> h / (Hq / Hkv)           */
   const mmsa_head_cfg* heads;       /* host [Hq]                                     */
   const mmsa_segment* segs;         /* host [n_segs]; NULL / 0 -> one text segment   */
@@ -168,8 +182,9 @@ mmsa_status mmsa_estimate_blocks(const mmsa_layer_desc* desc, const void* q, con
                                  void* ws, size_t ws_bytes, void* stream);
 
 /* 3. Permutation and plan: row orders (grid: line rows first; boundary:
- *    modality-grouped), gathered copies of permuted Q rows and grouped K/V, and
- *    the per-query-tile list of key tiles and gathered key columns
+ *    modality-grouped), with MMSA_FLAG_MATERIALIZE gathered copies of permuted Q
+ *    rows and grouped K/V, and the per-query-tile list of key tiles and
+ *    gathered key columns
  *    (MMInference verdict page, core_discovery: row-wise, column-wise and 2D
  *    permutations; key_machinery: kernels load only the permuted blocks). */
 mmsa_status mmsa_permute(const mmsa_layer_desc* desc, const void* q, const void* k, const void* v,
@@ -178,19 +193,22 @@ mmsa_status mmsa_permute(const mmsa_layer_desc* desc, const void* q, const void*
 /* 4. Block-sparse causal prefill over the planned tiles (MMInference verdict
  *    page, key_machinery: block-sparse FlashAttention-style kernels that keep
  *    matrix-core compute dense).  q, k, v as above; o: device bf16 [B,Hq,L,d]
- *    with o_strides — rows of heads whose row order is the identity are written
- *    here, the others go to the workspace until mmsa_unpermute.  lse: device
+ *    with o_strides — every row is written here at its original position
+ *    (with MMSA_FLAG_MATERIALIZE only the rows of heads whose row order is the
+ *    identity; the others go to the workspace until mmsa_unpermute).  lse: device
  *    float [B,Hq,L] (contiguous) or NULL; natural-log sum of exp of the scaled
  *    logits over the selected keys, -inf for a row with none. */
 mmsa_status mmsa_sparse_prefill(const mmsa_layer_desc* desc, const void* q, const void* k,
                                 const void* v, void* ws, size_t ws_bytes, void* o, float* lse,
                                 void* stream);
 
-/* 5. Inverse permutation: rows of permuted heads are scattered from the
- *    workspace back to their original positions in o (MMInference verdict page,
- *    core_discovery: the permutation leaves the model unchanged).  After this
- *    call every row of o holds the attention output (0 for a row with no
- *    selected key). */
+/* 5. Inverse permutation (MMInference verdict page, core_discovery: the
+ *    permutation leaves the model unchanged): with MMSA_FLAG_MATERIALIZE the
+ *    rows of permuted heads are scattered from the workspace back to their
+ *    original positions in o; by default mmsa_sparse_prefill already wrote
+ *    them there and this call only validates its arguments.  After this call
+ *    every row of o holds the attention output (0 for a row with no selected
+ *    key). */
 mmsa_status mmsa_unpermute(const mmsa_layer_desc* desc, void* ws, size_t ws_bytes, void* o,
                            void* stream);
 

@@ -24,11 +24,11 @@ def f64(t):
     return t.detach().float().cpu().numpy().astype(np.float64)
 
 
-def run_gpu(spec, device="cuda", q=None, k=None, v=None, lse=True):
+def run_gpu(spec, device="cuda", q=None, k=None, v=None, lse=True, materialize=False):
     if q is None:
         lay = synth.make_layer(spec, device)
         q, k, v = lay["q"], lay["k"], lay["v"]
-    L = mmsa.Layer(q, k, v, spec.heads, segs=spec.segs)
+    L = mmsa.Layer(q, k, v, spec.heads, segs=spec.segs, materialize=materialize)
     o = torch.full((spec_B(q), spec.Hq, spec.L, spec.d), float("nan"), dtype=torch.bfloat16, device=device)
     lse_t = torch.full((spec_B(q), spec.Hq, spec.L), float("nan"), dtype=torch.float32, device=device) if lse else None
     L.forward(q, k, v, o, lse_t)
@@ -171,8 +171,8 @@ def sample_rows(Lq, n_uniform, seed, extra=()):
     return np.array(sorted(rows), np.int64)
 
 
-def full_check(spec, rows_per_head=None, pair_tiles=None, seed=0, lse=True):
-    L, q, k, v, o, lse_t = run_gpu(spec, lse=lse)
+def full_check(spec, rows_per_head=None, pair_tiles=None, seed=0, lse=True, materialize=False):
+    L, q, k, v, o, lse_t = run_gpu(spec, lse=lse, materialize=materialize)
     qn, kn, vn = f64(q[0]), f64(k[0]), f64(v[0])
     on = f64(o[0])
     ln = lse_t[0].cpu().numpy().astype(np.float64) if lse_t is not None else None

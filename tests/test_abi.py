@@ -97,7 +97,7 @@ def last_error():
 @pytest.mark.parametrize("mutate,code,needle", [
     (lambda D: setattr(D, "d", 96), UNSUPPORTED, "head dimension"),
     (lambda D: setattr(D, "L", -1), INVALID, "negative shape"),
-    (lambda D: setattr(D, "flags", 1), INVALID, "flags"),
+    (lambda D: setattr(D, "flags", 2), INVALID, "flags"),
     (lambda D: setattr(D, "L", 1 << 22), UNSUPPORTED, "2^22"),
     (lambda D: setattr(D, "Hkv", 3), INVALID, "multiple"),
     (lambda D: setattr(D, "scale", float("nan")), INVALID, "scale"),
@@ -172,6 +172,19 @@ def test_workspace_sizes_and_views(L):
         assert lay.view_offset("v_scores", 2)[1] == 0         # A-shape has no scores
     with pytest.raises(mmsa.MMSAError):
         small.view_offset("v_scores", 3)                      # head out of range
+
+
+def test_materialize_flag_only_grows_workspace_of_permuted_layers(L):
+    segs = [(0, 500, 0), (500, 1500, 1), (2000, 96, 0)]
+    permuted = [synth.vs(10, 20, layout="boundary_2d"), synth.vs(10, 20, layout="q_boundary"),
+                synth.grid(1, 16, 100, layout="modality_grouped")]
+    plain = [synth.vs(10, 20), synth.block(4), synth.ashape(4, 64)]
+    for heads, grows in ((permuted, True), (plain, False)):
+        a = host_layer(heads, Lq=2096, Hkv=1, segs=segs)
+        b = host_layer(heads, Lq=2096, Hkv=1, segs=segs, materialize=True)
+        assert ws_status(b) == OK
+        na, nb = a.workspace_bytes(), b.workspace_bytes()
+        assert (nb > na) if grows else (nb == na), (na, nb)
 
 
 def _call(name, lay, ws, nbytes, ptr=16 * 1024):

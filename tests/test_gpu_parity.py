@@ -1,5 +1,7 @@
 """GPU parity of the whole path (estimation, permutation, plan, attention,
-inverse permutation) against the CPU oracle, through the C ABI.
+inverse permutation) against the CPU oracle, through the C ABI, with the
+permutation index-based inside the attention call (the default) and
+materialised by explicit gathers and an output scatter.
 
 Sizes are small enough for the oracle to finish in seconds and still span
 several 64-tiles with a ragged tail; every pattern and layout is covered.
@@ -43,11 +45,7 @@ def test_grid_plain_ragged():
 
 
 def test_boundary_layouts():
-    segs, L = synth.interleaved_segments(3, 4, 49, 77)
-    heads = [synth.grid(2, 16, 200, layout="modality_grouped"), synth.vs(20, 40, "q_boundary"),
-             synth.vs(25, 33, "boundary_2d"), synth.vs(15, 80, "plain")]
-    spec = synth.small_spec("boundary", L, 4, 1, 128, heads, seed=9, segs=segs, period=49, period_amp=3.0)
-    full_check(spec)
+    full_check(boundary_spec())
 
 
 def test_boundary_text_first_and_single_modality():
@@ -59,6 +57,41 @@ def test_boundary_text_first_and_single_modality():
     full_check(synth.small_spec("v", 333, 2, 1, 128, [synth.vs(10, 20, "boundary_2d"),
                                                       synth.vs(10, 20, "q_boundary")],
                                 seed=4, segs=[(0, 333, VIDEO)]))
+
+
+def boundary_spec():
+    segs, L = synth.interleaved_segments(3, 4, 49, 77)
+    heads = [synth.grid(2, 16, 200, layout="modality_grouped"), synth.vs(20, 40, "q_boundary"),
+             synth.vs(25, 33, "boundary_2d"), synth.vs(15, 80, "plain")]
+    return synth.small_spec("boundary", L, 4, 1, 128, heads, seed=9, segs=segs, period=49, period_amp=3.0)
+
+
+def test_boundary_layouts_materialized():
+    # explicit gathers of permuted Q and grouped K/V, output scattered by unpermute
+    full_check(boundary_spec(), materialize=True)
+
+
+@pytest.mark.parametrize("which", ["boundary", "grid"])
+def test_index_based_equals_materialized(which):
+    if which == "boundary":
+        spec = boundary_spec()
+    else:
+        frames = 9
+        L = 70 + 196 * frames + 23
+        segs = [(0, 70, TEXT), (70, 196 * frames, VIDEO), (70 + 196 * frames, 23, TEXT)]
+        heads = [synth.grid(1, 16, 400), synth.grid(2, 64, 512, layout="modality_grouped"), synth.vs(30, 60, "boundary_2d")]
+        spec = synth.small_spec("grid", L, 3, 1, 64, heads, seed=5, segs=segs, period=196, period_amp=3.0)
+    _, q, k, v, o_idx, lse_idx = run_gpu(spec)
+    L2, _, _, _, o_mat, lse_mat = run_gpu(spec, q=q, k=k, v=v, materialize=True)
+    # the same values in the same arithmetic order: bit-identical
+    assert torch.equal(o_idx.view(torch.int16), o_mat.view(torch.int16))
+    assert torch.equal(lse_idx.view(torch.int32), lse_mat.view(torch.int32))
+    assert L2.workspace_bytes() > mmsa_layer_bytes(spec, q, k, v)
+
+
+def mmsa_layer_bytes(spec, q, k, v):
+    from dynamic_sparse_attention_head_amd import mmsa
+    return mmsa.Layer(q, k, v, spec.heads, segs=spec.segs).workspace_bytes()
 
 
 @pytest.mark.parametrize("L", [1, 63, 64, 65, 130])
