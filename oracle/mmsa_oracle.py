@@ -500,6 +500,28 @@ def head_attention(hi, qh, kh, vh, scale, rows=None):
 
 
 # ---------------------------------------------------------------------------
+# Attention recall of a mask ([MI] "Approach": the offline search scores each
+# pattern and budget by attention recall at the FLOPs the kernel spends)
+# ---------------------------------------------------------------------------
+def head_recall(hi, qh, kh, scale, rows=None):
+    """Per row: the share of the row's dense causal softmax (keys j <= i) that
+    falls on the keys its mask selects.  Float64, straight from the
+    definition: normalise over all causal keys, then sum over the mask."""
+    rows = np.arange(hi.L) if rows is None else np.asarray(rows)
+    q = np.asarray(qh, np.float64)
+    k = np.asarray(kh, np.float64)
+    out = np.zeros(len(rows), np.float64)
+    cache = {}
+    for n_, i in enumerate(rows):
+        i = int(i)
+        s = scale * (k[:i + 1] @ q[i])
+        p = np.exp(s - s.max())
+        p /= p.sum()
+        out[n_] = p[row_mask(hi, i, cache)[:i + 1]].sum()
+    return out
+
+
+# ---------------------------------------------------------------------------
 # Permuted mode (self-check only): permute rows, plan tiles in the permuted
 # coordinates, attend tile by tile, scatter back.  Shares the definitions of
 # the index sets with the direct mode but not its mask construction.

@@ -1,0 +1,70 @@
+"""Recall of the estimated masks (share of each row's dense causal softmax
+mass on its selected keys), computed on the GPU from the library's own LSEs,
+against the oracle's recall from its definition; and the kernel-aware budget
+search on a small synthetic layer."""
+import math
+
+import numpy as np
+import pytest
+import torch
+
+import oracle.mmsa_oracle as O
+from dynamic_sparse_attention_head_amd import recall, synth
+from parity_util import check_head_indices, f64
+
+pytestmark = pytest.mark.gpu
+
+
+def test_row_recall_matches_oracle_definition():
+    spec = synth.config(1)   # 4K tokens, d = 64: A-shape (64, 512) and vertical-slash (128, 256)
+    lay = synth.make_layer(spec, "cuda")
+    q, k, v = lay["q"], lay["k"], lay["v"]
+    L, rec = recall.row_recall(q, k, v, spec.heads, spec.segs)
+    scale = 1.0 / math.sqrt(spec.d)
+    gmap = O.kv_head_map(spec.Hq, spec.Hkv)
+    rows = np.arange(0, spec.L, 7)
+    for h in range(spec.Hq):
+        qh, kh = f64(q[0, h]), f64(k[0, gmap[h]])
+        hi = check_head_indices(L, h, spec.heads[h], qh, kh, spec.segs, scale)
+        ref = O.head_recall(hi, qh, kh, scale, rows)
+        got = rec[h].cpu().numpy()[rows]
+        err = np.abs(got - ref)
+        assert err.max() <= 5e-3, f"head {h}: recall error {err.max():.3g}"
+        assert err.mean() <= 5e-4, f"head {h}: mean recall error {err.mean():.3g}"
+
+
+def test_all_blocks_have_recall_one():
+    # every causal block through the block path vs the all-causal A-shape plan
+    heads = [synth.block(10 ** 6), synth.vs(5000, 5000)]
+    spec = synth.small_spec("full", 1000, 2, 1, 128, heads, seed=3)
+    lay = synth.make_layer(spec, "cuda")
+    _, rec = recall.row_recall(lay["q"], lay["k"], lay["v"], spec.heads, spec.segs)
+    assert (rec - 1.0).abs().max().item() <= 2e-3
+
+
+def test_budget_search_picks_cheapest_budget_meeting_target():
+    heads = [synth.vs(8, 32), synth.vs(8, 32), synth.block(2), synth.ashape(16, 64)]
+    spec = synth.small_spec("search", 3000, 4, 2, 128, heads, seed=11, rope_base=1e4, strong_cols=16)
+    lay = synth.make_layer(spec, "cuda")
+    q, k, v = lay["q"], lay["k"], lay["v"]
+    cands = (recall.sweep(spec.heads, "vs", [dict(k_vertical=a, k_slash=b) for a, b in ((8, 32), (64, 256), (512, 3000))])
+             + recall.sweep(spec.heads, "block", [dict(k_blocks=kb) for kb in (2, 8, 47)]))
+    target = 0.9
+    chosen, table = recall.budget_search(q, k, v, cands, target=target, segs=spec.segs)
+    for h in range(spec.Hq):
+        stats = [t[h] for t in table]
+        pick = [i for i, c in enumerate(cands) if c[h] == chosen[h]]
+        assert pick, f"head {h}: chosen config is not a candidate"
+        s = stats[pick[0]]
+        ok = [t for t in stats if t["mean_recall"] >= target]
+        if ok:
+            assert s["mean_recall"] >= target
+            assert s["planned_flops"] == min(t["planned_flops"] for t in ok)
+        else:
+            assert s["mean_recall"] == max(t["mean_recall"] for t in stats)
+    # recall and kernel FLOPs both grow with the vertical-slash budget
+    for h in (0, 1):
+        r = [table[i][h]["mean_recall"] for i in range(3)]
+        f = [table[i][h]["planned_flops"] for i in range(3)]
+        assert r[0] <= r[1] + 1e-3 <= r[2] + 2e-3 and f[0] <= f[1] <= f[2]
+        assert r[2] >= 0.999

@@ -435,3 +435,64 @@ def test_vs_tile_mask_loops_2d():
                         keep = True
             ref[j] = keep
         assert (O.row_mask(hi, i) == ref).all()
+
+
+# ---------------------------------------------------------------------------
+# Attention recall of a mask
+# ---------------------------------------------------------------------------
+def test_recall_full_causal_mask_is_one_and_empty_mask_is_zero():
+    L, d = 150, 16
+    q, k, _, _ = small_layer(L, d, [synth.ashape(0, L)], seed=7)
+    scale = 1 / math.sqrt(d)
+    full = O.estimate_head(synth.ashape(0, L), q[0], k[0], None, scale)
+    np.testing.assert_allclose(O.head_recall(full, q[0], k[0], scale), 1.0, atol=1e-12, rtol=0)
+    empty = O.estimate_head(synth.vs(0, 0), q[0], k[0], None, scale)
+    assert (O.head_recall(empty, q[0], k[0], scale) == 0.0).all()
+
+
+def test_recall_matches_torch_softmax_on_causal_logits():
+    L, d = 130, 32
+    q, k, _, _ = small_layer(L, d, [synth.ashape(5, 20)], seed=8)
+    scale = 1 / math.sqrt(d)
+    hi = O.estimate_head(synth.ashape(5, 20), q[0], k[0], None, scale)
+    logits = torch.from_numpy(q[0] @ k[0].T * scale)
+    causal = torch.ones(L, L, dtype=torch.bool).tril()
+    p = torch.softmax(logits.masked_fill(~causal, float("-inf")), dim=-1).numpy()
+    i = np.arange(L)[:, None]
+    j = np.arange(L)[None, :]
+    mask = (j <= i) & ((j < 5) | (i - j < 20))
+    ref = (p * mask).sum(axis=1)
+    np.testing.assert_allclose(O.head_recall(hi, q[0], k[0], scale), ref, atol=1e-12, rtol=0)
+
+
+def test_recall_equals_exp_of_lse_difference():
+    # the identity the GPU side uses: sum over the mask of the dense softmax =
+    # exp(LSE over the mask - LSE over all causal keys)
+    L, d = 260, 16
+    heads = [synth.ashape(3, 40), synth.block(2)]
+    q, k, v, _ = small_layer(L, d, heads, seed=9)
+    scale = 1 / math.sqrt(d)
+    full = O.estimate_head(synth.ashape(0, L), q[0], k[0], None, scale)
+    _, lse_full = O.head_attention(full, q[0], k[0], v[0], scale)
+    for h, cfg in enumerate(heads):
+        hi = O.estimate_head(cfg, q[h], k[h], None, scale)
+        _, lse = O.head_attention(hi, q[h], k[h], v[h], scale)
+        _, lse_full_h = O.head_attention(O.estimate_head(synth.ashape(0, L), q[h], k[h], None, scale),
+                                         q[h], k[h], v[h], scale)
+        np.testing.assert_allclose(O.head_recall(hi, q[h], k[h], scale), np.exp(lse - lse_full_h),
+                                   atol=1e-12, rtol=0)
+    assert np.isfinite(lse_full).all()
+
+
+def test_recall_is_monotone_in_the_budget():
+    L, d = 300, 16
+    q, k, _, _ = small_layer(L, d, [synth.ashape(0, 16)], seed=10)
+    scale = 1 / math.sqrt(d)
+    prev = None
+    for window in (1, 16, 64, 300):
+        hi = O.estimate_head(synth.ashape(0, window), q[0], k[0], None, scale)
+        r = O.head_recall(hi, q[0], k[0], scale)
+        if prev is not None:
+            assert (r >= prev - 1e-15).all()
+        prev = r
+    np.testing.assert_allclose(prev, 1.0, atol=1e-12, rtol=0)
