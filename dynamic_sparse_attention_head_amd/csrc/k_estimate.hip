@@ -87,13 +87,19 @@ __global__ __launch_bounds__(256) void k_est_pass1(Dims dm, Tables tb, char* ws,
   for (int jb = G.job_begin; jb < G.job_end; ++jb, ++it) {
     const EstJob& J = jobs[jb];
     const int par = it & 1;
+    // row positions of the 4 row groups, then Q one group ahead of its MFMAs
+    int posv[4];
+#pragma unroll
+    for (int qb = 0; qb < 4; ++qb) posv[qb] = (16 * qb + qc < J.n_rows) ? J.rows[16 * qb + qc] : -1;
+    bf16x8 qfb[2][D / 32];
+    load_q_frag<D>(qfb[0], q + J.q_off, dm.q_sl, posv[0], lane);
 #pragma unroll
     for (int qb = 0; qb < 4; ++qb) {
       const int row = 16 * qb + qc;
       const bool rv = row < J.n_rows;
-      const int pos = rv ? J.rows[row] : -1;
-      bf16x8 qf[D / 32];
-      load_q_frag<D>(qf, q + J.q_off, dm.q_sl, pos, lane);
+      const int pos = posv[qb];
+      if (qb + 1 < 4) load_q_frag<D>(qfb[(qb + 1) & 1], q + J.q_off, dm.q_sl, posv[qb + 1], lane);
+      const bf16x8 (&qf)[D / 32] = qfb[qb & 1];
       float xs[16];
       float mx = -INFINITY;
 #pragma unroll
@@ -197,15 +203,21 @@ __global__ __launch_bounds__(256) void k_est_pass2(Dims dm, Tables tb, char* ws,
     const EstJob& J = jobs[jb];
     if (J.imax < kmin) continue;   // uniform
     const float2* stats = wsp<const float2>(ws, J.ws_stats);
+    // row positions of the 4 row groups, then Q one group ahead of its MFMAs
+    int posv[4];
+#pragma unroll
+    for (int qb = 0; qb < 4; ++qb) posv[qb] = (16 * qb + qc < J.n_rows) ? J.rows[16 * qb + qc] : -1;
+    bf16x8 qfb[2][D / 32];
+    load_q_frag<D>(qfb[0], q + J.q_off, dm.q_sl, posv[0], lane);
 #pragma unroll
     for (int qb = 0; qb < 4; ++qb) {
       const int row = 16 * qb + qc;
       const bool rv = row < J.n_rows;
-      const int pos = rv ? J.rows[row] : -1;
+      const int pos = posv[qb];
       const float2 st = stats[row];
       const float inv_l = (rv && st.y > 0.f) ? 1.0f / st.y : 0.f;
-      bf16x8 qf[D / 32];
-      load_q_frag<D>(qf, q + J.q_off, dm.q_sl, pos, lane);
+      if (qb + 1 < 4) load_q_frag<D>(qfb[(qb + 1) & 1], q + J.q_off, dm.q_sl, posv[qb + 1], lane);
+      const bf16x8 (&qf)[D / 32] = qfb[qb & 1];
 #pragma unroll
       for (int kb = 0; kb < 4; ++kb) {
         floatx4 acc = {0.f, 0.f, 0.f, 0.f};
@@ -229,8 +241,12 @@ __global__ __launch_bounds__(256) void k_est_pass2(Dims dm, Tables tb, char* ws,
     {
       const int kpos = kp_s[tid];
       if (kpos >= 0 && kpos <= J.imax) {
-        float sum = 0.f;
-        for (int r = 0; r < J.n_rows; ++r) sum += P[r][tid];
+        // rows past n_rows hold zeros (written as invalid above), so a fixed
+        // 64-row sum with independent partials lets the LDS reads overlap
+        float part[8] = {0.f, 0.f, 0.f, 0.f, 0.f, 0.f, 0.f, 0.f};
+#pragma unroll
+        for (int r = 0; r < EST_ROWS; ++r) part[r & 7] += P[r][tid];
+        const float sum = ((part[0] + part[1]) + (part[2] + part[3])) + ((part[4] + part[5]) + (part[6] + part[7]));
         const int slot = x0 + tid;
         if (J.kind == JOB_VS_ORIG || J.kind == JOB_GRID_PLAIN) {
           wsp<float>(ws, J.pair[0].ws_v)[kpos] = sum;
@@ -266,8 +282,16 @@ __global__ __launch_bounds__(256) void k_est_pass2(Dims dm, Tables tb, char* ws,
           const int idx = idx_lo + ii;
           if (idx < 0 || idx >= Pd.Ds) continue;
           const int rlo = max(r0, idx - A), rhi = min(r0 + len, idx - A + EST_CK);
-          float sum = 0.f;
-          for (int r = rlo; r < rhi; ++r) sum += P[r][A + r - idx];
+          // fixed 64-row loop, independent partials: the LDS reads overlap
+          float part[8] = {0.f, 0.f, 0.f, 0.f, 0.f, 0.f, 0.f, 0.f};
+#pragma unroll
+          for (int r = 0; r < EST_ROWS; ++r) {
+            const bool in = (r >= rlo) & (r < rhi);
+            const int c = in ? A + r - idx : 0;
+            const float x = P[r][c];
+            part[r & 7] += in ? x : 0.f;
+          }
+          const float sum = ((part[0] + part[1]) + (part[2] + part[3])) + ((part[4] + part[5]) + (part[6] + part[7]));
           if (sum != 0.f) atomicAdd(&sacc[idx], (unsigned long long)llrint((double)sum * SFIX));
         }
       }
