@@ -315,11 +315,20 @@ __global__ __launch_bounds__(256) void k_s_finalize(Tables tb, char* ws) {
 // ---------------------------------------------------------------------------
 // Exact top-k of a float32 vector over [lo, hi): value descending, ties to
 // the lowest index, output ascending.  Radix select on the 32-bit orderable
-// key (4 rounds of 8 bits), then one compaction pass in index order.
-// grid (tasks), block 1024.
+// key, 8 bits a round from the top, spread over the whole GPU: the vector is
+// cut into slices of TK_SL elements (one workgroup each).
+//   rounds 0-3  each slice's histogram of the next digit among the keys that
+//               match the prefix chosen so far; every workgroup derives that
+//               prefix itself from the earlier rounds' slice histograms
+//   count       keys above / equal to the final threshold, per slice
+//   offsets     one workgroup per vector: output offset and equal keys before
+//               each slice (equal keys are taken lowest index first)
+//   emit        each slice writes its selected indices in index order
+// Scratch per vector (TopkTask::ws_tmp): hist [4][slices][256] u32, counts
+// [slices] (greater, equal), offsets [slices] (output, equal before), state.
 // ---------------------------------------------------------------------------
-// Workgroup-wide exclusive prefix sum of v in thread order (1024 threads);
-// sets *total.  red: 17 ints of LDS.  Two barriers.
+// Workgroup-wide exclusive prefix sum of v in thread order; sets *total.
+// red: 17 ints of LDS.  Two barriers.
 __device__ __forceinline__ int block_excl_sum(int v, int* red, int* total) {
   const int lane = threadIdx.x & 63, wv = threadIdx.x >> 6, nw = blockDim.x >> 6;
   int inc = v;
@@ -341,103 +350,221 @@ __device__ __forceinline__ int block_excl_sum(int v, int* red, int* total) {
   return before + inc - v;
 }
 
-__global__ __launch_bounds__(1024) void k_topk(Tables tb, char* ws) {
-  constexpr int E = 8;   // elements per thread per pass step (index order: thread-major)
-  const TopkTask T = wsp<const TopkTask>(ws, tb.off_topk)[blockIdx.x];
-  const float* __restrict__ x = wsp<const float>(ws, T.ws_x);
-  int32_t* out = wsp<int32_t>(ws, T.ws_out);
-  const int tid = threadIdx.x, nthr = blockDim.x, wv = tid >> 6;
-  const int lo = T.lo, hi = T.hi, n = hi - lo;
-  const int k = min(T.k, n);
-  // one histogram per wave: scores cluster in a few exponent bins, and 16
-  // waves incrementing one shared counter would serialise on it
-  __shared__ uint32_t hist[16][256];
-  __shared__ uint32_t sh_pref, sh_mask, sh_krem;
+constexpr int TK_T = 1024;              // threads per top-k workgroup
+constexpr int TK_E = TK_SL / TK_T;      // elements per thread per slice
+
+struct TkState {
+  uint32_t pref, mask, krem;   // digits fixed so far, their mask, keys still to take at the threshold
+  int mode;                    // 0: select, 1: take all (k >= n), 2: take none (k <= 0)
+};
+
+// Threshold state after `rounds` rounds (identical in every workgroup): the
+// state after rounds-1 (stored by the previous launch; the initial one for a
+// single round) advanced by the slice histograms of round rounds-1, summed
+// by all TK_T threads.  The workgroup of slice 0 stores the result for the
+// next launch.  Needs all TK_T threads (barriers).
+__device__ TkState tk_state(const TopkTask& T, const uint32_t* hist, uint4* stored, int n_sl, int rounds,
+                            int* red, uint32_t* sh) {
+  const int n = T.hi - T.lo;
+  TkState st{0u, 0u, 0u, 0};
+  if (T.k <= 0 || n <= 0) {
+    st.mode = 2;
+    return st;
+  }
+  if (T.k >= n) {
+    st.mode = 1;
+    st.krem = (uint32_t)n;
+    return st;
+  }
+  st.krem = (uint32_t)T.k;
+  if (rounds == 0) return st;
+  const int r = rounds - 1, tid = threadIdx.x;
+  if (r > 0) {
+    const uint4 p = stored[r - 1];
+    st.pref = p.x;
+    st.mask = p.y;
+    st.krem = p.z;
+  }
+  const int shift = 24 - 8 * r;
+  // bin b = t & 255 over slices t>>8, t>>8 + 4, ...; then thread t (< 256)
+  // holds bin 255 - t, so a prefix sum in thread order is a suffix sum over bins
+  __shared__ uint32_t part[4][256];
+  {
+    const int b = tid & 255, g = tid >> 8;
+    uint32_t c0 = 0, c1 = 0;
+    int sl = g;
+    for (; sl + 4 < n_sl; sl += 8) {
+      c0 += hist[((int64_t)r * n_sl + sl) * 256 + b];
+      c1 += hist[((int64_t)r * n_sl + sl + 4) * 256 + b];
+    }
+    if (sl < n_sl) c0 += hist[((int64_t)r * n_sl + sl) * 256 + b];
+    part[g][b] = c0 + c1;
+  }
+  __syncthreads();
+  const uint32_t c = tid < 256 ? part[0][255 - tid] + part[1][255 - tid] + part[2][255 - tid] + part[3][255 - tid] : 0u;
+  int tot;
+  const uint32_t above = (uint32_t)block_excl_sum((int)c, red, &tot);
+  if (tid < 256 && above < st.krem && above + c >= st.krem) {
+    sh[0] = st.pref | ((uint32_t)(255 - tid) << shift);
+    sh[1] = st.krem - above;
+  }
+  __syncthreads();
+  st.pref = sh[0];
+  st.krem = sh[1];
+  st.mask |= 255u << shift;
+  if (blockIdx.x == 0 && tid == 0) stored[r] = make_uint4(st.pref, st.mask, st.krem, 0u);
+  return st;
+}
+
+// Round `round`: this slice's histogram of digit 24 - 8*round among the keys
+// matching the prefix of the earlier rounds.  grid (slices, tasks).
+__global__ __launch_bounds__(TK_T) void k_topk_hist(Tables tb, char* ws, int round) {
+  const TopkTask T = wsp<const TopkTask>(ws, tb.off_topk)[blockIdx.y];
+  const int n = T.hi - T.lo, n_sl = (int)topk_slices(n), sl = blockIdx.x;
+  if (sl >= n_sl) return;
+  uint32_t* hist = wsp<uint32_t>(ws, T.ws_tmp);
+  uint4* stored = reinterpret_cast<uint4*>(hist + 4ll * 256 * n_sl + 4ll * n_sl);
   __shared__ int red[17];
-  if (k <= 0) {
+  __shared__ uint32_t sh[2];
+  __shared__ uint32_t wh[16][256];   // one histogram per wave (keys cluster in few bins)
+  const TkState st = tk_state(T, hist, stored, n_sl, round, red, sh);
+  if (st.mode != 0) return;
+  const int tid = threadIdx.x, wv = tid >> 6, shift = 24 - 8 * round;
+  for (int i = tid; i < 16 * 256; i += TK_T) (&wh[0][0])[i] = 0;
+  __syncthreads();
+  const float* __restrict__ x = wsp<const float>(ws, T.ws_x);
+  const int s0 = T.lo + sl * TK_SL, s1 = min(T.hi, s0 + TK_SL);
+  uint32_t key[TK_E];
+#pragma unroll
+  for (int j = 0; j < TK_E; ++j) {
+    const int i = s0 + j * TK_T + tid;
+    key[j] = i < s1 ? order_key(x[i]) : 0u;
+  }
+#pragma unroll
+  for (int j = 0; j < TK_E; ++j) {
+    const int i = s0 + j * TK_T + tid;
+    if (i < s1 && (key[j] & st.mask) == st.pref) atomicAdd(&wh[wv][(key[j] >> shift) & 255u], 1u);
+  }
+  __syncthreads();
+  if (tid < 256) {
+    uint32_t c = 0;
+#pragma unroll
+    for (int w = 0; w < 16; ++w) c += wh[w][tid];
+    hist[((int64_t)round * n_sl + sl) * 256 + tid] = c;
+  }
+}
+
+// Per slice: keys above and equal to the final threshold.  grid (slices, tasks).
+__global__ __launch_bounds__(TK_T) void k_topk_count(Tables tb, char* ws) {
+  const TopkTask T = wsp<const TopkTask>(ws, tb.off_topk)[blockIdx.y];
+  const int n = T.hi - T.lo, n_sl = (int)topk_slices(n), sl = blockIdx.x;
+  if (sl >= n_sl) return;
+  uint32_t* hist = wsp<uint32_t>(ws, T.ws_tmp);
+  int2* cnt = reinterpret_cast<int2*>(hist + 4ll * 256 * n_sl);
+  uint4* stored = reinterpret_cast<uint4*>(cnt + 2ll * n_sl);
+  __shared__ int red[17];
+  __shared__ uint32_t sh[2];
+  const TkState st = tk_state(T, hist, stored, n_sl, 4, red, sh);
+  const int tid = threadIdx.x;
+  // final threshold for the offsets and emit launches (after the 4 rounds' states)
+  if (sl == 0 && tid == 0) stored[4] = make_uint4(st.pref, st.krem, (uint32_t)st.mode, 0u);
+  const float* __restrict__ x = wsp<const float>(ws, T.ws_x);
+  const int s0 = T.lo + sl * TK_SL, s1 = min(T.hi, s0 + TK_SL);
+  int gt = 0, eq = 0;
+  if (st.mode == 0) {
+#pragma unroll
+    for (int j = 0; j < TK_E; ++j) {
+      const int i = s0 + j * TK_T + tid;
+      if (i < s1) {
+        const uint32_t key = order_key(x[i]);
+        gt += key > st.pref;
+        eq += key == st.pref;
+      }
+    }
+  } else if (st.mode == 1) {
+    gt = max(0, min(TK_E, (s1 - s0 - tid + TK_T - 1) / TK_T));
+  }
+  int tg, te;
+  block_excl_sum(gt, red, &tg);
+  block_excl_sum(eq, red, &te);
+  if (tid == 0) cnt[sl] = make_int2(tg, te);
+}
+
+// Per vector: output offset and equal keys before each slice, and the count.
+// grid (tasks).
+__global__ __launch_bounds__(TK_T) void k_topk_offsets(Tables tb, char* ws) {
+  const TopkTask T = wsp<const TopkTask>(ws, tb.off_topk)[blockIdx.x];
+  const int n = T.hi - T.lo, n_sl = (int)topk_slices(n);
+  const int tid = threadIdx.x;
+  __shared__ int red[17];
+  if (n_sl == 0) {
     if (tid == 0) *wsp<int32_t>(ws, T.ws_cnt) = 0;
     return;
   }
-  uint32_t pref = 0, pmask = 0, krem = (uint32_t)k;
-  if (k < n) {
-    for (int shift = 24; shift >= 0; shift -= 8) {
-      for (int i = tid; i < 16 * 256; i += nthr) (&hist[0][0])[i] = 0;
-      __syncthreads();
-      for (int s0 = lo; s0 < hi; s0 += E * nthr) {
-        uint32_t key[E];
-#pragma unroll
-        for (int j = 0; j < E; ++j) {
-          const int i = s0 + j * nthr + tid;
-          key[j] = i < hi ? order_key(x[i]) : 0u;
-        }
-#pragma unroll
-        for (int j = 0; j < E; ++j) {
-          const int i = s0 + j * nthr + tid;
-          if (i < hi && (key[j] & pmask) == pref) atomicAdd(&hist[wv][(key[j] >> shift) & 255u], 1u);
-        }
-      }
-      __syncthreads();
-      if (tid < 256) {
-        uint32_t c = 0;
-        for (int ww = 0; ww < nthr / 64; ++ww) c += hist[ww][tid];
-        hist[0][tid] = c;
-      }
-      __syncthreads();
-      if (tid == 0) {
-        uint32_t cum = 0;
-        int b = 255;
-        for (; b > 0; --b) {
-          if (cum + hist[0][b] >= krem) break;
-          cum += hist[0][b];
-        }
-        sh_krem = krem - cum;
-        sh_pref = pref | ((uint32_t)b << shift);
-        sh_mask = pmask | (255u << shift);
-      }
-      __syncthreads();
-      pref = sh_pref;
-      pmask = sh_mask;
-      krem = sh_krem;
-      __syncthreads();
-    }
-  } else {
-    pref = 0;
-    krem = (uint32_t)n;
+  uint32_t* hist = wsp<uint32_t>(ws, T.ws_tmp);
+  const int2* cnt = reinterpret_cast<const int2*>(hist + 4ll * 256 * n_sl);
+  int2* off = const_cast<int2*>(cnt) + n_sl;
+  const uint4 fin = reinterpret_cast<const uint4*>(off + n_sl)[4];
+  const int need = (int)fin.y;
+  int out_base = 0, eq_base = 0;
+  for (int c0 = 0; c0 < n_sl; c0 += TK_T) {
+    const int sl = c0 + tid;
+    const int2 c = sl < n_sl ? cnt[sl] : make_int2(0, 0);
+    int te, ts;
+    const int eq_before = eq_base + block_excl_sum(c.y, red, &te);
+    const int take = c.x + max(0, min(c.y, need - eq_before));
+    const int out_off = out_base + block_excl_sum(take, red, &ts);
+    if (sl < n_sl) off[sl] = make_int2(out_off, eq_before);
+    out_base += ts;
+    eq_base += te;
   }
-  // Compaction in index order: thread t owns elements s0 + E*t .. + E-1 of each
-  // E*nthr block; keys above the threshold are taken, equal keys by rank.
-  const uint32_t thr = pref;
-  const int need = (int)krem;
-  int base = 0, eqb = 0;
-  for (int s0 = lo; s0 < hi; s0 += E * nthr) {
-    uint32_t key[E];
-    int n_eq = 0;
+  if (tid == 0) *wsp<int32_t>(ws, T.ws_cnt) = out_base;
+}
+
+// Per slice: the selected indices in index order (thread t owns elements
+// E t .. E t + E-1 of the slice).  grid (slices, tasks).
+__global__ __launch_bounds__(TK_T) void k_topk_emit(Tables tb, char* ws) {
+  const TopkTask T = wsp<const TopkTask>(ws, tb.off_topk)[blockIdx.y];
+  const int n = T.hi - T.lo, n_sl = (int)topk_slices(n), sl = blockIdx.x;
+  if (sl >= n_sl) return;
+  const uint32_t* hist = wsp<const uint32_t>(ws, T.ws_tmp);
+  const int2* cnt = reinterpret_cast<const int2*>(hist + 4ll * 256 * n_sl);
+  const int2* off = cnt + n_sl;
+  const uint4 fin = reinterpret_cast<const uint4*>(off + n_sl)[4];
+  const int mode = (int)fin.z;
+  if (mode == 2) return;
+  const uint32_t thr = fin.x;
+  const int need = (int)fin.y;
+  const int2 o = off[sl];
+  __shared__ int red[17];
+  const float* __restrict__ x = wsp<const float>(ws, T.ws_x);
+  int32_t* out = wsp<int32_t>(ws, T.ws_out);
+  const int tid = threadIdx.x;
+  const int s0 = T.lo + sl * TK_SL, s1 = min(T.hi, s0 + TK_SL);
+  uint32_t key[TK_E];
+  int n_eq = 0;
 #pragma unroll
-    for (int j = 0; j < E; ++j) {
-      const int i = s0 + E * tid + j;
-      key[j] = i < hi ? order_key(x[i]) : 0u;
-      n_eq += (i < hi && key[j] == thr) ? 1 : 0;
-    }
-    int eq_tot, sel_tot;
-    int er = eqb + block_excl_sum(n_eq, red, &eq_tot);
-    uint32_t selm = 0;
-#pragma unroll
-    for (int j = 0; j < E; ++j) {
-      const int i = s0 + E * tid + j;
-      const bool in = i < hi;
-      const bool eq = in && key[j] == thr;
-      const bool sel = (in && key[j] > thr) || (eq && er < need);
-      er += eq ? 1 : 0;
-      selm |= sel ? (1u << j) : 0u;
-    }
-    int r = base + block_excl_sum(__popc(selm), red, &sel_tot);
-#pragma unroll
-    for (int j = 0; j < E; ++j)
-      if (selm & (1u << j)) out[r++] = s0 + E * tid + j;
-    base += sel_tot;
-    eqb += eq_tot;
+  for (int j = 0; j < TK_E; ++j) {
+    const int i = s0 + TK_E * tid + j;
+    key[j] = i < s1 ? order_key(x[i]) : 0u;
+    n_eq += (mode == 0 && i < s1 && key[j] == thr) ? 1 : 0;
   }
-  if (tid == 0) *wsp<int32_t>(ws, T.ws_cnt) = base;
+  int eq_tot, sel_tot;
+  int er = o.y + block_excl_sum(n_eq, red, &eq_tot);
+  uint32_t selm = 0;
+#pragma unroll
+  for (int j = 0; j < TK_E; ++j) {
+    const int i = s0 + TK_E * tid + j;
+    const bool in = i < s1;
+    const bool eq = mode == 0 && in && key[j] == thr;
+    const bool sel = in && (mode == 1 || key[j] > thr || (eq && er < need));
+    er += eq ? 1 : 0;
+    selm |= sel ? (1u << j) : 0u;
+  }
+  int r = o.x + block_excl_sum(__popc(selm), red, &sel_tot);
+#pragma unroll
+  for (int j = 0; j < TK_E; ++j)
+    if (selm & (1u << j)) out[r++] = s0 + TK_E * tid + j;
 }
 
 // ---------------------------------------------------------------------------
@@ -620,9 +747,15 @@ hipError_t launch_est_pass2(const Dims& dm, const Tables& tb, char* ws, const vo
   return hipGetLastError();
 }
 
-hipError_t launch_topk(const Tables& tb, char* ws, hipStream_t s) {
+hipError_t launch_topk(const Tables& tb, char* ws, int max_slices, hipStream_t s) {
   if (tb.n_topk == 0) return hipSuccess;
-  k_topk<<<(unsigned)tb.n_topk, 1024, 0, s>>>(tb, ws);
+  if (max_slices > 0) {
+    const dim3 g((unsigned)max_slices, (unsigned)tb.n_topk);
+    for (int r = 0; r < 4; ++r) k_topk_hist<<<g, TK_T, 0, s>>>(tb, ws, r);
+    k_topk_count<<<g, TK_T, 0, s>>>(tb, ws);
+  }
+  k_topk_offsets<<<(unsigned)tb.n_topk, TK_T, 0, s>>>(tb, ws);
+  if (max_slices > 0) k_topk_emit<<<dim3((unsigned)max_slices, (unsigned)tb.n_topk), TK_T, 0, s>>>(tb, ws);
   return hipGetLastError();
 }
 

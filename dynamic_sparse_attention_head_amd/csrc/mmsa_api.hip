@@ -71,6 +71,7 @@ struct Layout {
   int n_chunks1 = 0, n_chunks2 = 0, max_ds = 0, max_strides = 0, nB = 0, max_tiles = 0, max_bm_words = 0;
   int max_gather_slots = 0, max_unperm_slots = 0;
   int64_t max_items = 0;
+  int64_t max_topk_slices = 0;
   int64_t zero_off = 0, zero_bytes = 0;       // vertical scores and slash accumulators
   int64_t gridrow_off = 0, gridrow_bytes = 0; // grid row orders (filled with -1)
   bool need_seg = false, any_vs_est = false, any_block = false;
@@ -641,8 +642,12 @@ mmsa_status build_layout(const mmsa_layer_desc* desc, Layout& Lo) {
         P.ws_sidx = bp.take(4ll * std::max(P.ks, 1));
         P.ws_nsel = bp.take(8);
         Lo.max_ds = std::max(Lo.max_ds, P.Ds);
-        Lo.topk.push_back(TopkTask{P.ws_v, P.ws_vidx, P.ws_nsel, P.v_lo, P.v_hi, P.kv, 0});
-        Lo.topk.push_back(TopkTask{P.ws_s, P.ws_sidx, P.ws_nsel + 4, P.s_lo, P.s_hi, P.ks, 0});
+        Lo.topk.push_back(TopkTask{P.ws_v, P.ws_vidx, P.ws_nsel, P.v_lo, P.v_hi, P.kv, 0,
+                                   bp.take(topk_tmp_bytes(P.v_hi - P.v_lo))});
+        Lo.topk.push_back(TopkTask{P.ws_s, P.ws_sidx, P.ws_nsel + 4, P.s_lo, P.s_hi, P.ks, 0,
+                                   bp.take(topk_tmp_bytes(P.s_hi - P.s_lo))});
+        Lo.max_topk_slices = std::max<int64_t>(Lo.max_topk_slices, std::max(topk_slices(P.v_hi - P.v_lo),
+                                                                            topk_slices(P.s_hi - P.s_lo)));
       } else {
         P.ws_s = P.ws_vidx = P.ws_sidx = P.ws_nsel = -1;
       }
@@ -927,7 +932,7 @@ mmsa_status mmsa_estimate_vs(const mmsa_layer_desc* desc, const void* q, const v
   MMSA_HIP(launch_est_pass1(Lo.dm, Lo.tb, w, q, k, Lo.n_chunks1, s), "estimation pass 1");
   MMSA_HIP(launch_fill_u32(w + Lo.zero_off, 0u, Lo.zero_bytes / 4, s), "score clear");
   MMSA_HIP(launch_est_pass2(Lo.dm, Lo.tb, w, q, k, Lo.n_chunks2, Lo.max_ds, s), "estimation pass 2");
-  MMSA_HIP(launch_topk(Lo.tb, w, s), "top-k");
+  MMSA_HIP(launch_topk(Lo.tb, w, (int)Lo.max_topk_slices, s), "top-k");
   MMSA_HIP(launch_grid(Lo.dm, Lo.tb, w, Lo.max_strides, s), "grid rule");
   return MMSA_OK;
 }

@@ -91,7 +91,14 @@ struct EstGroup {
 struct TopkTask {
   int64_t ws_x, ws_out, ws_cnt;
   int32_t lo, hi, k, _pad;
+  int64_t ws_tmp;            // slice histograms, counts, offsets and threshold (topk_tmp_bytes)
 };
+constexpr int TK_SL = 16384;   // elements per top-k slice (one workgroup)
+__host__ __device__ inline int64_t topk_slices(int n) { return n > 0 ? (n + TK_SL - 1) / TK_SL : 0; }
+// 4 rounds of 256-bin histograms per slice, (greater, equal) counts and
+// (output offset, equal keys before) per slice, then the threshold state after
+// rounds 1-4 and the final threshold (16 bytes each)
+__host__ __device__ inline int64_t topk_tmp_bytes(int n) { return 16ll * 256 * topk_slices(n) + 16ll * topk_slices(n) + 80; }
 
 struct GridTask {
   int32_t job, bh, D, n_rows;
@@ -168,7 +175,7 @@ hipError_t launch_est_pass1(const Dims& dm, const Tables& tb, char* ws, const vo
                             int n_chunks1, hipStream_t s);
 hipError_t launch_est_pass2(const Dims& dm, const Tables& tb, char* ws, const void* q, const void* k,
                             int n_chunks2, int max_ds, hipStream_t s);
-hipError_t launch_topk(const Tables& tb, char* ws, hipStream_t s);
+hipError_t launch_topk(const Tables& tb, char* ws, int max_slices, hipStream_t s);
 hipError_t launch_grid(const Dims& dm, const Tables& tb, char* ws, int max_strides, hipStream_t s);
 
 hipError_t launch_block_estimate(const Dims& dm, const Tables& tb, char* ws, const void* q, const void* k,
