@@ -205,6 +205,33 @@ __device__ __forceinline__ int count_le(const int32_t* a, int n, int p) {   // e
   return lo;
 }
 
+// Plain vertical-slash heads: a selected diagonal at offset o = 64q + r
+// crosses key tile t - q of a full query tile t (rows 64t .. 64t+63), and tile
+// t - q - 1 too when r > 0.  Bit q of this per-head bitmap says whether some
+// selected diagonal reaches key tile t - q; a full tile's key tiles are then a
+// reversed shift of it (k_plan).  grid (heads), block 256, dynamic LDS =
+// bitmap words.
+__global__ __launch_bounds__(256) void k_vs_shift(Tables tb, char* ws) {
+  const HeadDev& H = wsp<const HeadDev>(ws, tb.off_heads)[blockIdx.x];
+  if (H.ws_shift < 0) return;
+  extern __shared__ uint64_t mb[];
+  const int W = H.bm_words, tid = threadIdx.x;
+  for (int w = tid; w < W; w += 256) mb[w] = 0ull;
+  __syncthreads();
+  const EstJob& J = wsp<const EstJob>(ws, tb.off_jobs)[H.job[0]];
+  const PairDev& Pd = J.pair[0];
+  const int ns = min(max(wsp<const int32_t>(ws, Pd.ws_nsel)[1], 0), Pd.ks);
+  const int32_t* S = wsp<const int32_t>(ws, Pd.ws_sidx);
+  for (int e = tid; e < ns; e += 256) {
+    const int o = max(S[e], 0), q = o >> 6;
+    if (q < 64 * W) bm_set(mb, q);
+    if ((o & 63) && q + 1 < 64 * W) bm_set(mb, q + 1);
+  }
+  __syncthreads();
+  uint64_t* out = wsp<uint64_t>(ws, H.ws_shift);
+  for (int w = tid; w < W; w += 256) out[w] = mb[w];
+}
+
 __global__ __launch_bounds__(256) void k_plan(Dims dm, Tables tb, char* ws) {
   const int bh = blockIdx.y, t = blockIdx.x;
   const HeadDev& H = wsp<const HeadDev>(ws, tb.off_heads)[bh];
@@ -309,7 +336,20 @@ __global__ __launch_bounds__(256) void k_plan(Dims dm, Tables tb, char* ws) {
     }
     __syncthreads();
     const int nruns = sh_nruns;
-    for (int pi = 0; pi < J.n_pairs; ++pi) {
+    // a full tile of a plain head (rows 64t .. 64t+63): its key tiles are the
+    // per-head shift bitmap reversed and shifted by t (no per-diagonal work)
+    const bool shifted = H.ws_shift >= 0 && nrows == 64 && nruns == 1 && sh_run_r0[0] == 64 * t;
+    if (shifted) {
+      const uint64_t* M = wsp<const uint64_t>(ws, H.ws_shift);
+      for (int w = tid; w < W; w += 256) {
+        const int base = t - 64 * w - 63;   // bit b of word w (key tile 64w + b) <- shift bit t - 64w - b
+        const int wi = base >> 6, sh = base & 63;
+        uint64_t X = (wi >= 0 && wi < W) ? M[wi] >> sh : 0ull;
+        if (sh && wi + 1 >= 0 && wi + 1 < W) X |= M[wi + 1] << (64 - sh);
+        bm[w] = __builtin_bitreverse64(X);
+      }
+    }
+    for (int pi = 0; pi < (shifted ? 0 : J.n_pairs); ++pi) {
       const PairDev& Pd = J.pair[pi];
       const int32_t* nsel = wsp<const int32_t>(ws, Pd.ws_nsel);
       const int ns = min(max(nsel[1], 0), Pd.ks);
@@ -478,6 +518,7 @@ __global__ __launch_bounds__(64) void k_queue_reset(Dims dm, char* ws) {
 hipError_t launch_plan(const Dims& dm, const Tables& tb, char* ws, int max_tiles, int max_bm_words,
                        hipStream_t s) {
   if (max_tiles > 0 && tb.n_heads > 0) {
+    k_vs_shift<<<(unsigned)tb.n_heads, 256, (size_t)max_bm_words * 8, s>>>(tb, ws);
     k_plan<<<dim3(max_tiles, (unsigned)tb.n_heads), 256, (size_t)max_bm_words * 8, s>>>(dm, tb, ws);
     k_queue_enum<<<dim3((max_tiles / 2 + 64) / 64, (unsigned)tb.n_heads), 64, 0, s>>>(dm, tb, ws);
     k_queue_reset<<<1, 64, 0, s>>>(dm, ws);

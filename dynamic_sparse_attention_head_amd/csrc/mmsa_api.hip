@@ -718,6 +718,7 @@ mmsa_status build_layout(const mmsa_layer_desc* desc, Layout& Lo) {
   // plans
   for (HeadDev& H : Lo.heads) {
     H.ws_bm = bp.take(8ll * H.nT_rows * H.bm_words);
+    H.ws_shift = (H.pattern == MMSA_VS && H.layout == MMSA_PLAIN) ? bp.take(8ll * H.bm_words) : -1;
     H.ws_info = bp.take(16ll * H.nT_rows);
     H.ws_pairs = bp.take(8ll * H.nT_rows);
     if (H.gcap > 0) H.ws_gather = bp.take(4ll * H.nT_rows * H.gcap);

@@ -53,6 +53,8 @@ struct HeadDev {
   int64_t ws_gather;         // int32 [nT_rows][gcap]
   int64_t ws_blk_idx;        // int32 [nB][k_blocks]
   int64_t ws_qp, ws_kp, ws_z;// BLOCK: pooled Q (fp32 [nB][d]), pooled K of (b,g), logits [nB][nB]
+  int64_t ws_shift;          // plain VS: uint64 [bm_words], bit q = some selected diagonal reaches
+                             // key tile t - q from a full query tile t, else -1
 };
 
 // One score pair of an estimation job: the vectors a region produces for one
