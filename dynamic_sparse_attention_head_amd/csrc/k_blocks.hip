@@ -4,7 +4,7 @@
 // for c <= b, and each query block keeps its top-k key blocks (ties to the
 // lower block index, output ascending).  Ranking uses the pre-softmax logits:
 // a softmax is monotone within a row, so the selected set is the same.
-#include "mmsa_device.h"
+#include "block_scan.h"
 
 namespace mmsa {
 
@@ -61,11 +61,13 @@ __global__ __launch_bounds__(256) void k_block_logits(Dims dm, Tables tb, char* 
   const float* qp = wsp<const float>(ws, T.ws_qp);
   const float* kp = wsp<const float>(ws, T.ws_kp);
   const int tid = threadIdx.x;
-  for (int i = tid; i < 64 * D; i += 256) {
-    const int rr = i / D, cc = i % D;
+  for (int i = tid; i < 64 * D / 4; i += 256) {   // 16 bytes a thread
+    const int rr = i / (D / 4), cc = 4 * (i % (D / 4));
     const int bq = 64 * bt + rr, bk = 64 * ct + rr;
-    Qs[rr][cc] = bq < nB ? qp[(int64_t)bq * D + cc] : 0.f;
-    Ks[rr][cc] = bk < nB ? kp[(int64_t)bk * D + cc] : 0.f;
+    const float4 a = bq < nB ? *reinterpret_cast<const float4*>(qp + (int64_t)bq * D + cc) : make_float4(0.f, 0.f, 0.f, 0.f);
+    const float4 c = bk < nB ? *reinterpret_cast<const float4*>(kp + (int64_t)bk * D + cc) : make_float4(0.f, 0.f, 0.f, 0.f);
+    Qs[rr][cc] = a.x, Qs[rr][cc + 1] = a.y, Qs[rr][cc + 2] = a.z, Qs[rr][cc + 3] = a.w;
+    Ks[rr][cc] = c.x, Ks[rr][cc + 1] = c.y, Ks[rr][cc + 2] = c.z, Ks[rr][cc + 3] = c.w;
   }
   __syncthreads();
   const int ty = tid >> 4, tx = tid & 15;
@@ -98,14 +100,17 @@ __global__ __launch_bounds__(256) void k_block_logits(Dims dm, Tables tb, char* 
 }
 
 // Top-k key blocks of one query block from its LDS-resident logit row.
+// Radix select on the orderable key, 8 bits a round from the top: one
+// histogram per wave (logits cluster in few bins), then the threshold bin by a
+// suffix sum over the bins across the workgroup.
 // grid (query blocks, block heads), block 256, dynamic LDS nB floats.
 __global__ __launch_bounds__(256) void k_block_topk(Tables tb, char* ws, int nB) {
   const BlockTask T = wsp<const BlockTask>(ws, tb.off_block)[blockIdx.y];
   extern __shared__ float zs[];
-  __shared__ uint32_t hist[256];
-  __shared__ uint32_t sh_pref, sh_mask, sh_krem;
-  __shared__ int red[5];
-  const int b = blockIdx.x, tid = threadIdx.x;
+  __shared__ uint32_t hist[4][256];
+  __shared__ uint32_t sh_pref, sh_krem;
+  __shared__ int red[17];
+  const int b = blockIdx.x, tid = threadIdx.x, wv = tid >> 6;
   const int n = b + 1;
   const int k = min(T.kb, n);
   const float* zrow = wsp<const float>(ws, T.ws_z) + (int64_t)b * nB;
@@ -116,28 +121,25 @@ __global__ __launch_bounds__(256) void k_block_topk(Tables tb, char* ws, int nB)
   uint32_t pref = 0, pmask = 0, krem = (uint32_t)k;
   if (k < n) {
     for (int shift = 24; shift >= 0; shift -= 8) {
-      hist[tid] = 0;
+      for (int i = tid; i < 4 * 256; i += 256) (&hist[0][0])[i] = 0;
       __syncthreads();
       for (int i = tid; i < n; i += 256) {
         const uint32_t key = order_key(zs[i]);
-        if ((key & pmask) == pref) atomicAdd(&hist[(key >> shift) & 255u], 1u);
+        if ((key & pmask) == pref) atomicAdd(&hist[wv][(key >> shift) & 255u], 1u);
       }
       __syncthreads();
-      if (tid == 0) {
-        uint32_t cum = 0;
-        int bb = 255;
-        for (; bb > 0; --bb) {
-          if (cum + hist[bb] >= krem) break;
-          cum += hist[bb];
-        }
-        sh_krem = krem - cum;
-        sh_pref = pref | ((uint32_t)bb << shift);
-        sh_mask = pmask | (255u << shift);
+      // thread t holds bin 255 - t: a prefix sum in thread order is a suffix sum over bins
+      const uint32_t c = hist[0][255 - tid] + hist[1][255 - tid] + hist[2][255 - tid] + hist[3][255 - tid];
+      int tot;
+      const uint32_t above = (uint32_t)block_excl_sum((int)c, red, &tot);
+      if (above < krem && above + c >= krem) {
+        sh_pref = pref | ((uint32_t)(255 - tid) << shift);
+        sh_krem = krem - above;
       }
       __syncthreads();
       pref = sh_pref;
-      pmask = sh_mask;
       krem = sh_krem;
+      pmask |= 255u << shift;
       __syncthreads();
     }
   } else {

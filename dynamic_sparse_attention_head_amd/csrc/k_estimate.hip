@@ -14,7 +14,7 @@
 // bf16 MFMA with fp32 accumulation.  Diagonal sums cross workgroups; they are
 // added as 2^-40 fixed-point integers, so the result does not depend on the
 // order in which workgroups finish.
-#include "mmsa_device.h"
+#include "block_scan.h"
 
 namespace mmsa {
 
@@ -327,29 +327,6 @@ __global__ __launch_bounds__(256) void k_s_finalize(Tables tb, char* ws) {
 // Scratch per vector (TopkTask::ws_tmp): hist [4][slices][256] u32, counts
 // [slices] (greater, equal), offsets [slices] (output, equal before), state.
 // ---------------------------------------------------------------------------
-// Workgroup-wide exclusive prefix sum of v in thread order; sets *total.
-// red: 17 ints of LDS.  Two barriers.
-__device__ __forceinline__ int block_excl_sum(int v, int* red, int* total) {
-  const int lane = threadIdx.x & 63, wv = threadIdx.x >> 6, nw = blockDim.x >> 6;
-  int inc = v;
-#pragma unroll
-  for (int m = 1; m < 64; m <<= 1) {
-    const int o = __shfl_up(inc, m, 64);
-    if (lane >= m) inc += o;
-  }
-  if (lane == 63) red[wv] = inc;
-  __syncthreads();
-  int before = 0, tot = 0;
-  for (int i = 0; i < nw; ++i) {
-    const int c = red[i];
-    before += (i < wv) ? c : 0;
-    tot += c;
-  }
-  __syncthreads();
-  *total = tot;
-  return before + inc - v;
-}
-
 constexpr int TK_T = 1024;              // threads per top-k workgroup
 constexpr int TK_E = TK_SL / TK_T;      // elements per thread per slice
 
