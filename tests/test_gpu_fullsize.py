@@ -111,3 +111,22 @@ def test_video_grid_314k():
 @pytest.mark.timeout(600)
 def test_mixed_1m():
     run_config(5, n_uniform=6, n_tiles=1)
+
+
+@pytest.mark.timeout(600)
+def test_mixed_1m_materialized_equals_index_based():
+    # every permuted form (grid lines first, Q-boundary rows, 2D-boundary rows
+    # and key view) at 1M tokens: the explicit gathers and output scatter give
+    # the same bits as the index-based loads and stores
+    spec = synth.config(5)
+    t0 = time.time()
+    _, q, k, v, o_idx, lse_idx = run_gpu(spec)
+    o_idx = o_idx.view(torch.int16).clone()
+    lse_idx = lse_idx.view(torch.int32).clone()
+    torch.cuda.empty_cache()
+    _, _, _, _, o_mat, lse_mat = run_gpu(spec, q=q, k=k, v=v, materialize=True)
+    say(f"{spec.name}: both permutation forms in {time.time() - t0:.1f} s")
+    assert torch.equal(o_idx, o_mat.view(torch.int16))
+    assert torch.equal(lse_idx, lse_mat.view(torch.int32))
+    del q, k, v, o_idx, o_mat, lse_idx, lse_mat
+    torch.cuda.empty_cache()
