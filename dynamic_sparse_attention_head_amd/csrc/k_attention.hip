@@ -88,6 +88,19 @@ __device__ __forceinline__ float sum_xor32(float x) {
   const auto r = __builtin_amdgcn_permlane32_swap(__float_as_uint(x), __float_as_uint(x), false, false);
   return __uint_as_float(r[0]) + __uint_as_float(r[1]);
 }
+// Max over the 64 lanes in registers, no LDS round trip: DPP within each row
+// of 16 (quad swaps, then the half-row and row mirrors), then the row swaps of
+// v_permlane16_swap and v_permlane32_swap.  Every lane receives the result.
+__device__ __forceinline__ int wave_max_i32(int x) {
+  x = max(x, __builtin_amdgcn_update_dpp(x, x, 0xB1, 0xF, 0xF, false));    // lane ^ 1
+  x = max(x, __builtin_amdgcn_update_dpp(x, x, 0x4E, 0xF, 0xF, false));    // lane ^ 2
+  x = max(x, __builtin_amdgcn_update_dpp(x, x, 0x141, 0xF, 0xF, false));   // 7 - lane within 8
+  x = max(x, __builtin_amdgcn_update_dpp(x, x, 0x140, 0xF, 0xF, false));   // 15 - lane within 16
+  const auto r = __builtin_amdgcn_permlane16_swap((unsigned)x, (unsigned)x, false, false);
+  x = max((int)r[0], (int)r[1]);
+  const auto r2 = __builtin_amdgcn_permlane32_swap((unsigned)x, (unsigned)x, false, false);
+  return max((int)r2[0], (int)r2[1]);
+}
 
 constexpr uint32_t OOB = 0x80000000u;   // a buffer offset past every tensor slice
 constexpr float LAZY_LOG2 = 8.0f;       // stale-max slack of the online softmax (log2 units)
@@ -267,9 +280,7 @@ __device__ __forceinline__ void attn_pair(AttnSmem<D>& sm, const Dims& dm, const
   auto store_kp = [&](int kpr, bool valid, int par) {
     const int kpos = (valid & (kpr >= 0)) ? kpr : KPOS_NONE;
     sm.kp[par][lane] = kpos;
-    int mx = kpos;
-#pragma unroll
-    for (int m = 1; m < 64; m <<= 1) mx = max(mx, __shfl_xor(mx, m, 64));
+    const int mx = wave_max_i32(kpos);
     if (lane == 0) sm.kmax[par] = mx;
   };
 
@@ -521,8 +532,17 @@ __device__ __forceinline__ void attn_pair(AttnSmem<D>& sm, const Dims& dm, const
     if (doP) {
       const float m_use = soft_a(scur, n & 3);
       uint32_t pk[16];
-      if (doS) s_and_soft(snxt, par ^ 1, scur, m_use, pk);
-      else soft_b(scur, m_use, pk);
+      // The two branches compute the same probabilities; each takes the max
+      // through its own (different) empty asm, so the compiler cannot hoist
+      // them above the branch and out of the interleave with the MFMAs.
+      float mu = m_use;
+      if (doS) {
+        asm volatile("; interleaved" : "+v"(mu));
+        s_and_soft(snxt, par ^ 1, scur, mu, pk);
+      } else {
+        asm volatile("; plain" : "+v"(mu));
+        soft_b(scur, mu, pk);
+      }
       pv_chunk(pk, par);
     } else if (doS) {
       s_chunk(snxt, par ^ 1);
