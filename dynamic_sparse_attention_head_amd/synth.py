@@ -170,6 +170,12 @@ def grid(w=1, lo=64, hi=512, clip=8, layout='plain'):
     return dict(pattern='grid', layout=layout, grid_phases=w, stride_lo=lo, stride_hi=hi, grid_clip=clip)
 
 
+def parallel(sink, block, question):
+    """Parallel-encoding head: sink block, context blocks and question block
+    lengths in tokens."""
+    return dict(pattern='parallel', layout='plain', sink=sink, window=block, question=question)
+
+
 def interleaved_segments(n_chunks, frames, per_frame, text_len, lead_text=0):
     """[T0?][V0][T][V1]...[T][V_{n-1}] with `text_len` text between chunks."""
     segs, pos = [], 0

@@ -24,6 +24,10 @@ reading of their prose):
         column-wise permutation aligning key strides, 2D permutation isolating
         each modality pair; index estimated from the last 64 queries of each
         modality segment).
+  [PE]  the PEVLM verdict page (arXiv 2506.19651), field key_machinery: the
+        parallel-encoding mask (a sink block, frame-aligned context blocks that
+        each see themselves and the sink, a question block that sees
+        everything) and its operation count over those blocks.
 
 Precision: attention and estimation are computed in float64; the estimation
 scores are rounded to float32 before any selection, because the selection
@@ -55,7 +59,7 @@ Q24 = 1 << 24      # grid rule fixed-point quantum 2^-24
 # ---------------------------------------------------------------------------
 @dataclass
 class HeadCfg:
-    pattern: str                 # 'ashape' | 'vs' | 'block' | 'grid'
+    pattern: str                 # 'ashape' | 'vs' | 'block' | 'grid' | 'parallel'
     layout: str = 'plain'        # 'plain' | 'q_boundary' | 'boundary_2d' | 'modality_grouped'
     sink: int = 0
     window: int = 1
@@ -66,6 +70,7 @@ class HeadCfg:
     stride_lo: int = 64
     stride_hi: int = 512
     grid_clip: int = 8
+    question: int = 0            # parallel: length of the trailing question block
 
     @staticmethod
     def of(d) -> "HeadCfg":
@@ -325,7 +330,7 @@ def estimate_head(cfg, qh, kh, segs, scale, scores_override=None):
     segs = _segments(L, segs)
     hi = HeadIndex(cfg=cfg, L=L, segs=segs)
     ov = scores_override or {}
-    if cfg.pattern == 'ashape' or L == 0:
+    if cfg.pattern in ('ashape', 'parallel') or L == 0:
         return hi
     if cfg.pattern == 'block':
         qp, kp = pool_blocks(qh), pool_blocks(kh)
@@ -409,6 +414,21 @@ def _slash_tiles_original(rows, S):
     return np.unique(diff[diff >= 0] // TILE)
 
 
+def parallel_floor(cfg, L, i):
+    """[PE] key_machinery, the parallel-encoding mask.  Tokens [0, S) form the
+    sink block (S = cfg.sink), the last Q tokens the question block
+    (Q = cfg.question), and the tokens between them are cut into context
+    blocks of B = cfg.window tokens from S on (the last one may be shorter).
+    A context row sees the sink block and its own block; sink and question
+    rows see every earlier token.  Returns the first non-sink key row i may
+    see: the start of its context block, or 0 for sink and question rows."""
+    S, B = cfg.sink, cfg.window
+    qs = L - min(cfg.question, L)
+    if i < S or i >= qs:
+        return 0
+    return S + ((i - S) // B) * B
+
+
 def row_mask(hi, i, cache=None):
     """Boolean mask over keys 0..L-1 of the keys selected for query row i."""
     cfg, L = hi.cfg, hi.L
@@ -416,6 +436,8 @@ def row_mask(hi, i, cache=None):
     causal = j <= i
     if cfg.pattern == 'ashape':
         return causal & ((j < cfg.sink) | (i - j < cfg.window))
+    if cfg.pattern == 'parallel':
+        return causal & ((j < cfg.sink) | (j >= parallel_floor(cfg, L, i)))
     if cfg.pattern == 'block':
         sel = np.zeros(-(-L // TILE), bool)
         sel[hi.blocks[i // TILE]] = True
@@ -560,6 +582,13 @@ def tile_plan(hi, tile_rows):
         lo = max(0, int(tile_rows.min()) - cfg.window + 1) // TILE
         ts = sorted(set(range(min(-(-cfg.sink // TILE), t + 1))) | set(range(lo, t + 1)))
         return tiles_orig(ts), []
+    if cfg.pattern == 'parallel':
+        # the sink tiles, and every tile from the lowest first-visible key of
+        # the tile's rows up to its last row
+        t = pmax // TILE
+        lo = min(parallel_floor(cfg, L, int(r)) for r in tile_rows) // TILE
+        ts = sorted(set(range(min(-(-cfg.sink // TILE), t + 1))) | set(range(lo, t + 1)))
+        return tiles_orig(ts), []
     if cfg.pattern == 'block':
         return tiles_orig(hi.blocks[pmax // TILE]), []
     if cfg.pattern == 'grid':
@@ -614,6 +643,8 @@ def permuted_attention(hi, qh, kh, vh, scale):
             kk = keys[keys <= i]
             if cfg.pattern == 'ashape':
                 kk = kk[(kk < cfg.sink) | (i - kk < cfg.window)]
+            if cfg.pattern == 'parallel':
+                kk = kk[(kk < cfg.sink) | (kk >= parallel_floor(cfg, L, int(i)))]
             if kk.size == 0:
                 continue
             s = scale * (np.asarray(kh, np.float64)[kk] @ np.asarray(qh, np.float64)[i])

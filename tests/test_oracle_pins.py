@@ -342,6 +342,11 @@ def test_permuted_equals_direct_ashape_block():
     _check_perm(synth.block(2), 333, 16, seed=1)
 
 
+def test_permuted_equals_direct_parallel():
+    _check_perm(synth.parallel(70, 90, 40), 333, 16, seed=1)     # partial last context block
+    _check_perm(synth.parallel(0, 64, 0), 320, 16, seed=2)       # tile-aligned, no sink or question
+
+
 def test_single_modality_boundary_reduces_to_vs():
     L, d = 390, 16
     q, k, v, _ = small_layer(L, d, [synth.vs(10, 12)], seed=9)
@@ -496,3 +501,71 @@ def test_recall_is_monotone_in_the_budget():
             assert (r >= prev - 1e-15).all()
         prev = r
     np.testing.assert_allclose(prev, 1.0, atol=1e-12, rtol=0)
+
+
+# ---------------------------------------------------------------------------
+# Parallel-encoding mask (PEVLM verdict page, key_machinery)
+# ---------------------------------------------------------------------------
+def _parallel_head(L, cfg):
+    z = np.zeros((L, 4))
+    return O.estimate_head(cfg, z, z, None, 1.0)
+
+
+def page_block_count(S, B, N, Q):
+    """The page's operation count (per unit of its factor 2H), taken over
+    whole blocks: sink S^2, question Q^2 + QS + N QB, context N B^2 + N SB."""
+    return S * S + Q * Q + N * B * B + Q * S + N * Q * B + N * S * B
+
+
+@pytest.mark.parametrize("S,B,N,Q", [(64, 48, 5, 30), (0, 37, 4, 0), (100, 64, 3, 64), (7, 1, 9, 5),
+                                     (50, 20, 0, 40), (0, 90, 1, 0), (196, 392, 6, 128)])
+def test_parallel_pairs_are_the_pages_block_count_made_causal(S, B, N, Q):
+    # A causal prefill keeps j <= i, so each diagonal block (the sink, every
+    # context block, the question) loses its strict upper triangle.
+    L = S + N * B + Q
+    hi = _parallel_head(L, synth.parallel(S, B, Q))
+    upper = S * (S - 1) // 2 + N * (B * (B - 1) // 2) + Q * (Q - 1) // 2
+    assert O.pair_count(hi) == page_block_count(S, B, N, Q) - upper
+
+
+def loop_parallel_mask(L, S, B, Q):
+    """The mask built from block membership lists, by loops."""
+    m = np.zeros((L, L), bool)
+    qs = L - min(Q, L)
+    for i in range(L):
+        if i < S or i >= qs:             # sink and question rows: every earlier token
+            for j in range(i + 1):
+                m[i, j] = True
+    start = S
+    while start < qs:                    # context blocks of B rows from S on
+        members = list(range(start, min(start + B, qs)))
+        for i in members:
+            for j in range(min(S, i + 1)):
+                m[i, j] = True
+            for j in members:
+                if j <= i:
+                    m[i, j] = True
+        start += B
+    return m
+
+
+@pytest.mark.parametrize("L,S,B,Q", [(333, 70, 90, 40), (200, 0, 17, 0), (150, 200, 30, 10), (129, 5, 1, 129),
+                                     (260, 64, 64, 64), (90, 0, 1000, 0), (1, 0, 1, 0)])
+def test_parallel_mask_matches_loops(L, S, B, Q):
+    hi = _parallel_head(L, synth.parallel(S, B, Q))
+    ref = loop_parallel_mask(L, S, B, Q)
+    for i in range(L):
+        np.testing.assert_array_equal(O.row_mask(hi, i), ref[i], err_msg=f"row {i}")
+
+
+def test_parallel_single_block_and_all_question_are_dense():
+    L, d = 211, 16
+    q, k, v, _ = small_layer(L, d, [synth.parallel(0, L, 0)], seed=6)
+    scale = 1 / math.sqrt(d)
+    ref = torch.nn.functional.scaled_dot_product_attention(
+        torch.from_numpy(q[0])[None], torch.from_numpy(k[0])[None], torch.from_numpy(v[0])[None],
+        is_causal=True, scale=scale)[0].numpy()
+    for cfg in (synth.parallel(0, L, 0), synth.parallel(30, 5, L), synth.parallel(L, 3, 0)):
+        hi = O.estimate_head(cfg, q[0], k[0], None, scale)
+        got, _ = O.head_attention(hi, q[0], k[0], v[0], scale)
+        np.testing.assert_allclose(got, ref, atol=1e-10, rtol=0)
