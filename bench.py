@@ -15,6 +15,7 @@ CPU oracle timed on a bounded sample of the same layer.
 from __future__ import annotations
 
 import argparse
+import collections
 import hashlib
 import json
 import math
@@ -248,7 +249,8 @@ def main():
                                f"heads, d={spec.d}", "batch": 1, "seq_len": spec.L,
                    "permutation": "materialised" if args.materialize else "index-based",
                    "heads": "16 vertical-slash (1000/4096), 8 block (top-100), 8 A-shape (128, 4096)"
-                   if args.config == 2 else str([h["pattern"] for h in spec.heads])},
+                   if args.config == 2 else ", ".join(f"{n} {p}" for p, n in collections.Counter(
+                       f"{h['pattern']}/{h.get('layout', 'plain')}" for h in spec.heads).items())},
         "roofline": {"bound": "mfma", "achieved": round(achieved, 2), "peak": PEAK_BF16_TFLOPS,
                      "unit": "TFLOP/s", "frac": round(achieved / PEAK_BF16_TFLOPS, 4),
                      "traffic": read_traffic(spec.name),

@@ -22,8 +22,9 @@
 // and P.V run, S^T of chunk n+1 is computed (its MFMAs interleaved with the
 // softmax arithmetic), and the copies of K for chunk n+2 and V for chunk n+1
 // are in flight.  Masking is element-wise on original positions (causal,
-// A-shape window) and runs only for chunks whose keys may follow the wave's
-// first row.  The running max moves only when a row's max grows by more than
+// A-shape window, parallel-encoding blocks) and runs only for chunks whose
+// keys may follow the wave's first row, and for every chunk of those two
+// row-dependent patterns.  The running max moves only when a row's max grows by more than
 // 2^LAZY, so rescales of O are rare.
 #include "mmsa_device.h"
 
@@ -41,11 +42,12 @@ __device__ __forceinline__ floatx16 mfma32(bf16x8 a, bf16x8 b, floatx16 c) {
 }
 
 template <int D>
-struct AttnSmem {   // 2 stages of K and V (row-major, swizzled); key positions and their max, 4 slots
+struct AttnSmem {   // 2 stages of K and V (row-major, swizzled); key positions, their max and min, 4 slots
   bf16_t K[2][64 * D];
   bf16_t V[2][64 * D];
   int kp[4][64];
   int kmax[4];
+  int kmin[4];
 };
 
 // Swizzle of the 16-byte chunks of row r: physical chunk = logical ^ swz(r).
@@ -198,8 +200,20 @@ __device__ __forceinline__ void attn_pair(AttnSmem<D>& sm, const Dims& dm, const
   // through the grouped-slot map, like gathered columns
   const bool grouped_idx = grouped_view && H.ws_kgrp < 0;
   const int32_t* pgrp = wsp<const int32_t>(ws, dm.ws_pgrp);
-  const bool ashape = H.pattern == MMSA_ASHAPE;
-  const int sink = H.sink, window = H.window;
+  // A key j of row i is kept when j <= i and (j < sink or j >= klo(i)).
+  // A-shape: klo = i - window + 1; parallel encoding: the start of the row's
+  // context block, 0 for its sink and question rows; other patterns: no bound
+  // (INT_MIN).  Both are taken once here, through empty asm, so the chunk
+  // loop neither recomputes them nor branches on the pattern per element.
+  const bool ashape = H.pattern == MMSA_ASHAPE, parallel = H.pattern == MMSA_PARALLEL;
+  int windowed = uniform((ashape || parallel) ? 1 : 0);
+  asm volatile("" : "+s"(windowed));
+  const int sink = H.sink;
+  int klo = ashape ? qpos - H.window + 1 : parallel ? par_floor(H.sink, H.window, H.qstart, qpos) : INT_MIN;
+  asm volatile("" : "+v"(klo));
+  // the largest klo of the wave's rows: a chunk whose keys all lie at or past
+  // it (and before the first row) needs no mask
+  const int wave_klomax = uniform(wave_max_i32(qpos >= 0 ? klo : INT_MIN));
 
   // buffer views: the head's key view (tiles) and its original K/V (gathered columns)
   const bool grouped_copy = grouped_view && !grouped_idx;
@@ -282,6 +296,10 @@ __device__ __forceinline__ void attn_pair(AttnSmem<D>& sm, const Dims& dm, const
     sm.kp[par][lane] = kpos;
     const int mx = wave_max_i32(kpos);
     if (lane == 0) sm.kmax[par] = mx;
+    if (windowed) {
+      const int mn = -wave_max_i32(-kpos);   // positions are >= 0 (KPOS_NONE is the largest int)
+      if (lane == 0) sm.kmin[par] = mn;
+    }
   };
 
   // Chunk sequence (uniform across the workgroup): the union of both tiles'
@@ -392,7 +410,9 @@ __device__ __forceinline__ void attn_pair(AttnSmem<D>& sm, const Dims& dm, const
   // mask and running-max update of one chunk's logits (the part of the softmax
   // that may branch); returns the max to subtract
   auto soft_a = [&](floatx16 (&sa)[2], int ks) -> float {
-    const bool full = !ashape && uniform(sm.kmax[ks]) <= wave_qmin;
+    const int kmx = uniform(sm.kmax[ks]);
+    bool full = kmx <= wave_qmin;
+    if (windowed) full = full && (kmx < sink || uniform(sm.kmin[ks]) >= wave_klomax);
     if (!full) {
       // one lane-dependent base, constant offsets per (kb, i)
       const char* kpb = reinterpret_cast<const char*>(sm.kp[0]) + ks * 256 + 16 * hh;
@@ -404,8 +424,7 @@ __device__ __forceinline__ void attn_pair(AttnSmem<D>& sm, const Dims& dm, const
           const int kpv[4] = {kk.x, kk.y, kk.z, kk.w};
 #pragma unroll
           for (int j = 0; j < 4; ++j) {
-            bool ok = kpv[j] <= qpos;
-            if (ashape) ok = ok & ((kpv[j] < sink) | (qpos - kpv[j] < window));
+            const bool ok = (kpv[j] <= qpos) & ((kpv[j] < sink) | (kpv[j] >= klo));
             sa[kb][4 * i + j] = ok ? sa[kb][4 * i + j] : -INFINITY;
           }
         }

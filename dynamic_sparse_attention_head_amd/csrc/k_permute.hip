@@ -295,6 +295,20 @@ __global__ __launch_bounds__(256) void k_plan(Dims dm, Tables tb, char* ws) {
     const int ns = min((H.sink + 63) / 64, tmax + 1);
     bm_set_range(bm, 0, ns - 1);
     bm_set_range(bm, max(0, qmin - H.window + 1) >> 6, tmax);
+  } else if (H.pattern == MMSA_PARALLEL) {
+    // the sink tiles, then every tile from the lowest first-visible key of the
+    // tile's context and question rows up to its last row (sink rows need
+    // only sink tiles)
+    const int tmax = qmax >> 6;
+    const int ns = min((H.sink + 63) / 64, tmax + 1);
+    bm_set_range(bm, 0, ns - 1);
+    if (wv == 0) {
+      int lo = pos >= H.sink ? par_floor(H.sink, H.window, H.qstart, pos) : 0x7fffffff;
+      for (int m = 1; m < 64; m <<= 1) lo = min(lo, __shfl_xor(lo, m, 64));
+      if (lane == 0) red[3] = lo;
+    }
+    __syncthreads();
+    if (red[3] != 0x7fffffff) bm_set_range(bm, red[3] >> 6, tmax);
   } else if (H.pattern == MMSA_BLOCK) {
     const int32_t* ci = wsp<const int32_t>(ws, H.ws_blk_idx) + (int64_t)t * H.k_blocks;
     for (int i = tid; i < H.k_blocks; i += 256) {
@@ -422,6 +436,10 @@ __global__ __launch_bounds__(256) void k_plan(Dims dm, Tables tb, char* ws) {
     const int p = pos;
     if (H.pattern == MMSA_ASHAPE) {
       my_pairs = min(p + 1, H.window) + max(0, min(H.sink, p + 1 - H.window));
+    } else if (H.pattern == MMSA_PARALLEL) {
+      // a context row: the sink block and its own block up to itself
+      const bool ctx = p >= H.sink && p < H.qstart;
+      my_pairs = ctx ? (long long)H.sink + (p - par_floor(H.sink, H.window, H.qstart, p) + 1) : (long long)(p + 1);
     } else if (H.pattern == MMSA_GRID) {
       my_pairs = grid_is_line ? (p + 1) : count_le(grid_lines, grid_nline, p);
     } else if (H.view_kind == VIEW_IDENTITY) {

@@ -119,6 +119,7 @@ void set_runs(EstJob& J) {
 bool valid_combo(int pattern, int layout) {
   switch (pattern) {
     case MMSA_ASHAPE:
+    case MMSA_PARALLEL:
     case MMSA_BLOCK: return layout == MMSA_PLAIN;
     case MMSA_VS: return layout == MMSA_PLAIN || layout == MMSA_Q_BOUNDARY || layout == MMSA_BOUNDARY_2D;
     case MMSA_GRID: return layout == MMSA_PLAIN || layout == MMSA_MODALITY_GROUPED;
@@ -209,6 +210,10 @@ mmsa_status build_layout(const mmsa_layer_desc* desc, Layout& Lo) {
     }
     if (c.pattern == MMSA_ASHAPE && (c.sink < 0 || c.window < 1)) {
       set_err("head %d: A-shape needs sink >= 0 and window >= 1", h);
+      return MMSA_INVALID_ARGUMENT;
+    }
+    if (c.pattern == MMSA_PARALLEL && (c.sink < 0 || c.window < 1 || c.question < 0)) {
+      set_err("head %d: parallel encoding needs sink >= 0, window >= 1 and question >= 0", h);
       return MMSA_INVALID_ARGUMENT;
     }
     if (c.pattern == MMSA_VS && (c.k_vertical < 0 || c.k_slash < 0)) {
@@ -315,6 +320,7 @@ mmsa_status build_layout(const mmsa_layer_desc* desc, Layout& Lo) {
       H.layout = c.layout;
       H.sink = c.sink;
       H.window = c.window;
+      H.qstart = L - std::min(c.question, L);
       H.k_blocks = std::min(c.k_blocks, Lo.nB);
       H.grid_task = -1;
       H.job[0] = H.job[1] = -1;

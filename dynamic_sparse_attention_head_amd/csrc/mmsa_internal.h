@@ -30,9 +30,19 @@ struct SegDev {
 
 // Per (batch, q head): everything a kernel needs to find this head's data.
 // Offsets named ws_* are byte offsets into the workspace (-1: absent).
+// Parallel-encoding mask (PEVLM verdict page, key_machinery): the first key
+// past the sink block that row i sees -- the start of its context block, whose
+// blocks of `window` tokens start at `sink`; 0 for sink rows and for question
+// rows (from `qstart` on), which see every earlier token.
+__host__ __device__ inline int par_floor(int sink, int window, int qstart, int i) {
+  if (i < sink || i >= qstart) return 0;
+  return sink + ((i - sink) / window) * window;
+}
+
 struct HeadDev {
   int32_t b, h, g, pattern, layout;
   int32_t sink, window, k_blocks;
+  int32_t qstart;            // PARALLEL: first row of the question block
   int32_t row_kind, view_kind;
   int32_t n_row_slots;       // slots of the row order (a multiple of 64)
   int32_t nT_rows;           // query tiles = n_row_slots / 64

@@ -17,7 +17,7 @@ LIB_PATH = os.path.join(_HERE, "libmmsa.so")
 
 TILE = 64
 OK, INVALID_ARGUMENT, UNSUPPORTED, WORKSPACE_TOO_SMALL, HIP_ERROR = range(5)
-PATTERNS = {"ashape": 0, "vs": 1, "block": 2, "grid": 3}
+PATTERNS = {"ashape": 0, "vs": 1, "block": 2, "grid": 3, "parallel": 4}
 LAYOUTS = {"plain": 0, "q_boundary": 1, "boundary_2d": 2, "modality_grouped": 3}
 BUF = dict(v_scores=0, s_scores=1, v_index=2, s_index=3, nsel=4, grid=5, block_index=6, block_scores=7,
            row_order=8, tile_pairs=9, tile_info=10, est_stats=11, tile_bitmap=12)
@@ -30,7 +30,7 @@ BUF_DTYPE = dict(v_scores=torch.float32, s_scores=torch.float32, v_index=torch.i
 class HeadCfg(ctypes.Structure):
     _fields_ = [(n, ctypes.c_int32) for n in (
         "pattern", "layout", "sink", "window", "k_vertical", "k_slash", "k_blocks",
-        "grid_phases", "stride_lo", "stride_hi", "grid_clip")]
+        "grid_phases", "stride_lo", "stride_hi", "grid_clip", "question")]
 
 
 class Segment(ctypes.Structure):
@@ -118,6 +118,7 @@ def head_cfg(d):
     c.stride_lo = int(d.get("stride_lo", 64))
     c.stride_hi = int(d.get("stride_hi", 512))
     c.grid_clip = int(d.get("grid_clip", 8))
+    c.question = int(d.get("question", 0))
     return c
 
 

@@ -193,7 +193,7 @@ def interleaved_segments(n_chunks, frames, per_frame, text_len, lead_text=0):
 
 
 def config(i, L=None, seed=None):
-    """The five named workloads (1-based), optionally shortened to L tokens
+    """The six named workloads (1-based), optionally shortened to L tokens
     (structure kept, sizes scaled) for parity tests the oracle finishes fast."""
     s = i if seed is None else seed
     if i == 1:
@@ -257,6 +257,19 @@ def config(i, L=None, seed=None):
             else:
                 heads.append(vs(kv, ks, 'plain'))
         return LayerSpec('mixed-1m', L_, 32, 8, 128, s, heads, segs=segs, period=per)
+    if i == 6:
+        # parallel encoding over a long video: a prompt, frames of 196 tokens,
+        # a question as long as the prompt; the sink block is the prompt and
+        # the first 16 frames, context blocks are 16 frames
+        if L is None:
+            text, frames, per, fpb = 512, 512, 196, 16
+        else:
+            text, per, fpb = 64, 49, 2
+            frames = max(2 * fpb + 1, (L - 2 * text) // per)
+        segs = [(0, text, TEXT), (text, frames * per, VIDEO), (text + frames * per, text, TEXT)]
+        L_ = 2 * text + frames * per
+        heads = [parallel(text + fpb * per, fpb * per, text)] * 28
+        return LayerSpec('pevlm-video-101k', L_, 28, 4, 128, s, heads, segs=segs, period=per)
     raise ValueError(i)
 
 

@@ -46,7 +46,7 @@
 extern "C" {
 #endif
 
-#define MMSA_ABI_VERSION 2
+#define MMSA_ABI_VERSION 3
 #define MMSA_TILE 64       /* query and key tile (the 64-token blocks)      */
 #define MMSA_EST_ROWS 64   /* estimation rows: the last 64 queries          */
 
@@ -61,8 +61,14 @@ enum {
 
 /* Per-head sparse pattern (the offline per-head assignment; MInference summary
  * page, "Approach": A-shape, vertical-slash, block-sparse; MMInference
- * verdict page, core_discovery: grid, Q-boundary, 2D-boundary). */
-enum { MMSA_ASHAPE = 0, MMSA_VS = 1, MMSA_BLOCK = 2, MMSA_GRID = 3 };
+ * verdict page, core_discovery: grid, Q-boundary, 2D-boundary).
+ * MMSA_PARALLEL is the static parallel-encoding mask of the PEVLM verdict page
+ * (key_machinery): tokens [0, sink) form the sink block, the last `question`
+ * tokens the question block, and the tokens between are cut into context
+ * blocks of `window` tokens from `sink` on (the last may be shorter).  A
+ * context row sees the sink block and its own block; sink and question rows
+ * see every earlier token; j <= i throughout.  It needs no estimation. */
+enum { MMSA_ASHAPE = 0, MMSA_VS = 1, MMSA_BLOCK = 2, MMSA_GRID = 3, MMSA_PARALLEL = 4 };
 /* Layout (how modality boundaries are handled; MMInference verdict page,
  * core_discovery: row-wise permutation grouping same-modality queries, 2D
  * permutation isolating each modality pair). */
@@ -91,10 +97,11 @@ enum { MMSA_TEXT = 0, MMSA_VIDEO = 1 };
 #define MMSA_FLAG_MATERIALIZE 1u
 
 typedef struct {
-  int32_t pattern;      /* MMSA_ASHAPE / VS / BLOCK / GRID                          */
+  int32_t pattern;      /* MMSA_ASHAPE / VS / BLOCK / GRID / PARALLEL               */
   int32_t layout;       /* MMSA_PLAIN / Q_BOUNDARY / BOUNDARY_2D / MODALITY_GROUPED  */
-  int32_t sink;         /* A-shape: keys j < sink are kept                           */
-  int32_t window;       /* A-shape: keys with i - j < window are kept (>= 1)         */
+  int32_t sink;         /* A-shape: keys j < sink are kept; PARALLEL: sink block length */
+  int32_t window;       /* A-shape: keys with i - j < window are kept (>= 1);
+                           PARALLEL: context block length (>= 1)                     */
   int32_t k_vertical;   /* VS: vertical columns kept (per index set)                 */
   int32_t k_slash;      /* VS: slash diagonals kept (per index set)                  */
   int32_t k_blocks;     /* BLOCK: key blocks kept per query block                    */
@@ -102,6 +109,7 @@ typedef struct {
   int32_t stride_lo;    /* GRID: smallest stride searched (>= 16)                    */
   int32_t stride_hi;    /* GRID: largest stride searched (>= stride_lo, <= 1024)     */
   int32_t grid_clip;    /* GRID: clip constant C of the line score (1..64; 0 -> 8)   */
+  int32_t question;     /* PARALLEL: question block length (>= 0; clamped to L)     */
 } mmsa_head_cfg;
 
 /* A run of tokens of one modality.  Segments must tile [0, L) in order. */

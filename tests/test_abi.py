@@ -127,6 +127,10 @@ def test_descriptor_validation(L, mutate, code, needle):
     (dict(pattern="grid", stride_lo=8, stride_hi=64), "grid needs"),
     (dict(pattern="grid", stride_lo=64, stride_hi=2048), "grid needs"),
     (dict(pattern="grid", stride_lo=200, stride_hi=100), "grid needs"),
+    (dict(pattern="parallel", layout="q_boundary", sink=4, window=64), "valid combination"),
+    (dict(pattern="parallel", sink=-1, window=64), "parallel encoding"),
+    (dict(pattern="parallel", sink=64, window=0), "parallel encoding"),
+    (dict(pattern="parallel", sink=64, window=64, question=-3), "parallel encoding"),
 ])
 def test_head_validation(L, head, needle):
     lay = host_layer([head], Hkv=1)

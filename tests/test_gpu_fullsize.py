@@ -44,17 +44,17 @@ def representative_heads(spec):
     return heads
 
 
-def rows_for(spec, h, n_uniform, seed):
+def rows_for(spec, h, n_uniform, seed, extra=()):
     L = spec.L
     rng = np.random.default_rng(seed)
-    rows = {0, 1, 63, 64, L - 1, L - 2, L - 64, L // 2}
+    rows = {0, 1, 63, 64, L - 1, L - 2, L - 64, L // 2} | set(extra)
     rows |= set(int(x) for x in rng.integers(0, L, n_uniform))
     for s, n, m in (spec.segs or []):
         rows |= {s, s + 1, s + n - 1}
     return np.array(sorted(r for r in rows if 0 <= r < L), np.int64)
 
 
-def run_config(i, n_uniform=10, n_tiles=2):
+def run_config(i, n_uniform=10, n_tiles=2, extra_rows=(), whole_layer_check=None):
     spec = synth.config(i)
     t0 = time.time()
     Lg, q, k, v, o, lse = run_gpu(spec)
@@ -73,7 +73,7 @@ def run_config(i, n_uniform=10, n_tiles=2):
         g = gmap[h]
         qh, kh, vh = f64(q[0, h]), f64(k[0, g]), f64(v[0, g])
         hi = check_head_indices(Lg, h, spec.heads[h], qh, kh, spec.segs, scale)
-        rows = rows_for(spec, h, n_uniform, 1000 * i + h)
+        rows = rows_for(spec, h, n_uniform, 1000 * i + h, extra_rows)
         og = f64(o[0, h][torch.as_tensor(rows, device=o.device)])
         lg = lse[0, h][torch.as_tensor(rows, device=o.device)].cpu().numpy().astype(np.float64)
         # check_attention indexes og/lse by row, so scatter the sampled rows back
@@ -84,11 +84,14 @@ def run_config(i, n_uniform=10, n_tiles=2):
                         name=f"{spec.name} head {h} ({spec.heads[h]['pattern']}/"
                              f"{spec.heads[h].get('layout', 'plain')})")
         nT = -(-spec.L // 64)
-        tiles = sorted({0, nT - 1} | set(int(t) for t in rng.integers(0, nT, n_tiles)))
+        tiles = sorted({0, nT - 1} | set(int(t) for t in rng.integers(0, nT, n_tiles))
+                       | {int(r) // 64 for r in extra_rows if 0 <= r < spec.L})
         check_tile_pairs(Lg, h, hi, tiles)
         say(f"{spec.name}: head {h} {spec.heads[h]['pattern']}/{spec.heads[h].get('layout', 'plain')} ok "
             f"({len(rows)} rows, tiles {tiles}) in {time.time() - t1:.1f} s")
         del qh, kh, vh, hi
+    if whole_layer_check is not None:
+        whole_layer_check(spec, Lg)
     del Lg, q, k, v, o, lse
     torch.cuda.empty_cache()
 
@@ -130,3 +133,23 @@ def test_mixed_1m_materialized_equals_index_based():
     assert torch.equal(lse_idx, lse_mat.view(torch.int32))
     del q, k, v, o_idx, o_mat, lse_idx, lse_mat
     torch.cuda.empty_cache()
+
+
+@pytest.mark.timeout(600)
+def test_pevlm_video_101k():
+    # parallel encoding: rows and tiles at every kind of block edge, and each
+    # head's planned pairs equal to the page's block count made causal
+    spec = synth.config(6)
+    c = spec.heads[0]
+    S, B, Q = c["sink"], c["window"], c["question"]
+    N = (spec.L - S - Q) // B
+    assert S + N * B + Q == spec.L
+    edges = [S - 1, S, S + B - 1, S + B, S + 7 * B + 100, spec.L - Q - 1, spec.L - Q]
+
+    def totals(spec, Lg):
+        whole = S * S + Q * Q + N * B * B + Q * S + N * Q * B + N * S * B
+        upper = S * (S - 1) // 2 + N * (B * (B - 1) // 2) + Q * (Q - 1) // 2
+        for h in range(spec.Hq):
+            assert int(Lg.view("tile_pairs", h).sum().item()) == whole - upper, f"head {h}"
+
+    run_config(6, extra_rows=edges, whole_layer_check=totals)

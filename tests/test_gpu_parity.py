@@ -100,6 +100,32 @@ def test_edge_lengths(L):
     full_check(synth.small_spec("edge", L, 4, 4, 64, heads, seed=L))
 
 
+def test_parallel_encoding_ragged():
+    # sink, context and question blocks off the 64-token tiles, a partial last
+    # context block, a head with no sink or question, and 5-token blocks
+    heads = [synth.parallel(300, 517, 129), synth.parallel(0, 64, 0), synth.parallel(236, 392, 64),
+             synth.parallel(37, 5, 100)]
+    full_check(synth.small_spec("parallel", 3017, 4, 2, 128, heads, seed=21))
+
+
+@pytest.mark.parametrize("L", [1, 63, 65, 130])
+def test_parallel_encoding_edges(L):
+    # sink or question covering the whole layer, and one block per token
+    heads = [synth.parallel(40, 30, 20), synth.parallel(L + 5, 3, 0), synth.parallel(0, 1, 0),
+             synth.parallel(10, 7, L + 9)]
+    full_check(synth.small_spec("parallel-edge", L, 4, 4, 64, heads, seed=L + 100))
+
+
+def test_parallel_encoding_mixed_with_estimated_heads():
+    heads = [synth.parallel(128, 196, 64), synth.vs(30, 60), synth.ashape(16, 100), synth.block(4)]
+    full_check(synth.small_spec("parallel-mixed", 1500, 4, 1, 128, heads, seed=23))
+
+
+def test_parallel_encoding_video_layer_shortened():
+    # the 101K parallel-encoding workload's structure at 3K tokens
+    full_check(synth.config(6, L=3000), rows_per_head=300)
+
+
 def test_empty_layer_is_noop():
     spec = synth.small_spec("empty", 0, 2, 1, 128, [synth.vs(3, 5), synth.ashape(4, 8)], seed=0)
     q = torch.empty((1, 2, 0, 128), dtype=torch.bfloat16, device="cuda")
