@@ -36,9 +36,10 @@ on scores exported by the GPU.
 
 Parity pins live in tests/test_oracle_*.py.  Parity unpinned against the pages
 themselves: the slash-to-tile reading, the grid stride/phase rule and the
-boundary coordinates are this project's readings (listed in the design doc); they
-are pinned against brute force and mathematics, not against the authors'
-implementation, which is not available.
+boundary coordinates are this project's readings; they are pinned against
+brute force and mathematics, not against the authors' implementation, which
+is not available.  The parallel-encoding mask is the exception: its pair
+count is pinned against the operation count [PE] prints, made causal.
 """
 from __future__ import annotations
 
