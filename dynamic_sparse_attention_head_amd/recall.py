@@ -107,6 +107,43 @@ def budget_search(q, k, v, candidates, target=0.95, segs=None):
     return chosen, table
 
 
+def scene_cut_recall(spec, lse_dense=None):
+    """Mean recall per head of the video rows before the scene cut that come
+    after the planted keys (rows [(r0 + cut) // 2, cut)), and of the rows from
+    the cut on, for a layer from `synth.scene_cut`."""
+    q, k, v = spec["q"], spec["k"], spec["v"]
+    s = spec["spec"]
+    _, rec = row_recall(q, k, v, s.heads, s.segs, lse_dense)
+    r0, cut, r1 = s.target_rows
+    pre = rec[:, (r0 + cut) // 2:cut].mean(dim=1)
+    post = rec[:, cut:r1].mean(dim=1) if r1 > cut else torch.full_like(pre, float("nan"))
+    return pre, post
+
+
+def scene_cut_study(frames=160, per=196, text=512, amps=(6.0, 10.0), budgets=((256, 512), (1000, 4096))):
+    """The MMInference verdict page's falsifier on synthetic input: a video
+    segment whose last 64 queries (the rows the per-modality estimate uses)
+    aim at other keys than the rest of the segment.  For each amplitude and
+    vertical-slash budget, the recall of the earlier rows with and without the
+    cut, per layout (plain, Q-boundary, 2D-boundary)."""
+    from . import synth
+    out = []
+    for amp in amps:
+        for kv, ks in budgets:
+            heads = [synth.vs(kv, ks), synth.vs(kv, ks, "q_boundary"), synth.vs(kv, ks, "boundary_2d")]
+            row = dict(amp=amp, k_vertical=kv, k_slash=ks)
+            for cut in (False, True):
+                spec = synth.scene_cut(frames, per, text, cut=cut, amp=amp, heads=heads)
+                lay = synth.make_layer(spec, "cuda")
+                pre, post = scene_cut_recall(lay)
+                row["cut" if cut else "no_cut"] = [round(float(x), 4) for x in pre]
+                if cut:
+                    row["after_cut"] = [round(float(x), 4) for x in post]
+                del lay
+            out.append(row)
+    return out
+
+
 def _summary(rows):
     groups = {}
     for r in rows:
@@ -130,7 +167,17 @@ def main():
     ap = argparse.ArgumentParser(description="recall vs kernel FLOPs of the estimated masks on a synthetic layer")
     ap.add_argument("--config", type=int, default=2)
     ap.add_argument("--target", type=float, default=0.95)
+    ap.add_argument("--scene-cut", action="store_true",
+                    help="run the scene-cut stress (recall of a video segment's earlier rows when its last "
+                         "64 queries attend elsewhere) instead of the budget sweep")
     args = ap.parse_args()
+    if args.scene_cut:
+        print("scene cut at the end of the video segment; recall of the earlier rows "
+              "(plain, Q-boundary, 2D-boundary vertical-slash heads)", flush=True)
+        for r in scene_cut_study():
+            print(f"  amp {r['amp']:4.1f} budget {r['k_vertical']}/{r['k_slash']}: no cut {r['no_cut']}  "
+                  f"cut {r['cut']}  rows after the cut {r['after_cut']}", flush=True)
+        return
     spec = synth.config(args.config)
     lay = synth.make_layer(spec, "cuda")
     q, k, v = lay["q"], lay["k"], lay["v"]

@@ -47,6 +47,12 @@ class LayerSpec:
     period_amp: float = 2.0
     frame_amp: float = 0.5
     q_periodic: bool = True
+    # planted attention targets with a scene cut: query rows [r0, cut) aim at
+    # `targets` keys A and rows [cut, r1) at `targets` other keys B, both
+    # drawn from [r0, (r0 + cut) // 2); cut == r1 means no cut
+    targets: int = 0
+    target_amp: float = 10.0
+    target_rows: tuple = None         # (r0, cut, r1)
     meta: dict = field(default_factory=dict)
 
 
@@ -133,6 +139,15 @@ def make_layer(spec: LayerSpec, device='cpu'):
             delta = delta / delta.norm(dim=1, keepdim=True)
             fr = torch.clamp(frame, min=0)
             kg += pi + spec.frame_amp * delta[fr] * isv[:, None]
+        if spec.targets:
+            r0, cut, r1 = spec.target_rows
+            gt = _gen(spec.seed, 400 + g, dev)
+            span = max((r0 + cut) // 2 - r0, 2 * spec.targets)
+            pos = r0 + torch.randperm(span, generator=gt, device=dev)[:2 * spec.targets]
+            uab, _ = torch.linalg.qr(torch.randn((d, 2), generator=gt, device=dev).cpu())
+            u_a, u_b = uab[:, 0].to(dev), uab[:, 1].to(dev)
+            kg[pos[:spec.targets]] += spec.target_amp * u_a
+            kg[pos[spec.targets:]] += spec.target_amp * u_b
         k[0, g] = kg.to(torch.bfloat16)
         del kg
         gv = _gen(spec.seed, 200 + g, dev)
@@ -145,6 +160,9 @@ def make_layer(spec: LayerSpec, device='cpu'):
                 qh = _rope(qh, spec.rope_base)
             if spec.period and spec.q_periodic:
                 qh += pi
+            if spec.targets:
+                qh[r0:cut] += spec.target_amp * u_a
+                qh[cut:r1] += spec.target_amp * u_b
             q[0, h] = qh.to(torch.bfloat16)
             del qh
     return dict(q=q, k=k, v=v, spec=spec, heads=spec.heads, segs=spec.segs,
@@ -190,6 +208,20 @@ def interleaved_segments(n_chunks, frames, per_frame, text_len, lead_text=0):
         segs.append((pos, n, VIDEO))
         pos += n
     return segs, pos
+
+
+def scene_cut(frames=40, per=196, text=512, cut=True, targets=64, amp=10.0, heads=None, seed=7, d=128):
+    """A text prompt then one video segment whose queries aim at one set of
+    planted keys, except its last 64 queries, which aim at another (a scene
+    cut at the segment end); with cut=False every video query aims at the
+    first set.  Default heads: plain, Q-boundary and 2D-boundary
+    vertical-slash (256 / 512)."""
+    L = text + frames * per
+    segs = [(0, text, TEXT), (text, frames * per, VIDEO)]
+    heads = heads or [vs(256, 512), vs(256, 512, 'q_boundary'), vs(256, 512, 'boundary_2d')]
+    c = L - 64 if cut else L
+    return LayerSpec('scene-cut' if cut else 'no-cut', L, len(heads), 1, d, seed, heads, segs=segs,
+                     targets=targets, target_amp=amp, target_rows=(text, c, L))
 
 
 def config(i, L=None, seed=None):

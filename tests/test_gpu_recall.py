@@ -68,3 +68,27 @@ def test_budget_search_picks_cheapest_budget_meeting_target():
         f = [table[i][h]["planned_flops"] for i in range(3)]
         assert r[0] <= r[1] + 1e-3 <= r[2] + 2e-3 and f[0] <= f[1] <= f[2]
         assert r[2] >= 0.999
+
+
+def test_scene_cut_at_segment_end_lowers_recall_of_earlier_rows():
+    # The MMInference verdict page's falsifier: when a video segment's last 64
+    # queries (the rows its estimate uses) aim at other keys than the rest of
+    # the segment, the estimated masks miss the earlier rows' keys.
+    heads = [synth.vs(64, 64), synth.vs(64, 64, "q_boundary"), synth.vs(64, 64, "boundary_2d")]
+    pre = {}
+    for cut in (True, False):
+        spec = synth.scene_cut(frames=12, per=196, text=256, cut=cut, amp=10.0, heads=heads)
+        lay = synth.make_layer(spec, "cuda")
+        q, k, v = lay["q"], lay["k"], lay["v"]
+        L, rec = recall.row_recall(q, k, v, spec.heads, spec.segs)
+        scale = 1.0 / math.sqrt(spec.d)
+        r0, c, r1 = spec.target_rows
+        rows = np.arange((r0 + c) // 2, c, 13)
+        for h in range(spec.Hq):
+            qh, kh = f64(q[0, h]), f64(k[0, 0])
+            hi = check_head_indices(L, h, spec.heads[h], qh, kh, spec.segs, scale)
+            ref = O.head_recall(hi, qh, kh, scale, rows)
+            assert np.abs(rec[h].cpu().numpy()[rows] - ref).max() <= 5e-3, f"head {h}"
+        pre[cut] = recall.scene_cut_recall(lay)[0].cpu().numpy()
+    assert (pre[False] >= 0.95).all(), pre[False]
+    assert (pre[True] <= 0.6).all(), pre[True]
