@@ -61,7 +61,7 @@ Q24 = 1 << 24      # grid rule fixed-point quantum 2^-24
 @dataclass
 class HeadCfg:
     pattern: str                 # 'ashape' | 'vs' | 'block' | 'grid' | 'parallel'
-    layout: str = 'plain'        # 'plain' | 'q_boundary' | 'boundary_2d' | 'modality_grouped'
+    layout: str = 'plain'        # 'plain' | 'q_boundary' | 'boundary_2d' | 'q_segment' | 'modality_grouped'
     sink: int = 0
     window: int = 1
     k_vertical: int = 0
@@ -108,6 +108,14 @@ def modality_tables(L, segs):
         rank[sel] = np.arange(sel.size)
         n[mod] = sel.size
     return m, rank, n
+
+
+def segment_index(L, segs):
+    """Index of the segment holding each position."""
+    out = np.zeros(L, np.int64)
+    for n_, (start, ln, _) in enumerate(_segments(L, segs)):
+        out[start:start + ln] = n_
+    return out
 
 
 def grouped_positions(L, segs):
@@ -360,12 +368,17 @@ def estimate_head(cfg, qh, kh, segs, scale, scores_override=None):
     assert cfg.pattern == 'vs'
     if cfg.layout == 'plain':
         regions = [('all', estimation_rows(np.arange(L)))]
+    elif cfg.layout == 'q_segment':
+        # [MMV] core_discovery names estimation from the last 64 queries of
+        # each modality segment; this layout takes every segment on its own
+        regions = [(('seg', n_), estimation_rows(np.arange(start, start + ln)))
+                   for n_, (start, ln, _) in enumerate(segs)]
     else:
         regions = [(mod, _region_rows_for_modality(mtab, mod)) for mod in (TEXT, VIDEO) if n[mod] > 0]
     for key, rows in regions:
         a, mx, ssum = last_rows_attention(qh[rows], kh, rows, scale)
         hi.extras[('stats', key)] = (mx, ssum)
-        if cfg.layout in ('plain', 'q_boundary'):
+        if cfg.layout in ('plain', 'q_boundary', 'q_segment'):
             v, s = vs_scores_original(a, rows, L)
             vc, sc = vs_candidates_original(rows)
             v32 = ov.get(('v', key), v.astype(np.float32))
@@ -402,8 +415,24 @@ def _tile_rows(hi, i, mtab, rtab):
         t = rtab[i] // TILE
         pos = np.nonzero(mtab == mod)[0]
         return pos[t * TILE:(t + 1) * TILE]
+    if hi.cfg.layout == 'q_segment':   # 64 consecutive positions of one segment
+        for start, ln, _ in hi.segs:
+            if start <= i < start + ln:
+                t0 = start + ((i - start) // TILE) * TILE
+                return np.arange(t0, min(start + ln, t0 + TILE))
     t = i // TILE
     return np.arange(t * TILE, min(L, (t + 1) * TILE))
+
+
+def _vs_key(hi, i, mtab):
+    """The index set row i uses: the layer's, its modality's or its segment's."""
+    if hi.cfg.layout == 'plain':
+        return 'all'
+    if hi.cfg.layout == 'q_segment':
+        if 'segidx' not in hi.extras:
+            hi.extras['segidx'] = segment_index(hi.L, hi.segs)
+        return ('seg', int(hi.extras['segidx'][i]))
+    return int(mtab[i])
 
 
 def _slash_tiles_original(rows, S):
@@ -454,8 +483,8 @@ def row_mask(hi, i, cache=None):
     mtab, rtab, n = cache['mr']
     rows = _tile_rows(hi, i, mtab, rtab)
     sel = np.zeros(L, bool)
-    if cfg.layout in ('plain', 'q_boundary'):
-        key = 'all' if cfg.layout == 'plain' else int(mtab[i])
+    if cfg.layout in ('plain', 'q_boundary', 'q_segment'):
+        key = _vs_key(hi, i, mtab)
         V, S = hi.vs[key]
         tiles = _slash_tiles_original(rows, S)
         tsel = np.zeros(-(-L // TILE), bool)
@@ -566,6 +595,8 @@ def row_order(hi):
     if cfg.pattern == 'vs' and cfg.layout in ('q_boundary', 'boundary_2d'):
         mtab, _, _ = modality_tables(L, hi.segs)
         return np.concatenate([_pad_to_tile(np.nonzero(mtab == m)[0]) for m in (TEXT, VIDEO)])
+    if cfg.pattern == 'vs' and cfg.layout == 'q_segment':
+        return np.concatenate([_pad_to_tile(np.arange(start, start + ln)) for start, ln, _ in hi.segs])
     return _pad_to_tile(np.arange(L))
 
 
@@ -599,9 +630,8 @@ def tile_plan(hi, tile_rows):
         keys = np.nonzero(line)[0]
         return [], [keys[keys <= pmax]]
     mtab, rtab, n = modality_tables(L, hi.segs)
-    if cfg.layout in ('plain', 'q_boundary'):
-        key = 'all' if cfg.layout == 'plain' else int(mtab[tile_rows[0]])
-        V, S = hi.vs[key]
+    if cfg.layout in ('plain', 'q_boundary', 'q_segment'):
+        V, S = hi.vs[_vs_key(hi, int(tile_rows[0]), mtab)]
         ts = _slash_tiles_original(tile_rows, S)
         tset = set(int(c) for c in ts)
         gath = np.array([c for c in V if c <= pmax and (c // TILE) not in tset], np.int64)

@@ -569,3 +569,61 @@ def test_parallel_single_block_and_all_question_are_dense():
         hi = O.estimate_head(cfg, q[0], k[0], None, scale)
         got, _ = O.head_attention(hi, q[0], k[0], v[0], scale)
         np.testing.assert_allclose(got, ref, atol=1e-10, rtol=0)
+
+
+# ---------------------------------------------------------------------------
+# Per-segment estimation (the last 64 queries of each segment)
+# ---------------------------------------------------------------------------
+def _masks(hi, L):
+    cache = {}
+    return np.array([O.row_mask(hi, i, cache) for i in range(L)])
+
+
+@pytest.mark.parametrize("segs", [[(0, 130, 0), (130, 260, 1)], [(0, 200, 1), (200, 77, 0)]])
+def test_segment_layout_with_one_segment_per_modality_is_q_boundary(segs):
+    L, d = sum(s[1] for s in segs), 16
+    q, k, v, _ = small_layer(L, d, [synth.vs(9, 14)], seed=13, segs=segs)
+    scale = 1 / math.sqrt(d)
+    hs = O.estimate_head(synth.vs(9, 14, 'q_segment'), q[0], k[0], segs, scale)
+    hq = O.estimate_head(synth.vs(9, 14, 'q_boundary'), q[0], k[0], segs, scale)
+    for n_, (_, _, m) in enumerate(segs):
+        assert [list(x) for x in hs.vs[('seg', n_)]] == [list(x) for x in hq.vs[m]]
+    np.testing.assert_array_equal(_masks(hs, L), _masks(hq, L))
+
+
+def test_segment_layout_with_a_single_segment_is_plain():
+    L, d = 300, 16
+    q, k, v, _ = small_layer(L, d, [synth.vs(9, 14)], seed=14)
+    scale = 1 / math.sqrt(d)
+    hs = O.estimate_head(synth.vs(9, 14, 'q_segment'), q[0], k[0], [(0, L, 1)], scale)
+    hp = O.estimate_head(synth.vs(9, 14), q[0], k[0], None, scale)
+    np.testing.assert_array_equal(_masks(hs, L), _masks(hp, L))
+
+
+def test_segment_scores_and_tile_masks_by_loops():
+    L, d = 407, 8
+    segs = [(0, 100, 0), (100, 150, 1), (250, 37, 0), (287, 120, 1)]
+    q, k, v, _ = small_layer(L, d, [synth.vs(6, 4, 'q_segment')], seed=15, segs=segs)
+    scale = 1 / math.sqrt(d)
+    hi = O.estimate_head(synth.vs(6, 4, 'q_segment'), q[0], k[0], segs, scale)
+    for n_, (st, ln, _) in enumerate(segs):
+        # scores from the segment's last min(64, len) queries, by loops
+        rows = list(range(st + max(0, ln - 64), st + ln))
+        vref = np.zeros(L)
+        for r in rows:
+            lg = [scale * float(np.dot(q[0][r], k[0][j])) for j in range(r + 1)]
+            m = max(lg)
+            w = [math.exp(x - m) for x in lg]
+            for j in range(r + 1):
+                vref[j] += w[j] / sum(w)
+        np.testing.assert_allclose(hi.extras[('v', ('seg', n_))], vref, rtol=1e-5, atol=1e-7)
+        V, S = hi.vs[('seg', n_)]
+        for i in sorted({st, st + 63, st + 64, st + ln - 1} & set(range(st, st + ln))):
+            t0 = st + ((i - st) // TILE) * TILE
+            rows_of = lambda i, t0=t0, e=st + ln: list(range(t0, min(e, t0 + TILE)))
+            assert (O.row_mask(hi, i) == _loop_vs_mask(i, L, rows_of, V, S)).all(), (n_, i)
+
+
+def test_permuted_equals_direct_vs_segment():
+    segs = [(0, 100, 0), (100, 150, 1), (250, 37, 0), (287, 120, 1)]
+    _check_perm(synth.vs(20, 9, 'q_segment'), 407, 16, segs, seed=7)
