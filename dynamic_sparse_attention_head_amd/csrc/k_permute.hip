@@ -49,11 +49,16 @@ __global__ __launch_bounds__(256) void k_seg_tables(Dims dm, Tables tb, char* ws
   const int slot = (sg.modality == MMSA_VIDEO ? dm.video_base : dm.text_base) + rank;
   wsp<int32_t>(ws, dm.ws_gslot)[p] = slot;
   wsp<int32_t>(ws, dm.ws_pgrp)[slot] = p;
+  if (dm.ws_pseg >= 0) wsp<int32_t>(ws, dm.ws_pseg)[sg.slot0 + (int)(p - sg.start)] = p;
 }
 
 hipError_t launch_seg_tables(const Dims& dm, const Tables& tb, char* ws, hipStream_t s) {
   hipError_t e = launch_fill_u32(ws + dm.ws_pgrp, 0xffffffffu, dm.L_grp, s);
   if (e != hipSuccess) return e;
+  if (dm.ws_pseg >= 0) {
+    e = launch_fill_u32(ws + dm.ws_pseg, 0xffffffffu, dm.L_seg, s);
+    if (e != hipSuccess) return e;
+  }
   if (dm.L > 0) k_seg_tables<<<(dm.L + 255) / 256, 256, 0, s>>>(dm, tb, ws);
   return hipGetLastError();
 }
@@ -328,7 +333,19 @@ __global__ __launch_bounds__(256) void k_plan(Dims dm, Tables tb, char* ws) {
     const bool grouped_rows = H.row_kind == ROW_GROUPED;
     int m_q = MMSA_TEXT;
     if (grouped_rows) m_q = (64 * t >= dm.video_base && dm.n_video > 0 && (dm.video_base > 0 || dm.n_text == 0)) ? MMSA_VIDEO : MMSA_TEXT;
-    const EstJob& J = wsp<const EstJob>(ws, tb.off_jobs)[H.job[grouped_rows ? m_q : 0]];
+    int jidx = H.job[grouped_rows ? m_q : 0];
+    if (H.row_kind == ROW_SEGMENT) {
+      // the segment whose padded slots hold this tile, and its estimation job
+      const SegDev* segs = wsp<const SegDev>(ws, tb.off_segs);
+      int lo = 0, hi = (int)tb.n_segs - 1;
+      while (lo < hi) {
+        const int mid = (lo + hi + 1) >> 1;
+        if (segs[mid].slot0 <= 64 * t) lo = mid;
+        else hi = mid - 1;
+      }
+      jidx = wsp<const int32_t>(ws, tb.off_segjob)[H.segjob + lo];
+    }
+    const EstJob& J = wsp<const EstJob>(ws, tb.off_jobs)[jidx];
     // runs of the tile's rows in the slash coordinate (positions; ranks for 2D)
     if (tid == 0) {
       if (twod) {

@@ -45,6 +45,7 @@ struct Bump {
 struct Seg {
   int64_t start, len;
   int modality, rank_start;
+  int slot0;   // first slot in the segment-grouped order
 };
 
 struct Layout {
@@ -75,6 +76,8 @@ struct Layout {
   int64_t zero_off = 0, zero_bytes = 0;       // vertical scores and slash accumulators
   int64_t gridrow_off = 0, gridrow_bytes = 0; // grid row orders (filled with -1)
   bool need_seg = false, any_vs_est = false, any_block = false;
+  bool need_pseg = false;                 // some head uses the segment-grouped row order
+  std::vector<int32_t> segjob;            // per Q_SEGMENT head: the job of each segment
   bool empty = false;
   bool materialize = false;   // explicit gathers and output scatter (MMSA_FLAG_MATERIALIZE)
   // per (bh, part) index-set facts for mmsa_index_meta / views: job index and pair index
@@ -121,7 +124,9 @@ bool valid_combo(int pattern, int layout) {
     case MMSA_ASHAPE:
     case MMSA_PARALLEL:
     case MMSA_BLOCK: return layout == MMSA_PLAIN;
-    case MMSA_VS: return layout == MMSA_PLAIN || layout == MMSA_Q_BOUNDARY || layout == MMSA_BOUNDARY_2D;
+    case MMSA_VS:
+      return layout == MMSA_PLAIN || layout == MMSA_Q_BOUNDARY || layout == MMSA_BOUNDARY_2D ||
+             layout == MMSA_Q_SEGMENT;
     case MMSA_GRID: return layout == MMSA_PLAIN || layout == MMSA_MODALITY_GROUPED;
     default: return false;
   }
@@ -252,7 +257,7 @@ mmsa_status build_layout(const mmsa_layer_desc* desc, Layout& Lo) {
                 (long long)s.start, (long long)s.len, s.modality);
         return MMSA_INVALID_ARGUMENT;
       }
-      Lo.segs.push_back(Seg{s.start, s.len, s.modality, rank[s.modality]});
+      Lo.segs.push_back(Seg{s.start, s.len, s.modality, rank[s.modality], 0});
       rank[s.modality] += (int)s.len;
       pos += s.len;
     }
@@ -264,9 +269,14 @@ mmsa_status build_layout(const mmsa_layer_desc* desc, Layout& Lo) {
     set_err("n_segs=%d with segs=%p", D.n_segs, (const void*)D.segs);
     return MMSA_INVALID_ARGUMENT;
   } else if (D.L > 0) {
-    Lo.segs.push_back(Seg{0, D.L, MMSA_TEXT, 0});
+    Lo.segs.push_back(Seg{0, D.L, MMSA_TEXT, 0, 0});
   }
-  for (const Seg& s : Lo.segs) Lo.n_mod[s.modality] += (int)s.len;
+  int64_t seg_slots = 0;
+  for (Seg& s : Lo.segs) {
+    Lo.n_mod[s.modality] += (int)s.len;
+    s.slot0 = (int)seg_slots;
+    seg_slots += pad_to(s.len, TILE);
+  }
 
   Dims& dm = Lo.dm;
   dm.B = D.B;
@@ -280,6 +290,7 @@ mmsa_status build_layout(const mmsa_layer_desc* desc, Layout& Lo) {
   dm.text_base = 0;
   dm.video_base = (int)pad_to(dm.n_text, GRP_PAD);
   dm.L_grp = (int)(pad_to(dm.n_text, GRP_PAD) + pad_to(dm.n_video, GRP_PAD));
+  dm.L_seg = (int)seg_slots;
   dm.scale = D.scale > 0.f ? D.scale : 1.0f / std::sqrt((float)D.d);
   dm.scale_log2 = dm.scale * 1.4426950408889634f;
   dm.q_sb = D.q_strides[0];
@@ -304,7 +315,7 @@ mmsa_status build_layout(const mmsa_layer_desc* desc, Layout& Lo) {
 
   const int L = D.L, nT = Lo.nT;
   Lo.nB = nT;
-  Lo.set_of.assign(Lo.BH, std::vector<std::pair<int, int>>(4, {-1, -1}));
+  Lo.set_of.assign(Lo.BH, std::vector<std::pair<int, int>>(std::max<size_t>(4, Lo.segs.size()), {-1, -1}));
   // ---- heads, estimation jobs, tasks (offsets filled later) ----
   Lo.heads.resize(Lo.BH);
   for (int b = 0; b < D.B; ++b) {
@@ -321,6 +332,7 @@ mmsa_status build_layout(const mmsa_layer_desc* desc, Layout& Lo) {
       H.sink = c.sink;
       H.window = c.window;
       H.qstart = L - std::min(c.question, L);
+      H.segjob = -1;
       H.k_blocks = std::min(c.k_blocks, Lo.nB);
       H.grid_task = -1;
       H.job[0] = H.job[1] = -1;
@@ -333,7 +345,12 @@ mmsa_status build_layout(const mmsa_layer_desc* desc, Layout& Lo) {
       H.row_kind = ROW_IDENTITY;
       H.view_kind = VIEW_IDENTITY;
       H.n_row_slots = nT * TILE;
-      if (c.pattern == MMSA_VS && c.layout != MMSA_PLAIN) {
+      if (c.pattern == MMSA_VS && c.layout == MMSA_Q_SEGMENT) {
+        H.row_kind = ROW_SEGMENT;
+        H.n_row_slots = dm.L_seg;
+        Lo.need_seg = Lo.need_pseg = true;
+      }
+      if (c.pattern == MMSA_VS && (c.layout == MMSA_Q_BOUNDARY || c.layout == MMSA_BOUNDARY_2D)) {
         H.row_kind = ROW_GROUPED;
         H.n_row_slots = dm.L_grp;
         if (c.layout == MMSA_BOUNDARY_2D) H.view_kind = VIEW_GROUPED;
@@ -391,6 +408,24 @@ mmsa_status build_layout(const mmsa_layer_desc* desc, Layout& Lo) {
           H.job[0] = j;
           Lo.set_of[bh][0] = {j, 0};
           H.gcap = Lo.jobs[j].pair[0].kv;
+        } else if (c.layout == MMSA_Q_SEGMENT) {
+          // one estimation per segment: its last 64 queries, in original
+          // coordinates, for the rows of that segment
+          int gcap = 0;
+          H.segjob = (int)Lo.segjob.size();
+          for (size_t si = 0; si < Lo.segs.size(); ++si) {
+            const Seg& sg = Lo.segs[si];
+            std::vector<int> rows;
+            for (int64_t p = std::max<int64_t>(sg.start, sg.start + sg.len - EST_ROWS); p < sg.start + sg.len; ++p)
+              rows.push_back((int)p);
+            const int j = new_job(JOB_VS_ORIG, VIEW_IDENTITY, sg.modality, rows);
+            orig_pair(Lo.jobs[j]);
+            Lo.segjob.push_back(j);
+            if (si == 0) H.job[0] = j;
+            Lo.set_of[bh][si] = {j, 0};
+            gcap = std::max(gcap, Lo.jobs[j].pair[0].kv);
+          }
+          H.gcap = gcap;
         } else {
           int gcap = 0;
           for (int m = 0; m < 2; ++m) {
@@ -521,6 +556,7 @@ mmsa_status build_layout(const mmsa_layer_desc* desc, Layout& Lo) {
       for (int m = 0; m < 2; ++m)
         if (H.job[m] >= 0) H.job[m] = newidx[H.job[m]];
     for (GridTask& T : Lo.grids) T.job = newidx[T.job];
+    for (int32_t& j : Lo.segjob) j = newidx[j];
     for (auto& v : Lo.set_of)
       for (auto& pr : v)
         if (pr.first >= 0) pr.first = newidx[pr.first];
@@ -595,6 +631,7 @@ mmsa_status build_layout(const mmsa_layer_desc* desc, Layout& Lo) {
   tb.n_gather = n_perm + 2 * (int64_t)kv_grp.size();
   tb.n_unperm = n_perm;
   tb.n_qgroups = (int64_t)Lo.qgroups.size();
+  tb.n_segjob = (int64_t)Lo.segjob.size();
 
   Bump bp;
   tb.off_heads = bp.take((int64_t)sizeof(HeadDev) * tb.n_heads);
@@ -610,6 +647,7 @@ mmsa_status build_layout(const mmsa_layer_desc* desc, Layout& Lo) {
   tb.off_unperm = bp.take((int64_t)sizeof(UnpermTask) * tb.n_unperm);
   tb.off_qgroups = bp.take((int64_t)sizeof(QGroup) * tb.n_qgroups);
   tb.off_qgroup_heads = bp.take((int64_t)sizeof(int32_t) * (int64_t)Lo.qgroup_heads.size());
+  tb.off_segjob = bp.take((int64_t)sizeof(int32_t) * tb.n_segjob);
   const int64_t blob_bytes = pad_to(bp.off, 256);
 
   // ---- device buffers ----
@@ -617,6 +655,7 @@ mmsa_status build_layout(const mmsa_layer_desc* desc, Layout& Lo) {
   dm.ws_flag = bp.take(256);
   dm.ws_pgrp = bp.take(4ll * std::max(dm.L_grp, 1));
   dm.ws_gslot = bp.take(4ll * L);
+  dm.ws_pseg = Lo.need_pseg ? bp.take(4ll * std::max(dm.L_seg, 1)) : -1;
   for (const HeadDev& H : Lo.heads) Lo.max_items += (H.nT_rows + 1) / 2;
   dm.n_items = Lo.max_items;
   dm.ws_enum_item = bp.take(4 * Lo.max_items);
@@ -705,6 +744,7 @@ mmsa_status build_layout(const mmsa_layer_desc* desc, Layout& Lo) {
     }
     for (HeadDev& H : Lo.heads) {
       if (H.row_kind == ROW_GROUPED) H.ws_row_order = dm.ws_pgrp;
+      if (H.row_kind == ROW_SEGMENT) H.ws_row_order = dm.ws_pseg;
       if (Lo.materialize && H.row_kind != ROW_IDENTITY) {
         H.ws_qperm = bp.take(2ll * H.n_row_slots * dd);
         H.ws_operm = bp.take(2ll * H.n_row_slots * dd);
@@ -739,7 +779,7 @@ mmsa_status build_layout(const mmsa_layer_desc* desc, Layout& Lo) {
     if (bytes) std::memcpy(Lo.blob.data() + off, src, bytes);
   };
   std::vector<SegDev> sd;
-  for (const Seg& s : Lo.segs) sd.push_back(SegDev{s.start, s.len, s.modality, s.rank_start});
+  for (const Seg& s : Lo.segs) sd.push_back(SegDev{s.start, s.len, s.modality, s.rank_start, s.slot0, 0});
   put(tb.off_heads, Lo.heads.data(), sizeof(HeadDev) * Lo.heads.size());
   put(tb.off_jobs, Lo.jobs.data(), sizeof(EstJob) * Lo.jobs.size());
   put(tb.off_groups1, Lo.g1.data(), sizeof(EstGroup) * Lo.g1.size());
@@ -753,6 +793,7 @@ mmsa_status build_layout(const mmsa_layer_desc* desc, Layout& Lo) {
   put(tb.off_unperm, Lo.unperms.data(), sizeof(UnpermTask) * Lo.unperms.size());
   put(tb.off_qgroups, Lo.qgroups.data(), sizeof(QGroup) * Lo.qgroups.size());
   put(tb.off_qgroup_heads, Lo.qgroup_heads.data(), sizeof(int32_t) * Lo.qgroup_heads.size());
+  put(tb.off_segjob, Lo.segjob.data(), sizeof(int32_t) * Lo.segjob.size());
   return MMSA_OK;
 }
 
@@ -840,7 +881,7 @@ mmsa_status mmsa_workspace_view(const mmsa_layer_desc* desc, int32_t buf, int32_
   *offset_bytes = 0;
   *count = 0;
   if (Lo.empty) return MMSA_OK;
-  if (bh < 0 || bh >= Lo.BH || part < 0 || part > 3) {
+  if (bh < 0 || bh >= Lo.BH || part < 0 || part >= (int)Lo.set_of[bh].size()) {
     set_err("bh=%d / part=%d out of range", bh, part);
     return MMSA_INVALID_ARGUMENT;
   }
@@ -900,7 +941,7 @@ mmsa_status mmsa_index_meta(const mmsa_layer_desc* desc, int32_t bh, int32_t par
   MMSA_TRY(build_layout(desc, Lo));
   for (int i = 0; i < 8; ++i) out[i] = 0;
   if (Lo.empty) return MMSA_OK;
-  if (bh < 0 || bh >= Lo.BH || part < 0 || part > 3) {
+  if (bh < 0 || bh >= Lo.BH || part < 0 || part >= (int)Lo.set_of[bh].size()) {
     set_err("bh=%d / part=%d out of range", bh, part);
     return MMSA_INVALID_ARGUMENT;
   }

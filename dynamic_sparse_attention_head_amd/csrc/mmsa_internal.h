@@ -18,7 +18,7 @@ constexpr int N_XCD = 8;          // L2 domains (XCDs); workgroup i runs on XCD 
 constexpr int32_t KPOS_NONE = 0x7fffffff;  // key slot without a token (never causal)
 constexpr double SFIX = 1099511627776.0;   // 2^40: fixed-point scale of slash sums
 
-enum RowKind : int32_t { ROW_IDENTITY = 0, ROW_GROUPED = 1, ROW_GRID = 2 };
+enum RowKind : int32_t { ROW_IDENTITY = 0, ROW_GROUPED = 1, ROW_GRID = 2, ROW_SEGMENT = 3 };
 enum ViewKind : int32_t { VIEW_IDENTITY = 0, VIEW_GROUPED = 1 };
 enum JobKind : int32_t { JOB_VS_ORIG = 0, JOB_VS_2D = 1, JOB_GRID_PLAIN = 2, JOB_GRID_GROUPED = 3 };
 
@@ -26,6 +26,7 @@ enum JobKind : int32_t { JOB_VS_ORIG = 0, JOB_VS_2D = 1, JOB_GRID_PLAIN = 2, JOB
 struct SegDev {
   int64_t start, len;
   int32_t modality, rank_start;
+  int32_t slot0, _pad;         // first slot in the segment-grouped order (segments padded to 64)
 };
 
 // Per (batch, q head): everything a kernel needs to find this head's data.
@@ -43,6 +44,7 @@ struct HeadDev {
   int32_t b, h, g, pattern, layout;
   int32_t sink, window, k_blocks;
   int32_t qstart;            // PARALLEL: first row of the question block
+  int32_t segjob;            // Q_SEGMENT: first entry of its per-segment job list, else -1
   int32_t row_kind, view_kind;
   int32_t n_row_slots;       // slots of the row order (a multiple of 64)
   int32_t nT_rows;           // query tiles = n_row_slots / 64
@@ -157,19 +159,21 @@ struct QGroup {
 // Everything the kernels read, placed at the start of the workspace.
 struct Tables {
   int64_t n_heads, n_jobs, n_groups1, n_groups2, n_topk, n_grid, n_segs;
-  int64_t n_pool, n_block, n_gather, n_unperm, n_qgroups;
+  int64_t n_pool, n_block, n_gather, n_unperm, n_qgroups, n_segjob;
   int64_t off_heads, off_jobs, off_groups1, off_groups2, off_topk, off_grid, off_segs;
   int64_t off_pool, off_block, off_gather, off_unperm, off_qgroups, off_qgroup_heads;
+  int64_t off_segjob;        // int32: estimation job of each segment, per Q_SEGMENT head
 };
 
 // Shapes shared by every kernel of one call.
 struct Dims {
   int32_t B, Hq, Hkv, L, d, nT;
-  int32_t n_text, n_video, text_base, video_base, L_grp;
+  int32_t n_text, n_video, text_base, video_base, L_grp, L_seg;
   float scale, scale_log2;
   int64_t q_sb, q_sh, q_sl, k_sb, k_sh, k_sl, v_sb, v_sh, v_sl, o_sb, o_sh, o_sl;
   int64_t ws_pgrp;           // int32[L_grp]: original position at each grouped slot (-1 pad)
   int64_t ws_gslot;          // int32[L]: grouped slot of each position
+  int64_t ws_pseg;           // int32[L_seg]: original position at each segment-grouped slot (-1 pad), or -1
   int64_t n_items;           // queue length: every (head, pair of adjacent query tiles)
   int64_t ws_enum_item;      // int32 [n_items]: (bh << 16) | pair in queue order
   int64_t ws_enum_cost;      // int32 [n_items]: cost of each queued item

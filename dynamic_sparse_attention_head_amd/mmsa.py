@@ -18,7 +18,7 @@ LIB_PATH = os.path.join(_HERE, "libmmsa.so")
 TILE = 64
 OK, INVALID_ARGUMENT, UNSUPPORTED, WORKSPACE_TOO_SMALL, HIP_ERROR = range(5)
 PATTERNS = {"ashape": 0, "vs": 1, "block": 2, "grid": 3, "parallel": 4}
-LAYOUTS = {"plain": 0, "q_boundary": 1, "boundary_2d": 2, "modality_grouped": 3}
+LAYOUTS = {"plain": 0, "q_boundary": 1, "boundary_2d": 2, "modality_grouped": 3, "q_segment": 4}
 BUF = dict(v_scores=0, s_scores=1, v_index=2, s_index=3, nsel=4, grid=5, block_index=6, block_scores=7,
            row_order=8, tile_pairs=9, tile_info=10, est_stats=11, tile_bitmap=12)
 BUF_DTYPE = dict(v_scores=torch.float32, s_scores=torch.float32, v_index=torch.int32, s_index=torch.int32,

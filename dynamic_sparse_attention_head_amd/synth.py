@@ -225,7 +225,7 @@ def scene_cut(frames=40, per=196, text=512, cut=True, targets=64, amp=10.0, head
 
 
 def config(i, L=None, seed=None):
-    """The six named workloads (1-based), optionally shortened to L tokens
+    """The seven named workloads (1-based), optionally shortened to L tokens
     (structure kept, sizes scaled) for parity tests the oracle finishes fast."""
     s = i if seed is None else seed
     if i == 1:
@@ -289,6 +289,12 @@ def config(i, L=None, seed=None):
             else:
                 heads.append(vs(kv, ks, 'plain'))
         return LayerSpec('mixed-1m', L_, 32, 8, 128, s, heads, segs=segs, period=per)
+    if i == 7:
+        # the 1M mixed layer with per-segment estimation in place of the
+        # per-modality (Q-boundary) heads: 15 segments, 15 estimates per head
+        base = config(5, L=L, seed=s)
+        heads = [dict(h, layout='q_segment') if h['layout'] == 'q_boundary' else h for h in base.heads]
+        return replace(base, name='mixed-1m-segments', heads=heads)
     if i == 6:
         # parallel encoding over a long video: a prompt, frames of 196 tokens,
         # a question as long as the prompt; the sink block is the prompt and

@@ -76,7 +76,9 @@ enum {
   MMSA_PLAIN = 0,             /* no modality handling                              */
   MMSA_Q_BOUNDARY = 1,        /* VS only: rows grouped by modality, one index set per query modality */
   MMSA_BOUNDARY_2D = 2,       /* VS only: rows and keys grouped, one index set per (query, key) modality pair */
-  MMSA_MODALITY_GROUPED = 3   /* GRID only: stride/phase measured on the modality-grouped order */
+  MMSA_MODALITY_GROUPED = 3,  /* GRID only: stride/phase measured on the modality-grouped order */
+  MMSA_Q_SEGMENT = 4          /* VS only: rows grouped by segment (each padded to 64), one index set
+                                 per segment from its own last 64 queries (original coordinates) */
 };
 enum { MMSA_TEXT = 0, MMSA_VIDEO = 1 };
 
@@ -140,7 +142,8 @@ size_t mmsa_workspace_bytes(const mmsa_layer_desc* desc);
 /* Where a named intermediate of one (batch*Hq + head) `bh` lives in the
  * workspace, so a caller can read it after the stream has drained.
  * `part` selects the index set: 0 for plain heads; the query modality for
- * Q-boundary heads; 2*query_modality + key_modality for 2D-boundary heads.
+ * Q-boundary heads; 2*query_modality + key_modality for 2D-boundary heads;
+ * the segment index for Q-segment heads.
  * On success *offset_bytes and *count (elements) are set; a buffer that does
  * not exist for that head gives count 0.  Buffers: */
 enum {

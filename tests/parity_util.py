@@ -54,6 +54,10 @@ def gpu_scores(L, bh, cfg, segs, Lq):
         if cfg.layout == "plain":
             ov[("v", "all")] = L.view("v_scores", bh, 0).cpu().numpy()
             ov[("s", "all")] = L.view("s_scores", bh, 0).cpu().numpy()
+        elif cfg.layout == "q_segment":
+            for n_ in range(len(O._segments(Lq, segs))):
+                ov[("v", ("seg", n_))] = L.view("v_scores", bh, n_).cpu().numpy()
+                ov[("s", ("seg", n_))] = L.view("s_scores", bh, n_).cpu().numpy()
         elif cfg.layout == "q_boundary":
             for m in (TEXT, VIDEO):
                 if n[m]:
@@ -110,6 +114,8 @@ def check_head_indices(L, bh, cfg, qh, kh, segs, scale):
         for key, (V, S) in hi.vs.items():
             if cfg_o.layout == "plain":
                 part = 0
+            elif cfg_o.layout == "q_segment":
+                part = key[1]
             elif cfg_o.layout == "q_boundary":
                 part = key
             else:

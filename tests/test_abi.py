@@ -128,6 +128,8 @@ def test_descriptor_validation(L, mutate, code, needle):
     (dict(pattern="grid", stride_lo=64, stride_hi=2048), "grid needs"),
     (dict(pattern="grid", stride_lo=200, stride_hi=100), "grid needs"),
     (dict(pattern="parallel", layout="q_boundary", sink=4, window=64), "valid combination"),
+    (dict(pattern="block", layout="q_segment", k_blocks=4), "valid combination"),
+    (dict(pattern="grid", layout="q_segment"), "valid combination"),
     (dict(pattern="parallel", sink=-1, window=64), "parallel encoding"),
     (dict(pattern="parallel", sink=64, window=0), "parallel encoding"),
     (dict(pattern="parallel", sink=64, window=64, question=-3), "parallel encoding"),

@@ -54,7 +54,7 @@ def rows_for(spec, h, n_uniform, seed, extra=()):
     return np.array(sorted(r for r in rows if 0 <= r < L), np.int64)
 
 
-def run_config(i, n_uniform=10, n_tiles=2, extra_rows=(), whole_layer_check=None):
+def run_config(i, n_uniform=10, n_tiles=2, extra_rows=(), whole_layer_check=None, layouts=None):
     spec = synth.config(i)
     t0 = time.time()
     Lg, q, k, v, o, lse = run_gpu(spec)
@@ -69,6 +69,8 @@ def run_config(i, n_uniform=10, n_tiles=2, extra_rows=(), whole_layer_check=None
         assert 0 <= int(tp.sum().item()) <= causal
     rng = np.random.default_rng(i)
     for h in representative_heads(spec):
+        if layouts is not None and spec.heads[h].get("layout", "plain") not in layouts:
+            continue
         t1 = time.time()
         g = gmap[h]
         qh, kh, vh = f64(q[0, h]), f64(k[0, g]), f64(v[0, g])
@@ -153,3 +155,10 @@ def test_pevlm_video_101k():
             assert int(Lg.view("tile_pairs", h).sum().item()) == whole - upper, f"head {h}"
 
     run_config(6, extra_rows=edges, whole_layer_check=totals)
+
+
+@pytest.mark.timeout(600)
+def test_mixed_1m_segments():
+    # per-segment estimation on the 15-segment 1M layer: rows at every segment
+    # edge (run_config adds them) of the per-segment heads
+    run_config(7, n_uniform=6, n_tiles=1, layouts=("q_segment",))

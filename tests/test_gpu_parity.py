@@ -100,6 +100,28 @@ def test_edge_lengths(L):
     full_check(synth.small_spec("edge", L, 4, 4, 64, heads, seed=L))
 
 
+def segment_spec(d=128, seed=31):
+    # text and video segments of uneven, untiled lengths, one of them shorter
+    # than the 64 estimation rows
+    segs = [(0, 100, TEXT), (100, 49 * 9, VIDEO), (541, 37, TEXT), (578, 49 * 11, VIDEO), (1117, 130, TEXT)]
+    heads = [synth.vs(20, 40, "q_segment"), synth.vs(7, 90, "q_segment"), synth.vs(20, 40, "q_boundary"),
+             synth.vs(15, 30)]
+    return synth.small_spec("segment", 1247, 4, 2, d, heads, seed=seed, segs=segs, period=49, period_amp=3.0)
+
+
+def test_segment_layout():
+    full_check(segment_spec())
+
+
+def test_segment_layout_d64_materialized():
+    full_check(segment_spec(d=64, seed=32), materialize=True)
+
+
+def test_segment_layout_single_segment():
+    full_check(synth.small_spec("seg1", 333, 2, 1, 128, [synth.vs(10, 20, "q_segment"), synth.vs(10, 20)],
+                                seed=33, segs=[(0, 333, VIDEO)]))
+
+
 def test_parallel_encoding_ragged():
     # sink, context and question blocks off the 64-token tiles, a partial last
     # context block, a head with no sink or question, and 5-token blocks
