@@ -556,8 +556,12 @@ hipError_t launch_plan(const Dims& dm, const Tables& tb, char* ws, int max_tiles
     k_vs_shift<<<(unsigned)tb.n_heads, 256, (size_t)max_bm_words * 8, s>>>(tb, ws);
     k_plan<<<dim3(max_tiles, (unsigned)tb.n_heads), 256, (size_t)max_bm_words * 8, s>>>(dm, tb, ws);
     k_queue_enum<<<dim3((max_tiles / 2 + 64) / 64, (unsigned)tb.n_heads), 64, 0, s>>>(dm, tb, ws);
-    k_queue_reset<<<1, 64, 0, s>>>(dm, ws);
   }
+  return hipGetLastError();
+}
+
+hipError_t launch_queue_reset(const Dims& dm, char* ws, hipStream_t s) {
+  k_queue_reset<<<1, 64, 0, s>>>(dm, ws);
   return hipGetLastError();
 }
 

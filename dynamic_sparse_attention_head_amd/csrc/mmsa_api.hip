@@ -1033,6 +1033,8 @@ mmsa_status mmsa_sparse_prefill(const mmsa_layer_desc* desc, const void* q, cons
   int dev = 0, n_cu = 0;
   MMSA_HIP(hipGetDevice(&dev), "hipGetDevice");
   MMSA_HIP(hipDeviceGetAttribute(&n_cu, hipDeviceAttributeMultiprocessorCount, dev), "CU count");
+  // the pop counters start at zero on every call, so the call can be repeated
+  MMSA_HIP(launch_queue_reset(Lo.dm, (char*)ws, s), "queue reset");
   // two resident workgroups per CU (the kernel's LDS and register budget)
   MMSA_HIP(launch_attention(Lo.dm, Lo.tb, (char*)ws, q, k, v, o, lse, 2 * std::max(n_cu, 1), s), "attention");
   return MMSA_OK;

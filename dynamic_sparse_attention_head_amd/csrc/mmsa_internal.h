@@ -203,6 +203,7 @@ hipError_t launch_gather(const Dims& dm, const Tables& tb, char* ws, const void*
 hipError_t launch_plan(const Dims& dm, const Tables& tb, char* ws, int max_tiles, int max_bm_words,
                        hipStream_t s);
 
+hipError_t launch_queue_reset(const Dims& dm, char* ws, hipStream_t s);
 hipError_t launch_attention(const Dims& dm, const Tables& tb, char* ws, const void* q, const void* k,
                             const void* v, void* o, float* lse, int n_workgroups, hipStream_t s);
 hipError_t launch_unpermute(const Dims& dm, const Tables& tb, char* ws, void* o, int max_slots, hipStream_t s);

@@ -208,7 +208,9 @@ mmsa_status mmsa_permute(const mmsa_layer_desc* desc, const void* q, const void*
  *    (with MMSA_FLAG_MATERIALIZE only the rows of heads whose row order is the
  *    identity; the others go to the workspace until mmsa_unpermute).  lse: device
  *    float [B,Hq,L] (contiguous) or NULL; natural-log sum of exp of the scaled
- *    logits over the selected keys, -inf for a row with none. */
+ *    logits over the selected keys, -inf for a row with none.  The call resets
+ *    its own work queue, so it may be repeated on the plan the last
+ *    mmsa_permute built (for example to time it, or into another o). */
 mmsa_status mmsa_sparse_prefill(const mmsa_layer_desc* desc, const void* q, const void* k,
                                 const void* v, void* ws, size_t ws_bytes, void* o, float* lse,
                                 void* stream);

@@ -148,6 +148,19 @@ def test_parallel_encoding_video_layer_shortened():
     full_check(synth.config(6, L=3000), rows_per_head=300)
 
 
+def test_sparse_prefill_can_be_repeated_on_one_plan():
+    # the attention call resets its own work queue: a second call on the same
+    # plan writes the same output bits into a fresh buffer
+    spec = synth.config(1)
+    L, q, k, v, o, lse = run_gpu(spec)
+    o2 = torch.full_like(o, float("nan"))
+    lse2 = torch.full_like(lse, float("nan"))
+    L.sparse_prefill(q, k, v, o2, lse2)
+    torch.cuda.synchronize()
+    assert torch.equal(o.view(torch.int16), o2.view(torch.int16))
+    assert torch.equal(lse.view(torch.int32), lse2.view(torch.int32))
+
+
 def test_empty_layer_is_noop():
     spec = synth.small_spec("empty", 0, 2, 1, 128, [synth.vs(3, 5), synth.ashape(4, 8)], seed=0)
     q = torch.empty((1, 2, 0, 128), dtype=torch.bfloat16, device="cuda")
