@@ -9,7 +9,8 @@
 // Row orders:  grid heads put their line rows first (x mod stride in the kept
 // phases), then the other rows, each group ascending and padded to 64;
 // boundary heads use the modality-grouped order (text, then video, each
-// ascending and padded to 256).  Grid key lines are the same positions, so the
+// ascending and padded to 256); per-segment heads the segment-grouped order
+// (every segment ascending and padded to 64, in segment order).  Grid key lines are the same positions, so the
 // first rows of a grid head's row order are also its gathered key list.
 //
 // The plan of one query tile is a bitmap over the 64-key tiles of the head's
