@@ -183,6 +183,17 @@ mmsa_status build_layout(const mmsa_layer_desc* desc, Layout& Lo) {
       return MMSA_INVALID_ARGUMENT;
     }
   }
+  // The attention kernel copies K and V rows through buffer views of one
+  // (batch, KV head) slice with 32-bit offsets, and uses offset 2^31 as "past
+  // the slice" for key slots without a token: every slice must stay below 2 GiB.
+  for (int i = 1; i <= 2; ++i) {
+    const int64_t slice = D.L > 0 ? (int64_t)(D.L - 1) * st[i][2] * 2 + 2ll * D.d : 0;
+    if (slice >= (1ll << 31)) {
+      set_err("one (batch, KV head) slice of %s spans %lld bytes (L=%d, row stride %lld); the limit is 2 GiB", nm[i],
+              (long long)slice, D.L, (long long)st[i][2]);
+      return MMSA_UNSUPPORTED;
+    }
+  }
   // heads
   Lo.kvmap.assign(D.Hq, 0);
   if (D.Hq > 0) {

@@ -124,7 +124,9 @@ typedef struct {
 typedef struct {
   int32_t B, Hq, Hkv, L, d;
   int32_t _pad0;
-  int64_t q_strides[3], k_strides[3], v_strides[3], o_strides[3]; /* elements: batch, head, row */
+  int64_t q_strides[3], k_strides[3], v_strides[3], o_strides[3]; /* elements: batch, head, row;
+                                       (L-1) * k/v row stride * 2 + 2d must stay below 2 GiB
+                                       (MMSA_UNSUPPORTED otherwise)                     */
   float scale;                      /* softmax scale; 0 -> 1/sqrt(d)                 */
   uint32_t flags;                   /* 0 or MMSA_FLAG_MATERIALIZE                    */
   const int32_t* kv_head_of;        /* host [Hq] or NULL -> h / (Hq / Hkv)           */

@@ -104,6 +104,8 @@ def last_error():
     (lambda D: setattr(D, "scale", -1.0), INVALID, "scale"),
     (lambda D: D.q_strides.__setitem__(2, 100), INVALID, "strides"),
     (lambda D: D.k_strides.__setitem__(2, 64), INVALID, "strides"),
+    (lambda D: D.k_strides.__setitem__(2, 1 << 19), UNSUPPORTED, "2 GiB"),
+    (lambda D: D.v_strides.__setitem__(2, 1 << 19), UNSUPPORTED, "2 GiB"),
     (lambda D: setattr(D, "heads", None), INVALID, "heads is NULL"),
 ])
 def test_descriptor_validation(L, mutate, code, needle):
