@@ -48,44 +48,55 @@ __global__ __launch_bounds__(256) void k_pool(Dims dm, Tables tb, char* ws, cons
 }
 
 // Lower-triangle 64x64 tiles of z.  grid (tiles, block heads), block 256.
+// The pooled rows pass through LDS 32 dims at a time, stored d-major, so for
+// each d a thread reads its 4 query values and its 4 key values as one
+// 16-byte read each (2 LDS reads per 16 FMAs) and 16 KB of LDS lets many
+// workgroups share a CU; every output still sums over d in order.
 template <int D>
 __global__ __launch_bounds__(256) void k_block_logits(Dims dm, Tables tb, char* ws, int nB) {
+  constexpr int DC = 32;   // dims staged at a time
   const BlockTask T = wsp<const BlockTask>(ws, tb.off_block)[blockIdx.y];
   const int r = blockIdx.x;
   int bt = (int)((sqrtf(8.f * r + 1.f) - 1.f) * 0.5f);
   while ((bt + 1) * (bt + 2) / 2 <= r) ++bt;
   while (bt * (bt + 1) / 2 > r) --bt;
   const int ct = r - bt * (bt + 1) / 2;
-  __shared__ float Qs[64][D + 1];
-  __shared__ float Ks[64][D + 1];
+  __shared__ float4 Qs[DC][16];   // Qs[d][i] = pooled Q of rows 4i..4i+3 at dim d0 + d
+  __shared__ float4 Ks[DC][16];
   const float* qp = wsp<const float>(ws, T.ws_qp);
   const float* kp = wsp<const float>(ws, T.ws_kp);
   const int tid = threadIdx.x;
-  for (int i = tid; i < 64 * D / 4; i += 256) {   // 16 bytes a thread
-    const int rr = i / (D / 4), cc = 4 * (i % (D / 4));
-    const int bq = 64 * bt + rr, bk = 64 * ct + rr;
-    const float4 a = bq < nB ? *reinterpret_cast<const float4*>(qp + (int64_t)bq * D + cc) : make_float4(0.f, 0.f, 0.f, 0.f);
-    const float4 c = bk < nB ? *reinterpret_cast<const float4*>(kp + (int64_t)bk * D + cc) : make_float4(0.f, 0.f, 0.f, 0.f);
-    Qs[rr][cc] = a.x, Qs[rr][cc + 1] = a.y, Qs[rr][cc + 2] = a.z, Qs[rr][cc + 3] = a.w;
-    Ks[rr][cc] = c.x, Ks[rr][cc + 1] = c.y, Ks[rr][cc + 2] = c.z, Ks[rr][cc + 3] = c.w;
-  }
-  __syncthreads();
+  // this thread's staging element: row rr, dims cc..cc+3 of each 32-dim chunk
+  const int rr = tid % 64, cc = 4 * (tid / 64);   // 64 rows x 4 groups of 4 dims: 16 dims a pass
+  const int bq = 64 * bt + rr, bk = 64 * ct + rr;
   const int ty = tid >> 4, tx = tid & 15;
   float acc[4][4];
 #pragma unroll
   for (int i = 0; i < 4; ++i)
 #pragma unroll
     for (int j = 0; j < 4; ++j) acc[i][j] = 0.f;
-  for (int d = 0; d < D; ++d) {
-    float a[4], bv[4];
+  float* qs = reinterpret_cast<float*>(&Qs[0][0]);
+  float* ks = reinterpret_cast<float*>(&Ks[0][0]);
+  for (int d0 = 0; d0 < D; d0 += DC) {
 #pragma unroll
-    for (int i = 0; i < 4; ++i) a[i] = Qs[4 * ty + i][d];
+    for (int h = 0; h < DC / 16; ++h) {   // 256 threads x 4 dims = 16 dims of 64 rows per pass
+      const int c = cc + 16 * h;
+      const float4 a = bq < nB ? *reinterpret_cast<const float4*>(qp + (int64_t)bq * D + d0 + c) : make_float4(0.f, 0.f, 0.f, 0.f);
+      const float4 e = bk < nB ? *reinterpret_cast<const float4*>(kp + (int64_t)bk * D + d0 + c) : make_float4(0.f, 0.f, 0.f, 0.f);
+      qs[(c + 0) * 64 + rr] = a.x, qs[(c + 1) * 64 + rr] = a.y, qs[(c + 2) * 64 + rr] = a.z, qs[(c + 3) * 64 + rr] = a.w;
+      ks[(c + 0) * 64 + rr] = e.x, ks[(c + 1) * 64 + rr] = e.y, ks[(c + 2) * 64 + rr] = e.z, ks[(c + 3) * 64 + rr] = e.w;
+    }
+    __syncthreads();
+#pragma unroll 8
+    for (int d = 0; d < DC; ++d) {
+      const float4 a4 = Qs[d][ty], b4 = Ks[d][tx];
+      const float a[4] = {a4.x, a4.y, a4.z, a4.w}, bv[4] = {b4.x, b4.y, b4.z, b4.w};
 #pragma unroll
-    for (int j = 0; j < 4; ++j) bv[j] = Ks[4 * tx + j][d];
+      for (int i = 0; i < 4; ++i)
 #pragma unroll
-    for (int i = 0; i < 4; ++i)
-#pragma unroll
-      for (int j = 0; j < 4; ++j) acc[i][j] = fmaf(a[i], bv[j], acc[i][j]);
+        for (int j = 0; j < 4; ++j) acc[i][j] = fmaf(a[i], bv[j], acc[i][j]);
+    }
+    __syncthreads();
   }
   float* z = wsp<float>(ws, T.ws_z);
 #pragma unroll
