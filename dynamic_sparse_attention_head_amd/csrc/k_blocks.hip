@@ -157,21 +157,29 @@ __global__ __launch_bounds__(256) void k_block_topk(Tables tb, char* ws, int nB)
     pref = 0;
     krem = (uint32_t)n;
   }
+  // Emit: every key above the threshold, and the first `need` keys equal to
+  // it in index order.  Each thread takes a contiguous run of the row, so
+  // thread order is index order and two scans place every output.
   const uint32_t thr = pref;
   const int need = (int)krem;
-  int base = 0, eqb = 0;
-  for (int s0 = 0; s0 < n; s0 += 256) {
-    const int i = s0 + tid;
-    const bool in = i < n;
-    const uint32_t key = in ? order_key(zs[i]) : 0u;
-    const bool eq = in && key == thr, gt = in && key > thr;
-    int eq_tot, sel_tot;
-    const int eq_rank = eqb + block_excl_count(eq, red, &eq_tot);
-    const bool sel = gt || (eq && eq_rank < need);
-    const int r = base + block_excl_count(sel, red, &sel_tot);
-    if (sel) out[r] = i;
-    base += sel_tot;
-    eqb += eq_tot;
+  const int per = (n + 255) / 256;
+  const int i0 = min(n, tid * per), i1 = min(n, i0 + per);
+  int n_eq = 0, n_gt = 0;
+  for (int i = i0; i < i1; ++i) {
+    const uint32_t key = order_key(zs[i]);
+    n_eq += key == thr ? 1 : 0;
+    n_gt += key > thr ? 1 : 0;
+  }
+  int eq_tot, sel_tot;
+  const int eq_before = block_excl_sum(n_eq, red, &eq_tot);
+  const int take_eq = max(0, min(n_eq, need - eq_before));
+  int pos = block_excl_sum(n_gt + take_eq, red, &sel_tot);
+  int eq_seen = 0;
+  for (int i = i0; i < i1; ++i) {
+    const uint32_t key = order_key(zs[i]);
+    bool sel = key > thr;
+    if (key == thr) sel = eq_seen++ < take_eq;
+    if (sel) out[pos++] = i;
   }
 }
 

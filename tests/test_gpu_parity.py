@@ -161,6 +161,29 @@ def test_sparse_prefill_can_be_repeated_on_one_plan():
     assert torch.equal(lse.view(torch.int32), lse2.view(torch.int32))
 
 
+def test_block_topk_breaks_exact_ties_to_the_lower_block():
+    # key blocks 3, 5, 8, 9, 12 are copies of block 1, so their pooled logits
+    # tie exactly with block 1's in every row: the selection must keep the
+    # lower block indices among equal logits
+    import math
+    import oracle.mmsa_oracle as O
+    from parity_util import check_attention, check_head_indices, f64
+    spec = synth.small_spec("ties", 64 * 16, 2, 1, 128, [synth.block(4), synth.block(7)], seed=41)
+    lay = synth.make_layer(spec, "cuda")
+    q, k, v = lay["q"], lay["k"].clone(), lay["v"]
+    for c in (3, 5, 8, 9, 12):
+        k[0, 0, 64 * c:64 * c + 64] = k[0, 0, 64:128]
+    L, q, k, v, o, lse = run_gpu(spec, q=q, k=k, v=v)
+    scale = 1.0 / math.sqrt(spec.d)
+    qn, kn, vn, on = f64(q[0]), f64(k[0]), f64(v[0]), f64(o[0])
+    ln = lse[0].cpu().numpy().astype(np.float64)
+    for h in range(spec.Hq):
+        z = L.view("block_scores", h).cpu().numpy().reshape(16, 16)
+        assert (z[12:, [1, 3, 5, 8, 9, 12]] == z[12:, [1]]).all()   # the ties are exact
+        hi = check_head_indices(L, h, spec.heads[h], qn[h], kn[0], spec.segs, scale)
+        check_attention(hi, qn[h], kn[0], vn[0], on[h], ln[h], scale, np.arange(spec.L), name=f"ties head {h}")
+
+
 def test_empty_layer_is_noop():
     spec = synth.small_spec("empty", 0, 2, 1, 128, [synth.vs(3, 5), synth.ashape(4, 8)], seed=0)
     q = torch.empty((1, 2, 0, 128), dtype=torch.bfloat16, device="cuda")
