@@ -119,7 +119,7 @@ __global__ __launch_bounds__(256) void k_block_topk(Tables tb, char* ws, int nB)
   const BlockTask T = wsp<const BlockTask>(ws, tb.off_block)[blockIdx.y];
   extern __shared__ float zs[];
   __shared__ uint32_t hist[4][256];
-  __shared__ uint32_t sh_pref, sh_krem;
+  __shared__ uint32_t sh_pref, sh_krem, sh_all;
   __shared__ int red[17];
   const int b = blockIdx.x, tid = threadIdx.x, wv = tid >> 6;
   const int n = b + 1;
@@ -146,27 +146,33 @@ __global__ __launch_bounds__(256) void k_block_topk(Tables tb, char* ws, int nB)
       if (above < krem && above + c >= krem) {
         sh_pref = pref | ((uint32_t)(255 - tid) << shift);
         sh_krem = krem - above;
+        sh_all = (above + c == krem) ? 1u : 0u;   // the whole bin is taken
       }
       __syncthreads();
       pref = sh_pref;
       krem = sh_krem;
       pmask |= 255u << shift;
+      const bool done = sh_all != 0u;
       __syncthreads();
+      // every key of the threshold bin is selected: the lower bits decide nothing
+      if (done) break;
     }
   } else {
     pref = 0;
     krem = (uint32_t)n;
   }
   // Emit: every key above the threshold, and the first `need` keys equal to
-  // it in index order.  Each thread takes a contiguous run of the row, so
-  // thread order is index order and two scans place every output.
+  // it in index order, comparing the bits the rounds decided (all of them
+  // unless a round took its whole threshold bin).  Each thread takes a
+  // contiguous run of the row, so thread order is index order and two scans
+  // place every output.
   const uint32_t thr = pref;
   const int need = (int)krem;
   const int per = (n + 255) / 256;
   const int i0 = min(n, tid * per), i1 = min(n, i0 + per);
   int n_eq = 0, n_gt = 0;
   for (int i = i0; i < i1; ++i) {
-    const uint32_t key = order_key(zs[i]);
+    const uint32_t key = order_key(zs[i]) & pmask;
     n_eq += key == thr ? 1 : 0;
     n_gt += key > thr ? 1 : 0;
   }
@@ -176,7 +182,7 @@ __global__ __launch_bounds__(256) void k_block_topk(Tables tb, char* ws, int nB)
   int pos = block_excl_sum(n_gt + take_eq, red, &sel_tot);
   int eq_seen = 0;
   for (int i = i0; i < i1; ++i) {
-    const uint32_t key = order_key(zs[i]);
+    const uint32_t key = order_key(zs[i]) & pmask;
     bool sel = key > thr;
     if (key == thr) sel = eq_seen++ < take_eq;
     if (sel) out[pos++] = i;
