@@ -171,7 +171,9 @@ __global__ __launch_bounds__(256) void k_est_pass2(Dims dm, Tables tb, char* ws,
   const int tid = threadIdx.x, w = tid >> 6, lane = tid & 63, qc = lane & 15, g4 = lane >> 4;
 
   __shared__ int kp_s[EST_CK];
-  __shared__ float P[EST_ROWS][EST_CK + 4];
+  // one half of the estimation rows at a time (34 KB of LDS instead of 68)
+  constexpr int HR = EST_ROWS / 2;
+  __shared__ float P[HR][EST_CK + 4];
   {
     const int slot = x0 + tid;
     int pos;
@@ -209,94 +211,104 @@ __global__ __launch_bounds__(256) void k_est_pass2(Dims dm, Tables tb, char* ws,
     for (int qb = 0; qb < 4; ++qb) posv[qb] = (16 * qb + qc < J.n_rows) ? J.rows[16 * qb + qc] : -1;
     bf16x8 qfb[2][D / 32];
     load_q_frag<D>(qfb[0], q + J.q_off, dm.q_sl, posv[0], lane);
+    const bool slash = J.kind == JOB_VS_ORIG || J.kind == JOB_VS_2D;
+    const int kpos_mine = kp_s[tid];
+    float colsum = 0.f;
 #pragma unroll
-    for (int qb = 0; qb < 4; ++qb) {
-      const int row = 16 * qb + qc;
-      const bool rv = row < J.n_rows;
-      const int pos = posv[qb];
-      const float2 st = stats[row];
-      const float inv_l = (rv && st.y > 0.f) ? 1.0f / st.y : 0.f;
-      if (qb + 1 < 4) load_q_frag<D>(qfb[(qb + 1) & 1], q + J.q_off, dm.q_sl, posv[qb + 1], lane);
-      const bf16x8 (&qf)[D / 32] = qfb[qb & 1];
+    for (int half = 0; half < 2; ++half) {
 #pragma unroll
-      for (int kb = 0; kb < 4; ++kb) {
-        floatx4 acc = {0.f, 0.f, 0.f, 0.f};
+      for (int qh = 0; qh < 2; ++qh) {
+        const int qb = 2 * half + qh;
+        const int row = 16 * qb + qc;
+        const bool rv = row < J.n_rows;
+        const int pos = posv[qb];
+        const float2 st = stats[row];
+        const float inv_l = (rv && st.y > 0.f) ? 1.0f / st.y : 0.f;
+        if (qb + 1 < 4) load_q_frag<D>(qfb[(qb + 1) & 1], q + J.q_off, dm.q_sl, posv[qb + 1], lane);
+        const bf16x8 (&qf)[D / 32] = qfb[qb & 1];
 #pragma unroll
-        for (int c = 0; c < D / 32; ++c) acc = mfma16(kf[kb][c], qf[c], acc);
-        const int4 kq = *reinterpret_cast<const int4*>(&kp_s[64 * w + 16 * kb + 4 * g4]);
-        const int kk[4] = {kq.x, kq.y, kq.z, kq.w};
-        float4 pv;
-        float* pp = reinterpret_cast<float*>(&pv);
+        for (int kb = 0; kb < 4; ++kb) {
+          floatx4 acc = {0.f, 0.f, 0.f, 0.f};
 #pragma unroll
-        for (int i = 0; i < 4; ++i) {
-          const bool valid = rv && kk[i] >= 0 && kk[i] <= pos;
-          pp[i] = valid ? __builtin_amdgcn_exp2f(acc[i] * dm.scale_log2 - st.x) * inv_l : 0.f;
+          for (int c = 0; c < D / 32; ++c) acc = mfma16(kf[kb][c], qf[c], acc);
+          const int4 kq = *reinterpret_cast<const int4*>(&kp_s[64 * w + 16 * kb + 4 * g4]);
+          const int kk[4] = {kq.x, kq.y, kq.z, kq.w};
+          float4 pv;
+          float* pp = reinterpret_cast<float*>(&pv);
+#pragma unroll
+          for (int i = 0; i < 4; ++i) {
+            const bool valid = rv && kk[i] >= 0 && kk[i] <= pos;
+            pp[i] = valid ? __builtin_amdgcn_exp2f(acc[i] * dm.scale_log2 - st.x) * inv_l : 0.f;
+          }
+          *reinterpret_cast<float4*>(&P[row - HR * half][64 * w + 16 * kb + 4 * g4]) = pv;
         }
-        *reinterpret_cast<float4*>(&P[row][64 * w + 16 * kb + 4 * g4]) = pv;
       }
-    }
-    __syncthreads();
+      __syncthreads();
 
-    // column sums -> vertical scores (or grid line scores)
-    {
-      const int kpos = kp_s[tid];
-      if (kpos >= 0 && kpos <= J.imax) {
-        // rows past n_rows hold zeros (written as invalid above), so a fixed
-        // 64-row sum with independent partials lets the LDS reads overlap
+      // column sums of this half (rows past n_rows hold zeros); a fixed loop
+      // with independent partials lets the LDS reads overlap
+      if (kpos_mine >= 0 && kpos_mine <= J.imax) {
         float part[8] = {0.f, 0.f, 0.f, 0.f, 0.f, 0.f, 0.f, 0.f};
 #pragma unroll
-        for (int r = 0; r < EST_ROWS; ++r) part[r & 7] += P[r][tid];
-        const float sum = ((part[0] + part[1]) + (part[2] + part[3])) + ((part[4] + part[5]) + (part[6] + part[7]));
-        const int slot = x0 + tid;
-        if (J.kind == JOB_VS_ORIG || J.kind == JOB_GRID_PLAIN) {
-          wsp<float>(ws, J.pair[0].ws_v)[kpos] = sum;
-        } else if (J.kind == JOB_GRID_GROUPED) {
-          const int xg = (slot < dm.video_base) ? slot : dm.n_text + (slot - dm.video_base);
-          wsp<float>(ws, J.pair[0].ws_v)[xg] = sum;
-        } else {
-          const int pi = (J.pair[0].m_k == m_chunk) ? 0 : 1;
-          wsp<float>(ws, J.pair[pi].ws_v)[slot - chunk_base] = sum;
-        }
+        for (int r = 0; r < HR; ++r) part[r & 7] += P[r][tid];
+        colsum += ((part[0] + part[1]) + (part[2] + part[3])) + ((part[4] + part[5]) + (part[6] + part[7]));
       }
-    }
-    // diagonal sums -> slash scores
-    if (J.kind == JOB_VS_ORIG || J.kind == JOB_VS_2D) {
-      const int pi = (J.kind == JOB_VS_2D && J.pair[0].m_k != m_chunk) ? 1 : 0;
-      const PairDev& Pd = J.pair[pi];
-      unsigned long long* sacc = wsp<unsigned long long>(ws, Pd.ws_sacc);
-      const int n_runs = (J.kind == JOB_VS_2D) ? 1 : J.n_runs;
-      for (int ru = 0; ru < n_runs; ++ru) {
-        int r0, len, A;
-        if (J.kind == JOB_VS_2D) {
-          r0 = 0;
-          len = J.n_rows;
-          A = J.rho0 + Pd.n_k - 1 - (x0 - chunk_base);
-        } else {
-          r0 = J.run_r0[ru];
-          len = J.run_len[ru];
-          A = J.rows[r0] - r0 - x0;
-        }
-        const int span = len + EST_CK - 1;
-        const int idx_lo = A + r0 - (EST_CK - 1);
-        for (int ii = tid; ii < span; ii += 256) {
-          const int idx = idx_lo + ii;
-          if (idx < 0 || idx >= Pd.Ds) continue;
-          const int rlo = max(r0, idx - A), rhi = min(r0 + len, idx - A + EST_CK);
-          // fixed 64-row loop, independent partials: the LDS reads overlap
-          float part[8] = {0.f, 0.f, 0.f, 0.f, 0.f, 0.f, 0.f, 0.f};
-#pragma unroll
-          for (int r = 0; r < EST_ROWS; ++r) {
-            const bool in = (r >= rlo) & (r < rhi);
-            const int c = in ? A + r - idx : 0;
-            const float x = P[r][c];
-            part[r & 7] += in ? x : 0.f;
+      // diagonal sums of this half -> slash accumulators (fixed point, so the
+      // result does not depend on the order of the additions)
+      if (slash) {
+        const int pi = (J.kind == JOB_VS_2D && J.pair[0].m_k != m_chunk) ? 1 : 0;
+        const PairDev& Pd = J.pair[pi];
+        unsigned long long* sacc = wsp<unsigned long long>(ws, Pd.ws_sacc);
+        const int n_runs = (J.kind == JOB_VS_2D) ? 1 : J.n_runs;
+        const int h0 = HR * half;
+        for (int ru = 0; ru < n_runs; ++ru) {
+          int r0, len, A;
+          if (J.kind == JOB_VS_2D) {
+            r0 = 0;
+            len = J.n_rows;
+            A = J.rho0 + Pd.n_k - 1 - (x0 - chunk_base);
+          } else {
+            r0 = J.run_r0[ru];
+            len = J.run_len[ru];
+            A = J.rows[r0] - r0 - x0;
           }
-          const float sum = ((part[0] + part[1]) + (part[2] + part[3])) + ((part[4] + part[5]) + (part[6] + part[7]));
-          if (sum != 0.f) atomicAdd(&sacc[idx], (unsigned long long)llrint((double)sum * SFIX));
+          if (r0 >= h0 + HR || r0 + len <= h0) continue;   // run outside this half (uniform)
+          const int span = len + EST_CK - 1;
+          const int idx_lo = A + r0 - (EST_CK - 1);
+          for (int ii = tid; ii < span; ii += 256) {
+            const int idx = idx_lo + ii;
+            if (idx < 0 || idx >= Pd.Ds) continue;
+            const int rlo = max(max(r0, idx - A), h0), rhi = min(min(r0 + len, idx - A + EST_CK), h0 + HR);
+            float part[8] = {0.f, 0.f, 0.f, 0.f, 0.f, 0.f, 0.f, 0.f};
+#pragma unroll
+            for (int rl = 0; rl < HR; ++rl) {
+              const int r = h0 + rl;
+              const bool in = (r >= rlo) & (r < rhi);
+              const int c = in ? A + r - idx : 0;
+              const float x = P[rl][c];
+              part[rl & 7] += in ? x : 0.f;
+            }
+            const float sum = ((part[0] + part[1]) + (part[2] + part[3])) + ((part[4] + part[5]) + (part[6] + part[7]));
+            if (sum != 0.f) atomicAdd(&sacc[idx], (unsigned long long)llrint((double)sum * SFIX));
+          }
         }
       }
+      __syncthreads();
     }
-    __syncthreads();
+
+    // column sums -> vertical scores (or grid line scores)
+    if (kpos_mine >= 0 && kpos_mine <= J.imax) {
+      const int slot = x0 + tid;
+      if (J.kind == JOB_VS_ORIG || J.kind == JOB_GRID_PLAIN) {
+        wsp<float>(ws, J.pair[0].ws_v)[kpos_mine] = colsum;
+      } else if (J.kind == JOB_GRID_GROUPED) {
+        const int xg = (slot < dm.video_base) ? slot : dm.n_text + (slot - dm.video_base);
+        wsp<float>(ws, J.pair[0].ws_v)[xg] = colsum;
+      } else {
+        const int pi = (J.pair[0].m_k == m_chunk) ? 0 : 1;
+        wsp<float>(ws, J.pair[pi].ws_v)[slot - chunk_base] = colsum;
+      }
+    }
   }
 }
 
