@@ -22,9 +22,8 @@
 // and P.V run, S^T of chunk n+1 is computed (its MFMAs interleaved with the
 // softmax arithmetic), and the copies of K for chunk n+2 and V for chunk n+1
 // are in flight.  Masking is element-wise on original positions (causal,
-// A-shape window, parallel-encoding blocks) and runs only for chunks whose
-// keys may follow the wave's first row, and for every chunk of those two
-// row-dependent patterns.  The running max moves only when a row's max grows by more than
+// A-shape window, parallel-encoding blocks) and runs only for chunks holding
+// a key that some row of the wave does not see.  The running max moves only when a row's max grows by more than
 // 2^LAZY, so rescales of O are rare.
 #include "mmsa_device.h"
 
