@@ -153,6 +153,28 @@ def test_segment_validation(L, segs):
     assert ws_status(lay) == INVALID
 
 
+def test_segment_parts_span_every_segment(L):
+    """A per-segment head has one index set per segment (more than the four
+    parts other layouts use): each covers the causal keys up to its segment's
+    end with the last min(64, len) rows, and the part after the last is rejected."""
+    segs = [(0, 700, 0), (700, 30, 1), (730, 900, 0), (1630, 64, 1), (1694, 1200, 0), (2894, 1202, 1)]
+    lay = host_layer([synth.vs(40, 100, layout="q_segment")], segs=segs)
+    n, spans = lay.workspace_bytes(), []
+    for part, (s0, ln, _) in enumerate(segs):
+        m = lay.meta(0, part)
+        assert m[:4] == [0, s0 + ln, 0, s0 + ln]
+        assert m[4:8] == [min(40, s0 + ln), min(100, s0 + ln), 0, min(64, ln)]
+        off, cnt = lay.view_offset("v_index", 0, part)
+        assert cnt == min(40, s0 + ln) and off % 4 == 0 and off + 4 * cnt <= n
+        spans.append((off, off + 4 * cnt))
+    spans.sort()
+    assert all(a[1] <= b[0] for a, b in zip(spans, spans[1:]))    # disjoint index sets
+    with pytest.raises(mmsa.MMSAError):
+        lay.meta(0, len(segs))
+    with pytest.raises(mmsa.MMSAError):
+        lay.view_offset("v_index", 0, len(segs))
+
+
 def test_kv_head_map_validation(L):
     lay = host_layer([synth.vs(1, 2)] * 3, Hkv=2, kv_head_of=[0, 1, 2])
     assert ws_status(lay) == INVALID and "kv_head_of" in last_error()
