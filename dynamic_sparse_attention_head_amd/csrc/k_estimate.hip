@@ -9,11 +9,15 @@
 // The attention of the estimation rows is exact: pass 1 streams K once for the
 // row max and the sum of exponentials, pass 2 streams K again and forms the
 // normalised probabilities, their column sums (vertical scores) and their
-// diagonal sums (slash scores).  Each workgroup takes 256 keys and every
-// estimation region of its KV head, so K is read twice in total.  QK^T uses
-// bf16 MFMA with fp32 accumulation.  Diagonal sums cross workgroups; they are
-// added as 2^-40 fixed-point integers, so the result does not depend on the
-// order in which workgroups finish.
+// diagonal sums (slash scores).  Pass 1 workgroups stream key chunks of one
+// KV head against up to four regions whose rows sit in LDS; a pass 2
+// workgroup takes 256 keys and every region of its KV head.  Either way K is
+// read about twice in total.  QK^T uses bf16 MFMA with fp32 accumulation.
+// Diagonal sums cross workgroups; they are added as 2^-40 fixed-point
+// integers, so the result does not depend on the order in which workgroups
+// finish.
+#include <type_traits>
+
 #include "block_scan.h"
 
 namespace mmsa {
@@ -58,94 +62,192 @@ __device__ __forceinline__ void load_q_frag(bf16x8 (&qf)[D / 32], const bf16_t* 
   }
 }
 
+// Max and sum over the four 16-lane rows of a wave (lanes l, l^16, l^32,
+// l^48), in registers: v_permlane16_swap pairs rows 0-1 and 2-3, then
+// v_permlane32_swap pairs the halves.  Every lane receives the result, and
+// the pairs are combined symmetrically, so all four lanes agree bit for bit.
+__device__ __forceinline__ float max_rows4(float x) {
+  auto r = __builtin_amdgcn_permlane16_swap(__float_as_uint(x), __float_as_uint(x), false, false);
+  x = fmaxf(__uint_as_float(r[0]), __uint_as_float(r[1]));
+  r = __builtin_amdgcn_permlane32_swap(__float_as_uint(x), __float_as_uint(x), false, false);
+  return fmaxf(__uint_as_float(r[0]), __uint_as_float(r[1]));
+}
+__device__ __forceinline__ float sum_rows4(float x) {
+  auto r = __builtin_amdgcn_permlane16_swap(__float_as_uint(x), __float_as_uint(x), false, false);
+  x = __uint_as_float(r[0]) + __uint_as_float(r[1]);
+  r = __builtin_amdgcn_permlane32_swap(__float_as_uint(x), __float_as_uint(x), false, false);
+  return __uint_as_float(r[0]) + __uint_as_float(r[1]);
+}
+
+// Swizzle of the LDS copy of the estimation rows: physical 16-byte chunk =
+// logical ^ swz1(row), so the 16 rows one B-fragment read touches fall in 16
+// different bank groups (d = 128: 256-byte rows; d = 64: two 128-byte rows per
+// 256 bytes).
+template <int D>
+__device__ __forceinline__ int swz1(int r) {
+  return D == 128 ? (r & 15) : ((r >> 1) & 7);
+}
+
 // ---------------------------------------------------------------------------
-// Pass 1: partial (max, sum of exp2) of each estimation row over 256 keys.
-// grid (chunks of 256 keys, pass-1 groups), block 256 = 4 waves x 64 keys.
+// Pass 1: (max, sum of exp2) of each estimation row over its causal keys.
+// grid (workgroups per batch, job batches), block 256 = 4 waves.
+// A batch is at most EST1_JB jobs of one (b, KV head); their Q rows are
+// copied into LDS once, straight from memory (16 bytes a lane).  Workgroup x
+// of a batch takes the 256-key chunks x, x + gridDim.x, ...: each wave owns 64
+// keys of a chunk, held in registers while the next chunk's keys load into a
+// second register set, and keeps a running (max, sum) per row in LDS.  At the
+// end the workgroup merges its four waves into one partial per row.
 // ---------------------------------------------------------------------------
 template <int D>
-__global__ __launch_bounds__(256) void k_est_pass1(Dims dm, Tables tb, char* ws, const bf16_t* __restrict__ q,
-                                                   const bf16_t* __restrict__ k) {
+__global__ __launch_bounds__(256, 2) void k_est_pass1(Dims dm, Tables tb, char* ws, const bf16_t* __restrict__ q,
+                                                      const bf16_t* __restrict__ k) {
+  constexpr int NC = D / 32, CPR = D / 8, RPI = 64 / CPR, IPW = EST_ROWS / RPI / 4;
+  constexpr int QJ = EST_ROWS * D * 2;   // bytes of one job's rows of Q
+  __shared__ __attribute__((aligned(16))) char Qs[EST1_JB * QJ];
+  __shared__ int pos_s[EST1_JB][EST_ROWS];
+  __shared__ int minpos_s[EST1_JB];
+  __shared__ float2 st_s[EST1_JB][4][EST_ROWS];
   const EstGroup G = wsp<const EstGroup>(ws, tb.off_groups1)[blockIdx.y];
-  const EstJob* jobs = wsp<const EstJob>(ws, tb.off_jobs);
-  const int j0 = blockIdx.x * EST_CK;
-  const int tid = threadIdx.x, w = tid >> 6, lane = tid & 63, qc = lane & 15, g4 = lane >> 4;
+  const MMSA_CONST EstJob* jobs = cptr<EstJob>(ws, tb.off_jobs) + G.job_begin;
+  const int nj = min(G.job_end - G.job_begin, EST1_JB);
+  const int tid = threadIdx.x, lane = tid & 63, qc = lane & 15, g4 = lane >> 4;
+  const int w = __builtin_amdgcn_readfirstlane(tid >> 6);
   int gimax = -1;
-  for (int jb = G.job_begin; jb < G.job_end; ++jb) gimax = max(gimax, jobs[jb].imax);
-  if (j0 > gimax) return;   // no estimation row sees these keys (their partials are never read)
+  for (int jj = 0; jj < nj; ++jj) gimax = max(gimax, jobs[jj].imax);
+  const int n_ck = min((dm.L + EST_CK - 1) / EST_CK, gimax / EST_CK + 1);
 
-  int kp[4];
+  // ---- the batch's rows of Q into LDS; row positions; running stats ----
+  // Copy instruction i of a job fills rows i*RPI .. +RPI-1; lane l writes row
+  // i*RPI + l/CPR, physical chunk l%CPR, so it reads logical chunk
+  // (l%CPR) ^ swz1(row).  Rows past n_rows repeat the last row (never used).
+  for (int jj = 0; jj < nj; ++jj) {
+    const MMSA_CONST EstJob& J = jobs[jj];
+    if (tid < EST_ROWS) pos_s[jj][tid] = tid < J.n_rows ? J.rows[tid] : -1;
+    st_s[jj][w][lane] = make_float2(-INFINITY, 0.f);
+    const bf16_t* qh = q + J.q_off;
 #pragma unroll
-  for (int kb = 0; kb < 4; ++kb) {
-    int key = j0 + 64 * w + 16 * kb + qc;
-    kp[kb] = key < dm.L ? key : -1;
+    for (int p = 0; p < IPW; ++p) {
+      const int ins = w * IPW + p;
+      const int row = ins * RPI + lane / CPR;
+      const int lch = (lane % CPR) ^ swz1<D>(row);
+      const int pos = J.n_rows > 0 ? J.rows[min(row, J.n_rows - 1)] : 0;
+      __builtin_amdgcn_global_load_lds(qh + (int64_t)pos * dm.q_sl + 8 * lch,
+                                       (__attribute__((address_space(3))) void*)(Qs + jj * QJ + ins * 1024), 16, 0,
+                                       0);
+    }
   }
-  bf16x8 kf[4][D / 32];
-  load_k_frags<D>(kf, k + G.k_off, dm.k_sl, kp, lane);
+  __syncthreads();
+  // smallest row position of each job (-1 if it has padding rows): a wave's
+  // 64 keys all at or before it need no causal mask
+  if (tid < nj) {
+    int mn = pos_s[tid][0];
+    for (int r = 1; r < EST_ROWS; ++r) mn = min(mn, pos_s[tid][r]);
+    minpos_s[tid] = mn;
+  }
 
-  __shared__ float2 red[2][4][64];
-  int it = 0;
-  for (int jb = G.job_begin; jb < G.job_end; ++jb, ++it) {
-    const EstJob& J = jobs[jb];
-    const int par = it & 1;
-    // row positions of the 4 row groups, then Q one group ahead of its MFMAs
-    int posv[4];
+  // Keys past the end read the last row: they are masked, so their values never
+  // count, and the loads stay unconditional (the compiler then waits for the
+  // current chunk's loads only, not for the prefetch of the next).
+  const bf16_t* kh = k + G.k_off;
+  auto load_k = [&](bf16x8 (&kf)[4][NC], int c) {
 #pragma unroll
-    for (int qb = 0; qb < 4; ++qb) posv[qb] = (16 * qb + qc < J.n_rows) ? J.rows[16 * qb + qc] : -1;
-    bf16x8 qfb[2][D / 32];
-    load_q_frag<D>(qfb[0], q + J.q_off, dm.q_sl, posv[0], lane);
+    for (int kb = 0; kb < 4; ++kb) {
+      const int key = min(c * EST_CK + 64 * w + 16 * kb + qc, dm.L - 1);
+      const bf16_t* kr = kh + (int64_t)key * dm.k_sl + 8 * g4;
+#pragma unroll
+      for (int cc = 0; cc < NC; ++cc) kf[kb][cc] = as_bf16x8(ld16(kr + 32 * cc));
+    }
+  };
+  const float sl2 = dm.scale_log2;
+  // the 64 rows of one job against the wave's 64 keys (masked: causal mask on)
+  auto job = [&](const bf16x8 (&kf)[4][NC], int jj, int kbase, auto masked) {
+    const char* qt = Qs + jj * QJ;
 #pragma unroll
     for (int qb = 0; qb < 4; ++qb) {
       const int row = 16 * qb + qc;
-      const bool rv = row < J.n_rows;
-      const int pos = posv[qb];
-      if (qb + 1 < 4) load_q_frag<D>(qfb[(qb + 1) & 1], q + J.q_off, dm.q_sl, posv[qb + 1], lane);
-      const bf16x8 (&qf)[D / 32] = qfb[qb & 1];
-      float xs[16];
-      float mx = -INFINITY;
+      bf16x8 qf[NC];
+#pragma unroll
+      for (int cc = 0; cc < NC; ++cc)
+        qf[cc] = *reinterpret_cast<const bf16x8*>(qt + row * (2 * D) + 16 * ((4 * cc + g4) ^ swz1<D>(row)));
+      const float2 o = st_s[jj][w][row];
+      floatx4 acc[4];
 #pragma unroll
       for (int kb = 0; kb < 4; ++kb) {
-        floatx4 acc = {0.f, 0.f, 0.f, 0.f};
+        acc[kb] = floatx4{0.f, 0.f, 0.f, 0.f};
 #pragma unroll
-        for (int c = 0; c < D / 32; ++c) acc = mfma16(kf[kb][c], qf[c], acc);
-#pragma unroll
-        for (int i = 0; i < 4; ++i) {
-          const int key = j0 + 64 * w + 16 * kb + 4 * g4 + i;
-          const float x = (rv && key <= pos) ? acc[i] * dm.scale_log2 : -INFINITY;
-          xs[4 * kb + i] = x;
-          mx = fmaxf(mx, x);
-        }
+        for (int cc = 0; cc < NC; ++cc) acc[kb] = mfma16(kf[kb][cc], qf[cc], acc[kb]);
       }
+      if constexpr (decltype(masked)::value) {
+        const int pos = pos_s[jj][row];
+#pragma unroll
+        for (int kb = 0; kb < 4; ++kb)
+#pragma unroll
+          for (int i = 0; i < 4; ++i) acc[kb][i] = (kbase + 16 * kb + 4 * g4 + i <= pos) ? acc[kb][i] : -INFINITY;
+      }
+      float mx = -INFINITY;
+#pragma unroll
+      for (int kb = 0; kb < 4; ++kb) mx = fmaxf(mx, fmaxf(fmaxf(acc[kb][0], acc[kb][1]), fmaxf(acc[kb][2], acc[kb][3])));
+      mx = max_rows4(mx);
+      const float m_new = fmaxf(o.x, mx * sl2);
+      const float mu = m_new == -INFINITY ? 0.f : m_new;
       float sm = 0.f;
-      if (mx != -INFINITY) {
 #pragma unroll
-        for (int e = 0; e < 16; ++e) sm += __builtin_amdgcn_exp2f(xs[e] - mx);
-      }
-      float2 st = make_float2(mx, sm);
+      for (int kb = 0; kb < 4; ++kb)
 #pragma unroll
-      for (int m = 16; m <= 32; m <<= 1) {
-        float2 o = make_float2(shfl_xor_f(st.x, m), shfl_xor_f(st.y, m));
-        st = lse2_merge_hw(st, o);
-      }
-      if (g4 == 0) red[par][w][row] = st;
+        for (int i = 0; i < 4; ++i) sm += __builtin_amdgcn_exp2f(fmaf(acc[kb][i], sl2, -mu));
+      sm = sum_rows4(sm);
+      const float s_new = o.y * __builtin_amdgcn_exp2f(o.x - mu) + sm;
+      // the four lanes of a row hold the same values: all of them store (no branch)
+      st_s[jj][w][row] = make_float2(m_new, s_new);
     }
-    __syncthreads();
-    if (tid < 64) {
-      float2 st = red[par][0][tid];
-#pragma unroll
-      for (int ww = 1; ww < 4; ++ww) st = lse2_merge_hw(st, red[par][ww][tid]);
-      wsp<float2>(ws, J.ws_part)[(int64_t)blockIdx.x * 64 + tid] = st;
+  };
+  // one chunk: every job of the batch whose rows see some of the wave's keys
+  auto body = [&](const bf16x8 (&kf)[4][NC], int c) {
+    const int kbase = c * EST_CK + 64 * w;
+    for (int jj = 0; jj < nj; ++jj) {
+      if (kbase > jobs[jj].imax) continue;   // uniform
+      if (kbase + 63 <= __builtin_amdgcn_readfirstlane(minpos_s[jj]))
+        job(kf, jj, kbase, std::false_type{});
+      else
+        job(kf, jj, kbase, std::true_type{});
     }
+  };
+
+  // The next chunk's keys are loaded unconditionally (past the end: the last
+  // row again), so every path through the loop has the same loads in flight
+  // and the compiler's waits cover only the chunk being computed.
+  bf16x8 kA[4][NC], kB[4][NC];
+  int c = blockIdx.x;
+  load_k(kA, c);
+  asm volatile("s_waitcnt vmcnt(0)" ::: "memory");   // the copies of Q and the first keys
+  __syncthreads();
+  while (c < n_ck) {
+    load_k(kB, c + (int)gridDim.x);
+    body(kA, c);
+    c += gridDim.x;
+    if (c >= n_ck) break;
+    load_k(kA, c + (int)gridDim.x);
+    body(kB, c);
+    c += gridDim.x;
+  }
+  __syncthreads();
+  for (int t = tid; t < nj * EST_ROWS; t += 256) {
+    const int jj = t / EST_ROWS, r = t % EST_ROWS;
+    float2 st = st_s[jj][0][r];
+#pragma unroll
+    for (int ww = 1; ww < 4; ++ww) st = lse2_merge_hw(st, st_s[jj][ww][r]);
+    wsp<float2>(ws, jobs[jj].ws_part)[(int64_t)blockIdx.x * EST_ROWS + r] = st;
   }
 }
 
-// Final (max, sum) per estimation row: 16 waves each merge a contiguous range
-// of chunk partials (lane = row), then the 16 results are merged.
-__global__ __launch_bounds__(1024) void k_est_combine(Tables tb, char* ws) {
+// Final (max, sum) per estimation row from the n_part partials of its job
+// (one per pass-1 workgroup of its batch): 16 waves each merge a contiguous
+// range (lane = row), then the 16 results are merged.
+__global__ __launch_bounds__(1024) void k_est_combine(Tables tb, char* ws, int n_part) {
   const EstJob& J = wsp<const EstJob>(ws, tb.off_jobs)[blockIdx.x];
   const int r = threadIdx.x & 63, wv = threadIdx.x >> 6;
   const float2* part = wsp<const float2>(ws, J.ws_part);
-  const int last = J.imax / EST_CK + 1;
-  const int per = (last + 15) / 16, c0 = wv * per, c1 = min(last, c0 + per);
+  const int per = (n_part + 15) / 16, c0 = wv * per, c1 = min(n_part, c0 + per);
   float2 st = make_float2(-INFINITY, 0.f);
   for (int c = c0; c < c1; ++c) st = lse2_merge_hw(st, part[(int64_t)c * 64 + r]);
   __shared__ float2 red[16][64];
@@ -710,14 +812,14 @@ __global__ __launch_bounds__(512) void k_grid_select(Tables tb, char* ws) {
 // Launchers
 // ---------------------------------------------------------------------------
 hipError_t launch_est_pass1(const Dims& dm, const Tables& tb, char* ws, const void* q, const void* k,
-                            int n_chunks1, hipStream_t s) {
-  if (tb.n_groups1 == 0) return hipSuccess;
-  dim3 grid(n_chunks1, (unsigned)tb.n_groups1);
+                            int n_wg1, hipStream_t s) {
+  if (tb.n_groups1 == 0 || n_wg1 <= 0) return hipSuccess;
+  dim3 grid((unsigned)n_wg1, (unsigned)tb.n_groups1);
   if (dm.d == 128)
     k_est_pass1<128><<<grid, 256, 0, s>>>(dm, tb, ws, (const bf16_t*)q, (const bf16_t*)k);
   else
     k_est_pass1<64><<<grid, 256, 0, s>>>(dm, tb, ws, (const bf16_t*)q, (const bf16_t*)k);
-  k_est_combine<<<(unsigned)tb.n_jobs, 1024, 0, s>>>(tb, ws);
+  k_est_combine<<<(unsigned)tb.n_jobs, 1024, 0, s>>>(tb, ws, n_wg1);
   return hipGetLastError();
 }
 

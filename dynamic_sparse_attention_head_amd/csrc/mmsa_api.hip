@@ -69,7 +69,7 @@ struct Layout {
   std::vector<int32_t> qgroup_heads;
   std::vector<char> blob;
   int64_t ws_total = 0;
-  int n_chunks1 = 0, n_chunks2 = 0, max_ds = 0, max_strides = 0, nB = 0, max_tiles = 0, max_bm_words = 0;
+  int n_chunks1 = 0, n_wg1 = 0, n_chunks2 = 0, max_ds = 0, max_strides = 0, nB = 0, max_tiles = 0, max_bm_words = 0;
   int max_gather_slots = 0, max_unperm_slots = 0;
   int64_t max_items = 0;
   int64_t max_topk_slices = 0;
@@ -575,8 +575,13 @@ mmsa_status build_layout(const mmsa_layer_desc* desc, Layout& Lo) {
       const HeadDev& H0 = Lo.heads[Lo.jobs[i].bh];
       size_t e = i;
       while (e < Lo.jobs.size() && Lo.heads[Lo.jobs[e].bh].b == H0.b && Lo.heads[Lo.jobs[e].bh].g == H0.g) ++e;
-      EstGroup G1{H0.b, H0.g, 0, (int)i, (int)e, L, H0.k_off, -1};
-      Lo.g1.push_back(G1);
+      // pass 1: batches of at most EST1_JB jobs, sizes as equal as possible
+      const int nj = (int)(e - i), nb = (nj + EST1_JB - 1) / EST1_JB;
+      for (int bi = 0; bi < nb; ++bi) {
+        const int j0 = (int)i + bi * nj / nb, j1 = (int)i + (bi + 1) * nj / nb;
+        EstGroup G1{H0.b, H0.g, 0, j0, j1, L, H0.k_off, -1};
+        Lo.g1.push_back(G1);
+      }
       for (size_t s = i; s < e;) {
         size_t f = s;
         while (f < e && Lo.jobs[f].view == Lo.jobs[s].view) ++f;
@@ -589,6 +594,12 @@ mmsa_status build_layout(const mmsa_layer_desc* desc, Layout& Lo) {
     }
   }
   Lo.n_chunks1 = (L + EST_CK - 1) / EST_CK;
+  // pass-1 workgroups per batch: about EST1_WG in all, a multiple of the XCD
+  // count (the batches of one KV head then read each key chunk on one XCD)
+  if (!Lo.g1.empty()) {
+    const int per = (int)((EST1_WG + Lo.g1.size() - 1) / Lo.g1.size());
+    Lo.n_wg1 = std::min(Lo.n_chunks1, std::max(N_XCD, (per + N_XCD - 1) / N_XCD * N_XCD));
+  }
   Lo.n_chunks2 = (std::max(L, dm.L_grp) + EST_CK - 1) / EST_CK;
 
   // ---- queue groups: q heads sharing one (b, KV head) ----
@@ -675,7 +686,7 @@ mmsa_status build_layout(const mmsa_layer_desc* desc, Layout& Lo) {
   // estimation: stats and partials
   for (EstJob& J : Lo.jobs) {
     J.ws_stats = bp.take(8ll * EST_ROWS);
-    J.ws_part = bp.take(8ll * EST_ROWS * Lo.n_chunks1);
+    J.ws_part = bp.take(8ll * EST_ROWS * std::max(Lo.n_wg1, 1));
   }
   // zero region: vertical scores and slash accumulators
   bp.off = pad_to(bp.off, 256);
@@ -988,7 +999,7 @@ mmsa_status mmsa_estimate_vs(const mmsa_layer_desc* desc, const void* q, const v
   char* w = (char*)ws;
   MMSA_TRY(upload(Lo, ws, s));
   if (Lo.need_seg) MMSA_HIP(launch_seg_tables(Lo.dm, Lo.tb, w, s), "segment tables");
-  MMSA_HIP(launch_est_pass1(Lo.dm, Lo.tb, w, q, k, Lo.n_chunks1, s), "estimation pass 1");
+  MMSA_HIP(launch_est_pass1(Lo.dm, Lo.tb, w, q, k, Lo.n_wg1, s), "estimation pass 1");
   MMSA_HIP(launch_fill_u32(w + Lo.zero_off, 0u, Lo.zero_bytes / 4, s), "score clear");
   MMSA_HIP(launch_est_pass2(Lo.dm, Lo.tb, w, q, k, Lo.n_chunks2, Lo.max_ds, s), "estimation pass 2");
   MMSA_HIP(launch_topk(Lo.tb, w, (int)Lo.max_topk_slices, s), "top-k");
