@@ -79,6 +79,22 @@ __device__ __forceinline__ float sum_rows4(float x) {
   return __uint_as_float(r[0]) + __uint_as_float(r[1]);
 }
 
+// The batch of a workgroup of a 1-D estimation launch: groups hold
+// consecutive workgroup ranges [wg0, wg0 + nwg).  Returns the group and this
+// workgroup's index within it.
+__device__ __forceinline__ EstGroup est_group(const char* ws, int64_t off, int64_t n, int& x) {
+  const MMSA_CONST EstGroup* gs = cptr<EstGroup>(ws, off);
+  int lo = 0, hi = (int)n - 1;
+  const int b = (int)blockIdx.x;
+  while (lo < hi) {   // last group with wg0 <= b
+    const int mid = (lo + hi + 1) >> 1;
+    if (gs[mid].wg0 <= b) lo = mid;
+    else hi = mid - 1;
+  }
+  x = b - gs[lo].wg0;
+  return gs[lo];
+}
+
 // Swizzle of the LDS copy of the estimation rows: physical 16-byte chunk =
 // logical ^ swz1(row), so the 16 rows one B-fragment read touches fall in 16
 // different bank groups (d = 128: 256-byte rows; d = 64: two 128-byte rows per
@@ -90,10 +106,10 @@ __device__ __forceinline__ int swz1(int r) {
 
 // ---------------------------------------------------------------------------
 // Pass 1: (max, sum of exp2) of each estimation row over its causal keys.
-// grid (workgroups per batch, job batches), block 256 = 4 waves.
-// A batch is at most EST1_JB jobs of one (b, KV head); their Q rows are
-// copied into LDS once, straight from memory (16 bytes a lane).  Workgroup x
-// of a batch takes the 256-key chunks x, x + gridDim.x, ...: each wave owns 64
+// 1-D grid: each batch (at most EST1_JB jobs of one (b, KV head)) owns a range
+// of workgroups, block 256 = 4 waves.  The batch's Q rows are copied into
+// LDS once, straight from memory (16 bytes a lane).  Workgroup x of a batch's
+// nwg takes the 256-key chunks x, x + nwg, ...: each wave owns 64
 // keys of a chunk, held in registers while the next chunk's keys load into a
 // second register set, and keeps a running (max, sum) per row in LDS.  At the
 // end the workgroup merges its four waves into one partial per row.
@@ -107,7 +123,8 @@ __global__ __launch_bounds__(256, 2) void k_est_pass1(Dims dm, Tables tb, char* 
   __shared__ int pos_s[EST1_JB][EST_ROWS];
   __shared__ int minpos_s[EST1_JB];
   __shared__ float2 st_s[EST1_JB][4][EST_ROWS];
-  const EstGroup G = wsp<const EstGroup>(ws, tb.off_groups1)[blockIdx.y];
+  int xw;
+  const EstGroup G = est_group(ws, tb.off_groups1, tb.n_groups1, xw);
   const MMSA_CONST EstJob* jobs = cptr<EstJob>(ws, tb.off_jobs) + G.job_begin;
   const int nj = min(G.job_end - G.job_begin, EST1_JB);
   const int tid = threadIdx.x, lane = tid & 63, qc = lane & 15, g4 = lane >> 4;
@@ -217,18 +234,19 @@ __global__ __launch_bounds__(256, 2) void k_est_pass1(Dims dm, Tables tb, char* 
   // row again), so every path through the loop has the same loads in flight
   // and the compiler's waits cover only the chunk being computed.
   bf16x8 kA[4][NC], kB[4][NC];
-  int c = blockIdx.x;
+  const int gx = G.nwg;
+  int c = xw;
   load_k(kA, c);
   asm volatile("s_waitcnt vmcnt(0)" ::: "memory");   // the copies of Q and the first keys
   __syncthreads();
   while (c < n_ck) {
-    load_k(kB, c + (int)gridDim.x);
+    load_k(kB, c + gx);
     body(kA, c);
-    c += gridDim.x;
+    c += gx;
     if (c >= n_ck) break;
-    load_k(kA, c + (int)gridDim.x);
+    load_k(kA, c + gx);
     body(kB, c);
-    c += gridDim.x;
+    c += gx;
   }
   __syncthreads();
   for (int t = tid; t < nj * EST_ROWS; t += 256) {
@@ -236,15 +254,16 @@ __global__ __launch_bounds__(256, 2) void k_est_pass1(Dims dm, Tables tb, char* 
     float2 st = st_s[jj][0][r];
 #pragma unroll
     for (int ww = 1; ww < 4; ++ww) st = lse2_merge_hw(st, st_s[jj][ww][r]);
-    wsp<float2>(ws, jobs[jj].ws_part)[(int64_t)blockIdx.x * EST_ROWS + r] = st;
+    wsp<float2>(ws, jobs[jj].ws_part)[(int64_t)xw * EST_ROWS + r] = st;
   }
 }
 
-// Final (max, sum) per estimation row from the n_part partials of its job
-// (one per pass-1 workgroup of its batch): 16 waves each merge a contiguous
-// range (lane = row), then the 16 results are merged.
-__global__ __launch_bounds__(1024) void k_est_combine(Tables tb, char* ws, int n_part) {
+// Final (max, sum) per estimation row from the partials of its job (one per
+// pass-1 workgroup of its batch): 16 waves each merge a contiguous range
+// (lane = row), then the 16 results are merged.
+__global__ __launch_bounds__(1024) void k_est_combine(Tables tb, char* ws) {
   const EstJob& J = wsp<const EstJob>(ws, tb.off_jobs)[blockIdx.x];
+  const int n_part = J.n_part1;
   const int r = threadIdx.x & 63, wv = threadIdx.x >> 6;
   const float2* part = wsp<const float2>(ws, J.ws_part);
   const int per = (n_part + 15) / 16, c0 = wv * per, c1 = min(n_part, c0 + per);
@@ -261,156 +280,234 @@ __global__ __launch_bounds__(1024) void k_est_combine(Tables tb, char* ws, int n
 
 // ---------------------------------------------------------------------------
 // Pass 2: probabilities, column sums (v) and diagonal sums (s).
-// grid (chunks of 256 view slots, pass-2 groups), block 256.
+// 1-D grid: each batch (at most EST2_JB jobs sharing (b, KV head, key view))
+// owns a range of workgroups, block 256 = 4 waves.  Like pass 1, workgroup x
+// of a batch's nwg takes the 256-slot chunks x, x + nwg, ... with the rows of Q
+// in LDS and the next chunk's keys loading into a second register set; the
+// key positions are read into registers two chunks ahead.
+// Per job, the normalised probabilities of 32 rows at a time go to an LDS
+// tile whose rows carry 32 zero columns on either side: a diagonal then reads
+// one entry per row at a constant stride, with no bounds test (a diagonal
+// through 32 rows leaves the 256 keys by at most 31 columns).
 // ---------------------------------------------------------------------------
 template <int D>
-__global__ __launch_bounds__(256) void k_est_pass2(Dims dm, Tables tb, char* ws, const bf16_t* __restrict__ q,
-                                                   const bf16_t* __restrict__ k) {
-  const EstGroup G = wsp<const EstGroup>(ws, tb.off_groups2)[blockIdx.y];
-  const EstJob* jobs = wsp<const EstJob>(ws, tb.off_jobs);
-  const int x0 = blockIdx.x * EST_CK;
-  if (x0 >= G.n_keys) return;
-  const int tid = threadIdx.x, w = tid >> 6, lane = tid & 63, qc = lane & 15, g4 = lane >> 4;
+__global__ __launch_bounds__(256, 2) void k_est_pass2(Dims dm, Tables tb, char* ws, const bf16_t* __restrict__ q,
+                                                      const bf16_t* __restrict__ k) {
+  constexpr int NC = D / 32, CPR = D / 8, RPI = 64 / CPR, IPW = EST_ROWS / RPI / 4;
+  constexpr int QJ = EST_ROWS * D * 2;
+  constexpr int HR = EST_ROWS / 2;          // rows of the probability tile
+  constexpr int ZP = 32;                    // zero columns on either side
+  constexpr int PW = EST_CK + 2 * ZP + 4;   // row pitch in floats (the 4 spread the rows over the banks)
+  __shared__ __attribute__((aligned(16))) char Qs[EST2_JB * QJ];
+  __shared__ __attribute__((aligned(16))) float P[HR][PW];
+  __shared__ __attribute__((aligned(16))) int kp_s[2][EST_CK];   // key positions of the chunk (-1: no token)
+  __shared__ int pos_s[EST2_JB][EST_ROWS];
+  __shared__ float2 st_s[EST2_JB][EST_ROWS];   // (max, 1 / sum) of each row
+  int xw;
+  const EstGroup G = est_group(ws, tb.off_groups2, tb.n_groups2, xw);
+  const MMSA_CONST EstJob* jobs = cptr<EstJob>(ws, tb.off_jobs) + G.job_begin;
+  const int nj = min(G.job_end - G.job_begin, EST2_JB);
+  const int tid = threadIdx.x, lane = tid & 63, qc = lane & 15, g4 = lane >> 4;
+  const int w = __builtin_amdgcn_readfirstlane(tid >> 6);
+  const int n_ck = (G.n_keys + EST_CK - 1) / EST_CK;
+  const bool grouped = G.view == VIEW_GROUPED;
+  const int32_t* pgrp = wsp<const int32_t>(ws, dm.ws_pgrp);
 
-  __shared__ int kp_s[EST_CK];
-  // one half of the estimation rows at a time (34 KB of LDS instead of 68)
-  constexpr int HR = EST_ROWS / 2;
-  __shared__ float P[HR][EST_CK + 4];
-  {
+  // ---- rows of Q into LDS (as in pass 1), row positions and statistics ----
+  for (int jj = 0; jj < nj; ++jj) {
+    const MMSA_CONST EstJob& J = jobs[jj];
+    if (tid < EST_ROWS) {
+      pos_s[jj][tid] = tid < J.n_rows ? J.rows[tid] : -1;
+      const float2 st = wsp<const float2>(ws, J.ws_stats)[tid];
+      st_s[jj][tid] = make_float2(st.x, st.y > 0.f ? 1.0f / st.y : 0.f);
+    }
+    const bf16_t* qh = q + J.q_off;
+#pragma unroll
+    for (int p = 0; p < IPW; ++p) {
+      const int ins = w * IPW + p;
+      const int row = ins * RPI + lane / CPR;
+      const int lch = (lane % CPR) ^ swz1<D>(row);
+      const int pos = J.n_rows > 0 ? J.rows[min(row, J.n_rows - 1)] : 0;
+      __builtin_amdgcn_global_load_lds(qh + (int64_t)pos * dm.q_sl + 8 * lch,
+                                       (__attribute__((address_space(3))) void*)(Qs + jj * QJ + ins * 1024), 16, 0,
+                                       0);
+    }
+  }
+  for (int i = tid; i < HR * 2 * ZP; i += 256) {   // the zero columns, never written again
+    const int r = i / (2 * ZP), cz = i % (2 * ZP);
+    P[r][cz < ZP ? cz : EST_CK + cz] = 0.f;
+  }
+  // Key positions of chunk c: those of the rows this lane loads (slots
+  // 64w + 16kb + qc) and of this thread's own slot (-1: no token).  Identity
+  // views compute them; grouped views read the slot map.
+  struct Pos {
+    int kb[4], own;
+  };
+  auto load_pos = [&](Pos& P, int c) {
+    const int x0 = c * EST_CK, lim = min(G.n_keys, dm.L);
+#pragma unroll
+    for (int kb = 0; kb < 4; ++kb) {
+      const int slot = x0 + 64 * w + 16 * kb + qc;
+      P.kb[kb] = grouped ? pgrp[min(slot, G.n_keys - 1)] : (slot < lim ? slot : -1);
+    }
     const int slot = x0 + tid;
-    int pos;
-    if (G.view == VIEW_IDENTITY) pos = slot < dm.L ? slot : -1;
-    else pos = wsp<const int32_t>(ws, dm.ws_pgrp)[slot];
-    kp_s[tid] = pos;
-  }
-  __syncthreads();
-  int kmin = 0x7fffffff;
-  {
-    // smallest key position of the chunk: skip jobs whose rows see none of it
-    int mine = kp_s[tid] >= 0 ? kp_s[tid] : 0x7fffffff;
-    for (int m = 1; m < 64; m <<= 1) mine = min(mine, __shfl_xor(mine, m, 64));
-    __shared__ int wmin[4];
-    if (lane == 0) wmin[w] = mine;
-    __syncthreads();
-    kmin = min(min(wmin[0], wmin[1]), min(wmin[2], wmin[3]));
-  }
-  int kp[4];
+    P.own = grouped ? (slot < G.n_keys ? pgrp[slot] : -1) : (slot < lim ? slot : -1);
+  };
+  const bf16_t* kh = k + G.k_off;
+  // keys of a chunk; slots without a token read row 0 (masked)
+  auto load_k = [&](bf16x8 (&kf)[4][NC], const Pos& P) {
 #pragma unroll
-  for (int kb = 0; kb < 4; ++kb) kp[kb] = kp_s[64 * w + 16 * kb + qc];
-  bf16x8 kf[4][D / 32];
-  load_k_frags<D>(kf, k + G.k_off, dm.k_sl, kp, lane);
+    for (int kb = 0; kb < 4; ++kb) {
+      const bf16_t* kr = kh + (int64_t)max(P.kb[kb], 0) * dm.k_sl + 8 * g4;
+#pragma unroll
+      for (int cc = 0; cc < NC; ++cc) kf[kb][cc] = as_bf16x8(ld16(kr + 32 * cc));
+    }
+  };
 
-  const int m_chunk = (G.view == VIEW_GROUPED && x0 >= dm.video_base) ? MMSA_VIDEO : MMSA_TEXT;
-  const int chunk_base = (m_chunk == MMSA_VIDEO) ? dm.video_base : dm.text_base;
-
-  for (int jb = G.job_begin; jb < G.job_end; ++jb) {
-    const EstJob& J = jobs[jb];
-    if (J.imax < kmin) continue;   // uniform
-    const float2* stats = wsp<const float2>(ws, J.ws_stats);
-    // row positions of the 4 row groups, then Q one group ahead of its MFMAs
-    int posv[4];
+  const float sl2 = dm.scale_log2;
+  // one chunk (positions in kp_s[sl])
+  auto body = [&](const bf16x8 (&kf)[4][NC], int c, int sl) {
+    const int x0 = c * EST_CK;
+    const int kmin = __builtin_amdgcn_readfirstlane(kp_s[sl][0]);   // smallest position (ascending; -1: empty)
+    const int kpos_mine = kp_s[sl][tid];
+    const int m_chunk = (grouped && x0 >= dm.video_base) ? MMSA_VIDEO : MMSA_TEXT;
+    const int chunk_base = (m_chunk == MMSA_VIDEO) ? dm.video_base : dm.text_base;
+    for (int jj = 0; jj < nj; ++jj) {
+      const MMSA_CONST EstJob& J = jobs[jj];
+      if (kmin < 0 || J.imax < kmin) continue;   // uniform
+      const char* qt = Qs + jj * QJ;
+      const bool slash = J.kind == JOB_VS_ORIG || J.kind == JOB_VS_2D;
+      float colsum = 0.f;
 #pragma unroll
-    for (int qb = 0; qb < 4; ++qb) posv[qb] = (16 * qb + qc < J.n_rows) ? J.rows[16 * qb + qc] : -1;
-    bf16x8 qfb[2][D / 32];
-    load_q_frag<D>(qfb[0], q + J.q_off, dm.q_sl, posv[0], lane);
-    const bool slash = J.kind == JOB_VS_ORIG || J.kind == JOB_VS_2D;
-    const int kpos_mine = kp_s[tid];
-    float colsum = 0.f;
-#pragma unroll
-    for (int half = 0; half < 2; ++half) {
-#pragma unroll
-      for (int qh = 0; qh < 2; ++qh) {
-        const int qb = 2 * half + qh;
-        const int row = 16 * qb + qc;
-        const bool rv = row < J.n_rows;
-        const int pos = posv[qb];
-        const float2 st = stats[row];
-        const float inv_l = (rv && st.y > 0.f) ? 1.0f / st.y : 0.f;
-        if (qb + 1 < 4) load_q_frag<D>(qfb[(qb + 1) & 1], q + J.q_off, dm.q_sl, posv[qb + 1], lane);
-        const bf16x8 (&qf)[D / 32] = qfb[qb & 1];
-#pragma unroll
-        for (int kb = 0; kb < 4; ++kb) {
-          floatx4 acc = {0.f, 0.f, 0.f, 0.f};
-#pragma unroll
-          for (int c = 0; c < D / 32; ++c) acc = mfma16(kf[kb][c], qf[c], acc);
-          const int4 kq = *reinterpret_cast<const int4*>(&kp_s[64 * w + 16 * kb + 4 * g4]);
-          const int kk[4] = {kq.x, kq.y, kq.z, kq.w};
-          float4 pv;
-          float* pp = reinterpret_cast<float*>(&pv);
-#pragma unroll
-          for (int i = 0; i < 4; ++i) {
-            const bool valid = rv && kk[i] >= 0 && kk[i] <= pos;
-            pp[i] = valid ? __builtin_amdgcn_exp2f(acc[i] * dm.scale_log2 - st.x) * inv_l : 0.f;
-          }
-          *reinterpret_cast<float4*>(&P[row - HR * half][64 * w + 16 * kb + 4 * g4]) = pv;
-        }
-      }
-      __syncthreads();
-
-      // column sums of this half (rows past n_rows hold zeros); a fixed loop
-      // with independent partials lets the LDS reads overlap
-      if (kpos_mine >= 0 && kpos_mine <= J.imax) {
-        float part[8] = {0.f, 0.f, 0.f, 0.f, 0.f, 0.f, 0.f, 0.f};
-#pragma unroll
-        for (int r = 0; r < HR; ++r) part[r & 7] += P[r][tid];
-        colsum += ((part[0] + part[1]) + (part[2] + part[3])) + ((part[4] + part[5]) + (part[6] + part[7]));
-      }
-      // diagonal sums of this half -> slash accumulators (fixed point, so the
-      // result does not depend on the order of the additions)
-      if (slash) {
-        const int pi = (J.kind == JOB_VS_2D && J.pair[0].m_k != m_chunk) ? 1 : 0;
-        const PairDev& Pd = J.pair[pi];
-        unsigned long long* sacc = wsp<unsigned long long>(ws, Pd.ws_sacc);
-        const int n_runs = (J.kind == JOB_VS_2D) ? 1 : J.n_runs;
+      for (int half = 0; half < 2; ++half) {
         const int h0 = HR * half;
-        for (int ru = 0; ru < n_runs; ++ru) {
-          int r0, len, A;
-          if (J.kind == JOB_VS_2D) {
-            r0 = 0;
-            len = J.n_rows;
-            A = J.rho0 + Pd.n_k - 1 - (x0 - chunk_base);
-          } else {
-            r0 = J.run_r0[ru];
-            len = J.run_len[ru];
-            A = J.rows[r0] - r0 - x0;
-          }
-          if (r0 >= h0 + HR || r0 + len <= h0) continue;   // run outside this half (uniform)
-          const int span = len + EST_CK - 1;
-          const int idx_lo = A + r0 - (EST_CK - 1);
-          for (int ii = tid; ii < span; ii += 256) {
-            const int idx = idx_lo + ii;
-            if (idx < 0 || idx >= Pd.Ds) continue;
-            const int rlo = max(max(r0, idx - A), h0), rhi = min(min(r0 + len, idx - A + EST_CK), h0 + HR);
-            float part[8] = {0.f, 0.f, 0.f, 0.f, 0.f, 0.f, 0.f, 0.f};
 #pragma unroll
-            for (int rl = 0; rl < HR; ++rl) {
-              const int r = h0 + rl;
-              const bool in = (r >= rlo) & (r < rhi);
-              const int c = in ? A + r - idx : 0;
-              const float x = P[rl][c];
-              part[rl & 7] += in ? x : 0.f;
+        for (int qh = 0; qh < 2; ++qh) {
+          const int row = h0 + 16 * qh + qc;
+          bf16x8 qf[NC];
+#pragma unroll
+          for (int cc = 0; cc < NC; ++cc)
+            qf[cc] = *reinterpret_cast<const bf16x8*>(qt + row * (2 * D) + 16 * ((4 * cc + g4) ^ swz1<D>(row)));
+          const int pos = pos_s[jj][row];
+          const float2 st = st_s[jj][row];
+#pragma unroll
+          for (int kb = 0; kb < 4; ++kb) {
+            floatx4 acc = {0.f, 0.f, 0.f, 0.f};
+#pragma unroll
+            for (int cc = 0; cc < NC; ++cc) acc = mfma16(kf[kb][cc], qf[cc], acc);
+            const int4 kq = *reinterpret_cast<const int4*>(&kp_s[sl][64 * w + 16 * kb + 4 * g4]);
+            const int kk[4] = {kq.x, kq.y, kq.z, kq.w};
+            float4 pv;
+            float* pp = reinterpret_cast<float*>(&pv);
+#pragma unroll
+            for (int i = 0; i < 4; ++i) {
+              const bool valid = kk[i] >= 0 && kk[i] <= pos;   // pos = -1 for padding rows
+              pp[i] = valid ? __builtin_amdgcn_exp2f(fmaf(acc[i], sl2, -st.x)) * st.y : 0.f;
             }
-            const float sum = ((part[0] + part[1]) + (part[2] + part[3])) + ((part[4] + part[5]) + (part[6] + part[7]));
-            if (sum != 0.f) atomicAdd(&sacc[idx], (unsigned long long)llrint((double)sum * SFIX));
+            *reinterpret_cast<float4*>(&P[16 * qh + qc][ZP + 64 * w + 16 * kb + 4 * g4]) = pv;
           }
         }
-      }
-      __syncthreads();
-    }
+        __syncthreads();
 
-    // column sums -> vertical scores (or grid line scores)
-    if (kpos_mine >= 0 && kpos_mine <= J.imax) {
-      const int slot = x0 + tid;
-      if (J.kind == JOB_VS_ORIG || J.kind == JOB_GRID_PLAIN) {
-        wsp<float>(ws, J.pair[0].ws_v)[kpos_mine] = colsum;
-      } else if (J.kind == JOB_GRID_GROUPED) {
-        const int xg = (slot < dm.video_base) ? slot : dm.n_text + (slot - dm.video_base);
-        wsp<float>(ws, J.pair[0].ws_v)[xg] = colsum;
-      } else {
-        const int pi = (J.pair[0].m_k == m_chunk) ? 0 : 1;
-        wsp<float>(ws, J.pair[pi].ws_v)[slot - chunk_base] = colsum;
+        // column sums of this half (rows past n_rows hold zeros)
+        {
+          float part[8] = {0.f, 0.f, 0.f, 0.f, 0.f, 0.f, 0.f, 0.f};
+#pragma unroll
+          for (int r = 0; r < HR; ++r) part[r & 7] += P[r][ZP + tid];
+          colsum += ((part[0] + part[1]) + (part[2] + part[3])) + ((part[4] + part[5]) + (part[6] + part[7]));
+        }
+        // diagonal sums of this half -> slash accumulators (fixed point, so the
+        // result does not depend on the order of the additions)
+        if (slash) {
+          const int pi = (J.kind == JOB_VS_2D && J.pair[0].m_k != m_chunk) ? 1 : 0;
+          const MMSA_CONST PairDev& Pd = J.pair[pi];
+          unsigned long long* sacc = wsp<unsigned long long>(ws, Pd.ws_sacc);
+          const int n_runs = (J.kind == JOB_VS_2D) ? 1 : J.n_runs;
+          for (int ru = 0; ru < n_runs; ++ru) {
+            int r0, len, A;
+            if (J.kind == JOB_VS_2D) {
+              r0 = 0;
+              len = J.n_rows;
+              A = J.rho0 + Pd.n_k - 1 - (x0 - chunk_base);
+            } else {
+              r0 = J.run_r0[ru];
+              len = J.run_len[ru];
+              A = J.rows[r0] - r0 - x0;
+            }
+            // rows [ra, rb) of this run in this half; diagonal idx holds the
+            // entries (r, A + r - idx), whose columns stay within 31 of the keys
+            const int ra = max(r0, h0), rb = min(r0 + len, h0 + HR);
+            if (ra >= rb) continue;   // uniform
+            const int idx_lo = A + ra - (EST_CK - 1), span = rb - ra + EST_CK - 1;
+            const bool whole = ra == h0 && rb == h0 + HR;
+            for (int ii = tid; ii < span; ii += 256) {
+              const int idx = idx_lo + ii;
+              if (idx < 0 || idx >= Pd.Ds) continue;
+              // &P[r - h0][ZP + A + r - idx]: one pitch plus one float per row
+              const float* pd = &P[0][ZP + A + h0 - idx];
+              float part[8] = {0.f, 0.f, 0.f, 0.f, 0.f, 0.f, 0.f, 0.f};
+              if (whole) {
+#pragma unroll
+                for (int rl = 0; rl < HR; ++rl) part[rl & 7] += pd[rl * (PW + 1)];
+              } else {
+                for (int rl = ra - h0; rl < rb - h0; ++rl) part[0] += pd[rl * (PW + 1)];
+              }
+              const float sum = ((part[0] + part[1]) + (part[2] + part[3])) + ((part[4] + part[5]) + (part[6] + part[7]));
+              if (sum != 0.f) atomicAdd(&sacc[idx], (unsigned long long)llrint((double)sum * SFIX));
+            }
+          }
+        }
+        __syncthreads();
+      }
+
+      // column sums -> vertical scores (or grid line scores)
+      if (kpos_mine >= 0 && kpos_mine <= J.imax) {
+        const int slot = x0 + tid;
+        if (J.kind == JOB_VS_ORIG || J.kind == JOB_GRID_PLAIN) {
+          wsp<float>(ws, J.pair[0].ws_v)[kpos_mine] = colsum;
+        } else if (J.kind == JOB_GRID_GROUPED) {
+          const int xg = (slot < dm.video_base) ? slot : dm.n_text + (slot - dm.video_base);
+          wsp<float>(ws, J.pair[0].ws_v)[xg] = colsum;
+        } else {
+          const int pi = (J.pair[0].m_k == m_chunk) ? 0 : 1;
+          wsp<float>(ws, J.pair[pi].ws_v)[slot - chunk_base] = colsum;
+        }
       }
     }
+  };
+
+  // Pipeline: iteration it computes chunk c_it (positions in kp_s[it & 1],
+  // keys in one register set) while the keys of c_it+1 load into the other
+  // set and the positions of c_it+2 into registers.  Each iteration ends by
+  // waiting for everything it issued -- the prefetches have had a whole chunk
+  // of work to land -- so the compiler's waits inside the job loop, whose
+  // stores would otherwise mix with loads in flight, are never needed.
+  bf16x8 kA[4][NC], kB[4][NC];
+  Pos p0, p1;
+  const int gx = G.nwg;
+  int c = xw;
+  load_pos(p0, c);
+  load_pos(p1, c + gx);
+  load_k(kA, p0);
+  kp_s[0][tid] = p0.own;
+  __builtin_amdgcn_s_waitcnt(0);   // rows of Q, the first keys and positions
+  __syncthreads();
+  while (c < n_ck) {
+    load_pos(p0, c + 2 * gx);
+    load_k(kB, p1);
+    body(kA, c, 0);
+    __builtin_amdgcn_s_waitcnt(0);
+    kp_s[1][tid] = p1.own;
+    __syncthreads();
+    c += gx;
+    if (c >= n_ck) break;
+    load_pos(p1, c + 2 * gx);
+    load_k(kA, p0);
+    body(kB, c, 1);
+    __builtin_amdgcn_s_waitcnt(0);
+    kp_s[0][tid] = p0.own;
+    __syncthreads();
+    c += gx;
   }
 }
 
@@ -814,19 +911,19 @@ __global__ __launch_bounds__(512) void k_grid_select(Tables tb, char* ws) {
 hipError_t launch_est_pass1(const Dims& dm, const Tables& tb, char* ws, const void* q, const void* k,
                             int n_wg1, hipStream_t s) {
   if (tb.n_groups1 == 0 || n_wg1 <= 0) return hipSuccess;
-  dim3 grid((unsigned)n_wg1, (unsigned)tb.n_groups1);
+  const dim3 grid((unsigned)n_wg1);
   if (dm.d == 128)
     k_est_pass1<128><<<grid, 256, 0, s>>>(dm, tb, ws, (const bf16_t*)q, (const bf16_t*)k);
   else
     k_est_pass1<64><<<grid, 256, 0, s>>>(dm, tb, ws, (const bf16_t*)q, (const bf16_t*)k);
-  k_est_combine<<<(unsigned)tb.n_jobs, 1024, 0, s>>>(tb, ws, n_wg1);
+  k_est_combine<<<(unsigned)tb.n_jobs, 1024, 0, s>>>(tb, ws);
   return hipGetLastError();
 }
 
 hipError_t launch_est_pass2(const Dims& dm, const Tables& tb, char* ws, const void* q, const void* k,
-                            int n_chunks2, int max_ds, hipStream_t s) {
-  if (tb.n_groups2 == 0) return hipSuccess;
-  dim3 grid(n_chunks2, (unsigned)tb.n_groups2);
+                            int n_wg2, int max_ds, hipStream_t s) {
+  if (tb.n_groups2 == 0 || n_wg2 <= 0) return hipSuccess;
+  const dim3 grid((unsigned)n_wg2);
   if (dm.d == 128)
     k_est_pass2<128><<<grid, 256, 0, s>>>(dm, tb, ws, (const bf16_t*)q, (const bf16_t*)k);
   else

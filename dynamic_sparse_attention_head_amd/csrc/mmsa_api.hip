@@ -69,7 +69,7 @@ struct Layout {
   std::vector<int32_t> qgroup_heads;
   std::vector<char> blob;
   int64_t ws_total = 0;
-  int n_chunks1 = 0, n_wg1 = 0, n_chunks2 = 0, max_ds = 0, max_strides = 0, nB = 0, max_tiles = 0, max_bm_words = 0;
+  int n_chunks1 = 0, n_wg1 = 0, n_chunks2 = 0, n_wg2 = 0, max_ds = 0, max_strides = 0, nB = 0, max_tiles = 0, max_bm_words = 0;
   int max_gather_slots = 0, max_unperm_slots = 0;
   int64_t max_items = 0;
   int64_t max_topk_slices = 0;
@@ -579,27 +579,55 @@ mmsa_status build_layout(const mmsa_layer_desc* desc, Layout& Lo) {
       const int nj = (int)(e - i), nb = (nj + EST1_JB - 1) / EST1_JB;
       for (int bi = 0; bi < nb; ++bi) {
         const int j0 = (int)i + bi * nj / nb, j1 = (int)i + (bi + 1) * nj / nb;
-        EstGroup G1{H0.b, H0.g, 0, j0, j1, L, H0.k_off, -1};
+        EstGroup G1{H0.b, H0.g, 0, j0, j1, L, H0.k_off, -1, 0, 0};
         Lo.g1.push_back(G1);
       }
       for (size_t s = i; s < e;) {
         size_t f = s;
         while (f < e && Lo.jobs[f].view == Lo.jobs[s].view) ++f;
         const int view = Lo.jobs[s].view;
-        EstGroup G2{H0.b, H0.g, view, (int)s, (int)f, view == VIEW_GROUPED ? dm.L_grp : L, H0.k_off, -1};
-        Lo.g2.push_back(G2);
+        // pass 2: batches of at most EST2_JB jobs of one key view
+        const int nv = (int)(f - s), nb2 = (nv + EST2_JB - 1) / EST2_JB;
+        for (int bi = 0; bi < nb2; ++bi) {
+          const int j0 = (int)s + bi * nv / nb2, j1 = (int)s + (bi + 1) * nv / nb2;
+          EstGroup G2{H0.b, H0.g, view, j0, j1, view == VIEW_GROUPED ? dm.L_grp : L, H0.k_off, -1, 0, 0};
+          Lo.g2.push_back(G2);
+        }
         s = f;
       }
       i = e;
     }
   }
   Lo.n_chunks1 = (L + EST_CK - 1) / EST_CK;
-  // pass-1 workgroups per batch: about EST1_WG in all, a multiple of the XCD
-  // count (the batches of one KV head then read each key chunk on one XCD)
-  if (!Lo.g1.empty()) {
-    const int per = (int)((EST1_WG + Lo.g1.size() - 1) / Lo.g1.size());
-    Lo.n_wg1 = std::min(Lo.n_chunks1, std::max(N_XCD, (per + N_XCD - 1) / N_XCD * N_XCD));
-  }
+  // Workgroups of each estimation batch: about EST1_WG per pass in all, in
+  // proportion to the batch's work (jobs x key chunks it reads), each count a
+  // multiple of the XCD count, so that workgroup x of every batch of one KV
+  // head runs on the same XCD and their reads of a key chunk meet in its L2.
+  auto spread = [&](std::vector<EstGroup>& gs, int& total) {
+    std::vector<double> work(gs.size());
+    double sum = 0;
+    for (size_t i = 0; i < gs.size(); ++i) {
+      int imax = -1;
+      for (int j = gs[i].job_begin; j < gs[i].job_end; ++j) imax = std::max(imax, Lo.jobs[j].imax);
+      const int chunks = gs[i].view == VIEW_GROUPED ? (gs[i].n_keys + EST_CK - 1) / EST_CK : imax / EST_CK + 1;
+      work[i] = (double)(gs[i].job_end - gs[i].job_begin) * std::max(chunks, 1);
+      sum += work[i];
+    }
+    total = 0;
+    for (size_t i = 0; i < gs.size(); ++i) {
+      const int chunks = (gs[i].n_keys + EST_CK - 1) / EST_CK;
+      int n = (int)std::lround(EST1_WG * work[i] / std::max(sum, 1.0));
+      n = std::max(N_XCD, (n + N_XCD - 1) / N_XCD * N_XCD);
+      n = std::min(n, (chunks + N_XCD - 1) / N_XCD * N_XCD);
+      gs[i].wg0 = total;
+      gs[i].nwg = n;
+      total += n;
+    }
+  };
+  spread(Lo.g1, Lo.n_wg1);
+  spread(Lo.g2, Lo.n_wg2);
+  for (const EstGroup& G : Lo.g1)
+    for (int j = G.job_begin; j < G.job_end; ++j) Lo.jobs[j].n_part1 = G.nwg;
   Lo.n_chunks2 = (std::max(L, dm.L_grp) + EST_CK - 1) / EST_CK;
 
   // ---- queue groups: q heads sharing one (b, KV head) ----
@@ -686,7 +714,7 @@ mmsa_status build_layout(const mmsa_layer_desc* desc, Layout& Lo) {
   // estimation: stats and partials
   for (EstJob& J : Lo.jobs) {
     J.ws_stats = bp.take(8ll * EST_ROWS);
-    J.ws_part = bp.take(8ll * EST_ROWS * std::max(Lo.n_wg1, 1));
+    J.ws_part = bp.take(8ll * EST_ROWS * std::max(J.n_part1, 1));
   }
   // zero region: vertical scores and slash accumulators
   bp.off = pad_to(bp.off, 256);
@@ -1001,7 +1029,7 @@ mmsa_status mmsa_estimate_vs(const mmsa_layer_desc* desc, const void* q, const v
   if (Lo.need_seg) MMSA_HIP(launch_seg_tables(Lo.dm, Lo.tb, w, s), "segment tables");
   MMSA_HIP(launch_est_pass1(Lo.dm, Lo.tb, w, q, k, Lo.n_wg1, s), "estimation pass 1");
   MMSA_HIP(launch_fill_u32(w + Lo.zero_off, 0u, Lo.zero_bytes / 4, s), "score clear");
-  MMSA_HIP(launch_est_pass2(Lo.dm, Lo.tb, w, q, k, Lo.n_chunks2, Lo.max_ds, s), "estimation pass 2");
+  MMSA_HIP(launch_est_pass2(Lo.dm, Lo.tb, w, q, k, Lo.n_wg2, Lo.max_ds, s), "estimation pass 2");
   MMSA_HIP(launch_topk(Lo.tb, w, (int)Lo.max_topk_slices, s), "top-k");
   MMSA_HIP(launch_grid(Lo.dm, Lo.tb, w, Lo.max_strides, s), "grid rule");
   return MMSA_OK;

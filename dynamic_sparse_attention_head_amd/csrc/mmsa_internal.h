@@ -11,7 +11,8 @@ constexpr int TILE = 64;        // query / key tile and pooling block
 constexpr int EST_ROWS = 64;    // estimation rows per region
 constexpr int EST_CK = 256;     // keys per workgroup chunk in the estimation passes
 constexpr int EST1_JB = 4;      // estimation jobs per pass-1 batch (their Q rows stay in LDS)
-constexpr int EST1_WG = 512;    // pass-1 workgroups to aim for (two per compute unit)
+constexpr int EST1_WG = 512;    // workgroups per estimation pass to aim for (two per compute unit)
+constexpr int EST2_JB = 2;      // estimation jobs per pass-2 batch
 constexpr int GRP_PAD = 256;    // modality parts of the grouped order are padded to this
 constexpr int MAX_PHASES = 16;  // grid phases kept at most
 constexpr int MAX_STRIDE = 1024;// largest grid stride searched
@@ -87,21 +88,24 @@ struct PairDev {
 struct EstJob {
   int32_t bh, kind, view, m_q;
   int32_t n_rows, rho0, n_runs, n_pairs;
-  int32_t imax, _pad0;
+  int32_t imax;
+  int32_t n_part1;           // pass-1 partials of this job (workgroups of its batch)
   int64_t q_off, k_off;
   int64_t ws_stats;          // float2 [64] final (max in log2 units, sum)
-  int64_t ws_part;           // float2 [pass-1 workgroups per batch][64] partials of pass 1
+  int64_t ws_part;           // float2 [n_part1][64] partials of pass 1
   int32_t rows[EST_ROWS];    // ascending original positions
   int32_t run_r0[EST_ROWS];  // runs of consecutive positions: first row index
   int32_t run_len[EST_ROWS];
   PairDev pair[2];
 };
 
-// A set of jobs sharing (b, g) [pass 1: at most EST1_JB of them] or (b, g, view) [pass 2].
+// A set of jobs sharing (b, g) [pass 1: at most EST1_JB of them] or (b, g, view)
+// [pass 2: at most EST2_JB].
 struct EstGroup {
   int32_t b, g, view, job_begin, job_end, n_keys;
   int64_t k_off;             // element offset of K of (b,g)
   int64_t ws_kgrp;           // grouped K (view 1), else -1
+  int32_t wg0, nwg;          // its workgroups wg0 .. wg0+nwg-1 of the (1-D) launch
 };
 
 struct TopkTask {
@@ -190,9 +194,9 @@ hipError_t launch_fill_u32(void* p, uint32_t value, int64_t n_words, hipStream_t
 hipError_t launch_seg_tables(const Dims& dm, const Tables& tb, char* ws, hipStream_t s);
 
 hipError_t launch_est_pass1(const Dims& dm, const Tables& tb, char* ws, const void* q, const void* k,
-                            int n_wg1, hipStream_t s);
+                            int n_wg1, hipStream_t s);   // n_wg1: workgroups of all pass-1 batches
 hipError_t launch_est_pass2(const Dims& dm, const Tables& tb, char* ws, const void* q, const void* k,
-                            int n_chunks2, int max_ds, hipStream_t s);
+                            int n_wg2, int max_ds, hipStream_t s);
 hipError_t launch_topk(const Tables& tb, char* ws, int max_slices, hipStream_t s);
 hipError_t launch_grid(const Dims& dm, const Tables& tb, char* ws, int max_strides, hipStream_t s);
 
