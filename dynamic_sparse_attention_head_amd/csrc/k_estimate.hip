@@ -30,38 +30,6 @@ __device__ __forceinline__ float2 lse2_merge_hw(float2 a, float2 b) {
   return make_float2(m, a.y * __builtin_amdgcn_exp2f(a.x - m) + b.y * __builtin_amdgcn_exp2f(b.x - m));
 }
 
-// ---------------------------------------------------------------------------
-// Fragments of 64 keys x D dims of K for the A operand (rows = keys).
-// ---------------------------------------------------------------------------
-template <int D>
-__device__ __forceinline__ void load_k_frags(bf16x8 (&kf)[4][D / 32], const bf16_t* __restrict__ kbase,
-                                             int64_t k_sl, const int* kpos, int lane) {
-  const int qc = lane & 15, g4 = lane >> 4;
-#pragma unroll
-  for (int kb = 0; kb < 4; ++kb) {
-    int p = kpos[kb];
-#pragma unroll
-    for (int c = 0; c < D / 32; ++c) {
-      uint4 u = make_uint4(0, 0, 0, 0);
-      if (p >= 0) u = ld16(kbase + (int64_t)p * k_sl + 32 * c + 8 * g4);
-      kf[kb][c] = as_bf16x8(u);
-    }
-  }
-  (void)qc;
-}
-
-template <int D>
-__device__ __forceinline__ void load_q_frag(bf16x8 (&qf)[D / 32], const bf16_t* __restrict__ qbase, int64_t q_sl,
-                                            int pos, int lane) {
-  const int g4 = lane >> 4;
-#pragma unroll
-  for (int c = 0; c < D / 32; ++c) {
-    uint4 u = make_uint4(0, 0, 0, 0);
-    if (pos >= 0) u = ld16(qbase + (int64_t)pos * q_sl + 32 * c + 8 * g4);
-    qf[c] = as_bf16x8(u);
-  }
-}
-
 // Max and sum over the four 16-lane rows of a wave (lanes l, l^16, l^32,
 // l^48), in registers: v_permlane16_swap pairs rows 0-1 and 2-3, then
 // v_permlane32_swap pairs the halves.  Every lane receives the result, and
