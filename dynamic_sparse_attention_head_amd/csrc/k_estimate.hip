@@ -48,10 +48,9 @@ __device__ __forceinline__ float sum_rows4(float x) {
 }
 
 // The batch of a workgroup of a 1-D estimation launch: groups hold
-// consecutive workgroup ranges [wg0, wg0 + nwg).  Returns the group and this
-// workgroup's index within it.
-__device__ __forceinline__ EstGroup est_group(const char* ws, int64_t off, int64_t n, int& x) {
-  const MMSA_CONST EstGroup* gs = cptr<EstGroup>(ws, off);
+// consecutive workgroup ranges [wg0, wg0 + nwg).  Returns the group's index
+// and sets x to this workgroup's index within it.
+__device__ __forceinline__ int est_group(const MMSA_CONST EstGroup* gs, int64_t n, int& x) {
   int lo = 0, hi = (int)n - 1;
   const int b = (int)blockIdx.x;
   while (lo < hi) {   // last group with wg0 <= b
@@ -60,7 +59,7 @@ __device__ __forceinline__ EstGroup est_group(const char* ws, int64_t off, int64
     else hi = mid - 1;
   }
   x = b - gs[lo].wg0;
-  return gs[lo];
+  return lo;
 }
 
 // Swizzle of the LDS copy of the estimation rows: physical 16-byte chunk =
@@ -92,7 +91,8 @@ __global__ __launch_bounds__(256, 2) void k_est_pass1(Dims dm, Tables tb, char* 
   __shared__ int minpos_s[EST1_JB];
   __shared__ float2 st_s[EST1_JB][4][EST_ROWS];
   int xw;
-  const EstGroup G = est_group(ws, tb.off_groups1, tb.n_groups1, xw);
+  const MMSA_CONST EstGroup* gs = cptr<EstGroup>(ws, tb.off_groups1);
+  const MMSA_CONST EstGroup& G = gs[est_group(gs, tb.n_groups1, xw)];
   const MMSA_CONST EstJob* jobs = cptr<EstJob>(ws, tb.off_jobs) + G.job_begin;
   const int nj = min(G.job_end - G.job_begin, EST1_JB);
   const int tid = threadIdx.x, lane = tid & 63, qc = lane & 15, g4 = lane >> 4;
@@ -272,13 +272,19 @@ __global__ __launch_bounds__(256, 2) void k_est_pass2(Dims dm, Tables tb, char* 
   __shared__ int pos_s[EST2_JB][EST_ROWS];
   __shared__ float2 st_s[EST2_JB][EST_ROWS];   // (max, 1 / sum) of each row
   int xw;
-  const EstGroup G = est_group(ws, tb.off_groups2, tb.n_groups2, xw);
+  const MMSA_CONST EstGroup* gs = cptr<EstGroup>(ws, tb.off_groups2);
+  const MMSA_CONST EstGroup& G = gs[est_group(gs, tb.n_groups2, xw)];
   const MMSA_CONST EstJob* jobs = cptr<EstJob>(ws, tb.off_jobs) + G.job_begin;
   const int nj = min(G.job_end - G.job_begin, EST2_JB);
   const int tid = threadIdx.x, lane = tid & 63, qc = lane & 15, g4 = lane >> 4;
   const int w = __builtin_amdgcn_readfirstlane(tid >> 6);
-  const int n_ck = (G.n_keys + EST_CK - 1) / EST_CK;
   const bool grouped = G.view == VIEW_GROUPED;
+  // identity views: no chunk past the batch's last estimation row holds a
+  // key any of its rows sees (grouped views order keys by modality first)
+  int gimax = -1;
+  for (int jj = 0; jj < nj; ++jj) gimax = max(gimax, jobs[jj].imax);
+  const int n_ck = grouped ? (G.n_keys + EST_CK - 1) / EST_CK
+                           : min((G.n_keys + EST_CK - 1) / EST_CK, gimax / EST_CK + 1);
   const int32_t* pgrp = wsp<const int32_t>(ws, dm.ws_pgrp);
 
   // ---- rows of Q into LDS (as in pass 1), row positions and statistics ----

@@ -599,29 +599,48 @@ mmsa_status build_layout(const mmsa_layer_desc* desc, Layout& Lo) {
     }
   }
   Lo.n_chunks1 = (L + EST_CK - 1) / EST_CK;
-  // Workgroups of each estimation batch: about EST1_WG per pass in all, in
-  // proportion to the batch's work (jobs x key chunks it reads), each count a
-  // multiple of the XCD count, so that workgroup x of every batch of one KV
-  // head runs on the same XCD and their reads of a key chunk meet in its L2.
+  // Workgroups of each estimation batch: EST1_WG per pass in all (one wave of
+  // two workgroups per CU), shared in proportion to each batch's work (jobs x
+  // key chunks it reads) by largest remainders, at least one each and at most
+  // one per chunk.  Equal batches (the usual case) get equal counts; when
+  // those are multiples of 8, workgroup x of every batch of a KV head runs on
+  // the same XCD and their reads of a key chunk meet in its L2.
   auto spread = [&](std::vector<EstGroup>& gs, int& total) {
-    std::vector<double> work(gs.size());
+    const size_t n = gs.size();
+    std::vector<double> work(n);
+    std::vector<int> cap(n);
     double sum = 0;
-    for (size_t i = 0; i < gs.size(); ++i) {
+    for (size_t i = 0; i < n; ++i) {
       int imax = -1;
       for (int j = gs[i].job_begin; j < gs[i].job_end; ++j) imax = std::max(imax, Lo.jobs[j].imax);
-      const int chunks = gs[i].view == VIEW_GROUPED ? (gs[i].n_keys + EST_CK - 1) / EST_CK : imax / EST_CK + 1;
+      const int all = (gs[i].n_keys + EST_CK - 1) / EST_CK;
+      const int chunks = gs[i].view == VIEW_GROUPED ? all : std::min(all, imax / EST_CK + 1);
       work[i] = (double)(gs[i].job_end - gs[i].job_begin) * std::max(chunks, 1);
+      cap[i] = std::max(all, 1);
       sum += work[i];
     }
+    std::vector<int> cnt(n);
+    std::vector<std::pair<double, size_t>> rem;
+    int used = 0;
+    for (size_t i = 0; i < n; ++i) {
+      const double share = EST1_WG * work[i] / std::max(sum, 1.0);
+      cnt[i] = std::min(cap[i], std::max(1, (int)share));
+      used += cnt[i];
+      rem.push_back({share - (int)share, i});
+    }
+    std::sort(rem.begin(), rem.end(), [](const auto& a, const auto& b) { return a.first > b.first || (a.first == b.first && a.second < b.second); });
+    for (size_t r = 0; r < rem.size() && used < EST1_WG; ++r) {
+      const size_t i = rem[r].second;
+      if (cnt[i] < cap[i]) {
+        ++cnt[i];
+        ++used;
+      }
+    }
     total = 0;
-    for (size_t i = 0; i < gs.size(); ++i) {
-      const int chunks = (gs[i].n_keys + EST_CK - 1) / EST_CK;
-      int n = (int)std::lround(EST1_WG * work[i] / std::max(sum, 1.0));
-      n = std::max(N_XCD, (n + N_XCD - 1) / N_XCD * N_XCD);
-      n = std::min(n, (chunks + N_XCD - 1) / N_XCD * N_XCD);
+    for (size_t i = 0; i < n; ++i) {
       gs[i].wg0 = total;
-      gs[i].nwg = n;
-      total += n;
+      gs[i].nwg = cnt[i];
+      total += cnt[i];
     }
   };
   spread(Lo.g1, Lo.n_wg1);
