@@ -512,10 +512,17 @@ __global__ __launch_bounds__(256) void k_plan(Dims dm, Tables tb, char* ws) {
 
 // ---------------------------------------------------------------------------
 // Attention work queue.  Items (head, pair of adjacent query tiles) are ordered
-// by queue group (q heads sharing one b, KV head), then pair descending, then
-// head: the most expensive pairs of a KV head come first, and the attention
-// kernel deals the order round-robin to the XCDs.
+// by queue group (q heads sharing one b, KV head) and, within a group, by pair
+// descending, then head: the most expensive pairs of a KV head come first, and
+// the attention kernel deals the order round-robin to the XCDs.  Once the K/V
+// of one KV head (4·L·d bytes) reach half the 256 MB last-level cache, a group
+// is ordered by head, then pair descending: the workgroups running at one time
+// then belong to one head, advance through its key tiles at one pace and keep
+// the part of K/V they share in that cache (measured: 4.5 % faster at 1M and
+// 1.6 % at 256K tokens, but 4.3 % slower at 128K, where the interleaved order
+// lets the heads of a pair share their key tiles instead).
 // ---------------------------------------------------------------------------
+constexpr int64_t HEAD_MAJOR_KV_BYTES = 128ll << 20;
 
 // Queue position and cost of every (head, pair of adjacent query tiles).
 // grid (pairs/64, heads).
@@ -529,11 +536,19 @@ __global__ __launch_bounds__(64) void k_queue_enum(Dims dm, Tables tb, char* ws)
   const QGroup G = wsp<const QGroup>(ws, tb.off_qgroups)[H.qgroup];
   const int32_t* gh = wsp<const int32_t>(ws, tb.off_qgroup_heads);
   int64_t e = G.item_base;
-  for (int i = G.head_begin; i < G.head_end; ++i) {
-    const int h2 = gh[i];
-    const int np2 = (heads[h2].nT_rows + 1) / 2;
-    e += max(0, np2 - 1 - pr);               // items of larger pairs
-    if (h2 < bh && np2 > pr) e += 1;          // same pair, earlier head
+  if (4ll * dm.L * dm.d >= HEAD_MAJOR_KV_BYTES) {
+    for (int i = G.head_begin; i < G.head_end; ++i) {
+      const int h2 = gh[i];
+      if (h2 < bh) e += (heads[h2].nT_rows + 1) / 2;   // every item of an earlier head
+    }
+    e += np - 1 - pr;                                   // larger pairs of this head
+  } else {
+    for (int i = G.head_begin; i < G.head_end; ++i) {
+      const int h2 = gh[i];
+      const int np2 = (heads[h2].nT_rows + 1) / 2;
+      e += max(0, np2 - 1 - pr);               // items of larger pairs
+      if (h2 < bh && np2 > pr) e += 1;          // same pair, earlier head
+    }
   }
   const int4 i0 = wsp<const int4>(ws, H.ws_info)[2 * pr];
   const int4 i1 = (2 * pr + 1 < H.nT_rows) ? wsp<const int4>(ws, H.ws_info)[2 * pr + 1] : make_int4(0, 0, 0, 0);
