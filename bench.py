@@ -34,7 +34,7 @@ from dynamic_sparse_attention_head_amd import mmsa, synth  # noqa: E402
 PEAK_BF16_TFLOPS = 2500.0     # MI355X dense bf16 MFMA
 PEAK_HBM_GBPS = 8000.0
 CSRC = os.path.join(ROOT, "dynamic_sparse_attention_head_amd", "csrc")
-ATTN_SOURCES = ("k_attention.hip", "mmsa_device.h", "mmsa_internal.h")
+ATTN_SOURCES = ("k_attention.hip", "mmsa_device.h", "mmsa_internal.h", "k_permute.hip")
 PROFILES = os.path.join(ROOT, "profiles")
 COPY_BYTES = 1 << 30
 
@@ -64,8 +64,9 @@ def est_bytes(spec):
 
 
 def attn_source_digest():
-    """sha256 over the attention kernel's sources: counter figures taken on
-    another version of the kernel are not reported."""
+    """sha256 over the attention kernel's sources and the plan kernels that
+    order its work queue: counter figures taken on another version of either
+    are not reported."""
     h = hashlib.sha256()
     for f in ATTN_SOURCES:
         with open(os.path.join(CSRC, f), "rb") as fh:

@@ -516,17 +516,20 @@ __global__ __launch_bounds__(256) void k_plan(Dims dm, Tables tb, char* ws) {
 // descending, then head: the most expensive pairs of a KV head come first, and
 // the attention kernel deals the order round-robin to the XCDs (queue position
 // e goes to XCD e % 8).
-// Once the K/V of one KV head (4·L·d bytes) reach half the 256 MB last-level
-// cache, a group is ordered by head, then pair descending: the workgroups
-// running at one time belong to one head, advance through its key tiles at
-// one pace and keep the part of K/V they share in that cache.  Unless every
-// head of the group is a block head (scattered key tiles), the order is also
-// dealt in runs of XCD_RUN consecutive pairs per XCD, so an XCD's workgroups
-// walk neighbouring pairs and share key tiles in its L2.  Measured against the
-// pair-interleaved order: 1M tokens 3560 -> 3160 ms, 314K 169 -> 158 ms, the
-// 256K block layer 52.9 -> 51.4 ms; at 128K the interleaved order is 4.3 %
-// faster (the heads of a pair share their key tiles there).
+// Groups whose heads walk long key prefixes (a vertical-slash or grid head
+// among them) are instead ordered by head, then pair descending, and dealt in
+// runs of XCD_RUN consecutive pairs per XCD once the K/V of the KV head (4·L·d
+// bytes) reach WALK_KV_BYTES: the workgroups running at one time then belong
+// to one head, an XCD's workgroups walk neighbouring pairs and share key tiles
+// in its L2, and the chip's advance through K/V stays within the 256 MB
+// last-level cache.  Other groups switch to the head-major order, still dealt
+// round-robin, only at HEAD_MAJOR_KV_BYTES (block heads select scattered
+// tiles, parallel-encoding heads short local ones; runs make both slower).
+// Measured against the interleaved order: 128K 75.9 -> 73.4 ms, 314K 169 ->
+// 158 ms, 1M 3560 -> 3160 ms, the 256K block layer (head-major only) 52.9 ->
+// 51.4 ms; with runs the 101K parallel-encoding layer took 11.4 ms, not 10.0.
 // ---------------------------------------------------------------------------
+constexpr int64_t WALK_KV_BYTES = 32ll << 20;
 constexpr int64_t HEAD_MAJOR_KV_BYTES = 128ll << 20;
 constexpr int XCD_RUN = 64;
 
@@ -542,15 +545,20 @@ __global__ __launch_bounds__(64) void k_queue_enum(Dims dm, Tables tb, char* ws)
   const QGroup G = wsp<const QGroup>(ws, tb.off_qgroups)[H.qgroup];
   const int32_t* gh = wsp<const int32_t>(ws, tb.off_qgroup_heads);
   int64_t e = G.item_base;
-  if (4ll * dm.L * dm.d >= HEAD_MAJOR_KV_BYTES) {
+  bool walk = false;
+  for (int i = G.head_begin; i < G.head_end; ++i) {
+    const int p = heads[gh[i]].pattern;
+    walk = walk || p == MMSA_VS || p == MMSA_GRID;
+  }
+  const int64_t kv_bytes = 4ll * dm.L * dm.d;
+  const bool runs = walk && kv_bytes >= WALK_KV_BYTES;
+  if (runs || kv_bytes >= HEAD_MAJOR_KV_BYTES) {
     int64_t n = 0;
-    bool all_block = true;
     for (int i = G.head_begin; i < G.head_end; ++i) {
       const int h2 = gh[i];
       const int np2 = (heads[h2].nT_rows + 1) / 2;
       if (h2 < bh) e += np2;                            // every item of an earlier head
       n += np2;
-      all_block = all_block && heads[h2].pattern == MMSA_BLOCK;
     }
     e += np - 1 - pr;                                   // larger pairs of this head
     // runs of XCD_RUN positions per XCD: within each whole block of 8 runs,
@@ -558,7 +566,7 @@ __global__ __launch_bounds__(64) void k_queue_enum(Dims dm, Tables tb, char* ws)
     // 8*XCD_RUN*sb + 8*i + x, which the kernel deals to XCD x (the tail of the
     // group keeps its order)
     const int64_t l = e - G.item_base, SB = 8ll * XCD_RUN;
-    if (!all_block && l < n / SB * SB) {
+    if (runs && l < n / SB * SB) {
       const int64_t sb = l / SB, rem = l % SB;
       e = G.item_base + sb * SB + (rem % XCD_RUN) * 8 + rem / XCD_RUN;
     }
