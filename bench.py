@@ -167,8 +167,8 @@ def main():
                          "instead of index-based loads and stores in the attention call")
     args = ap.parse_args()
     if args.gpus != 1:
-        print(f"bench.py runs on one GPU only (asked for --gpus {args.gpus}); the path shards by KV head "
-              f"without collectives but multi-GPU runs are not part of this build.", file=sys.stderr)
+        print(f"bench.py measures one GPU only (asked for --gpus {args.gpus}): the path would shard by KV "
+              f"head without collectives, but no multi-GPU launch is implemented.", file=sys.stderr)
         sys.exit(2)
     if args.copy_calibration:
         copy_calibration(max(args.steps, 1))
