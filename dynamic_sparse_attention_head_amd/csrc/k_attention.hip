@@ -302,22 +302,24 @@ __device__ __forceinline__ void attn_pair(AttnSmem<D>& sm, const Dims& dm, const
   };
 
   // Chunk sequence (uniform across the workgroup): the union of both tiles'
-  // key tiles, highest first -- workgroups on neighbouring query tiles then
-  // stream the same key tiles at about the same time and share them in L2, and
-  // the diagonal comes first -- then the gathered columns.
-  int wi = W;
+  // key tiles, then the gathered columns.  Key tiles go highest first --
+  // workgroups on neighbouring query tiles then stream the same key tiles at
+  // about the same time and share them in L2, and the diagonal comes first --
+  // or, when one KV head's K/V exceed the last-level cache, lowest first.
+  const bool asc = dm.chunk_asc != 0;
+  int wi = asc ? -1 : W;
   uint64_t bits = 0, wb0 = 0, wb1 = 0;
   auto next_chunk = [&](int ci) -> Chunk {
     Chunk c{0, 0, 0};
     if (ci >= n_chunks) return c;
     if (ci < n_union) {
-      while (bits == 0ull && wi > 0) {
-        --wi;
+      while (bits == 0ull && (asc ? wi < W - 1 : wi > 0)) {
+        wi += asc ? 1 : -1;
         wb0 = use0 ? bm0[wi] : 0ull;
         wb1 = use1 ? bm1[wi] : 0ull;
         bits = wb0 | wb1;
       }
-      const int b = bits ? 63 - __clzll((long long)bits) : -1;
+      const int b = bits ? (asc ? __builtin_ctzll(bits) : 63 - __clzll((long long)bits)) : -1;
       bits &= ~(1ull << (b & 63));
       c.src = -1;
       c.idx = b < 0 ? (view_rows + 63) / 64 : 64 * wi + b;   // (b < 0 only for a corrupt plan)

@@ -185,6 +185,8 @@ struct Dims {
   int64_t ws_enum_cost;      // int32 [n_items]: cost of each queued item
   int64_t ws_ctr;            // int32 [N_XCD] pop counters of the attention queue
   int64_t ws_flag;           // int32 debug / status word
+  int32_t chunk_asc;         // attention walks key tiles lowest first (else highest first)
+  int32_t _pad_dims;
 };
 
 // ---------------------------------------------------------------------------
