@@ -525,9 +525,12 @@ __global__ __launch_bounds__(256) void k_plan(Dims dm, Tables tb, char* ws) {
 // last-level cache.  Other groups switch to the head-major order, still dealt
 // round-robin, only at HEAD_MAJOR_KV_BYTES (block heads select scattered
 // tiles, parallel-encoding heads short local ones; runs make both slower).
-// Measured against the interleaved order: 128K 75.9 -> 73.4 ms, 314K 169 ->
-// 158 ms, 1M 3560 -> 3160 ms, the 256K block layer (head-major only) 52.9 ->
-// 51.4 ms; with runs the 101K parallel-encoding layer took 11.4 ms, not 10.0.
+// Runs are 128 pairs long when every head has at most 1024 pairs (each XCD
+// then takes one contiguous eighth of a head), else XCD_RUN.
+// Measured against the interleaved order: 128K 75.9 -> 73.4 ms (runs of 64;
+// 128 took 1.6 % off that), 314K 169 -> 158 ms, 1M 3560 -> 3160 ms, the 256K
+// block layer (head-major only) 52.9 -> 51.4 ms; with runs the 101K
+// parallel-encoding layer took 11.4 ms, not 10.0.
 // ---------------------------------------------------------------------------
 constexpr int64_t WALK_KV_BYTES = 32ll << 20;
 constexpr int64_t HEAD_MAJOR_KV_BYTES = 128ll << 20;
@@ -561,14 +564,17 @@ __global__ __launch_bounds__(64) void k_queue_enum(Dims dm, Tables tb, char* ws)
       n += np2;
     }
     e += np - 1 - pr;                                   // larger pairs of this head
-    // runs of XCD_RUN positions per XCD: within each whole block of 8 runs,
-    // local position l = 8*XCD_RUN*sb + XCD_RUN*x + i moves to
-    // 8*XCD_RUN*sb + 8*i + x, which the kernel deals to XCD x (the tail of the
-    // group keeps its order)
-    const int64_t l = e - G.item_base, SB = 8ll * XCD_RUN;
+    // runs of `run` positions per XCD: within each whole block of 8 runs,
+    // local position l = 8*run*sb + run*x + i moves to 8*run*sb + 8*i + x,
+    // which the kernel deals to XCD x (the tail of the group keeps its order)
+    int nmax = 0;
+    for (int i = G.head_begin; i < G.head_end; ++i) nmax = max(nmax, (heads[gh[i]].nT_rows + 1) / 2);
+    // heads of at most 8 runs of 128 pairs: one contiguous run per XCD and head
+    const int run = nmax <= 8 * 128 ? 128 : XCD_RUN;
+    const int64_t l = e - G.item_base, SB = 8ll * run;
     if (runs && l < n / SB * SB) {
       const int64_t sb = l / SB, rem = l % SB;
-      e = G.item_base + sb * SB + (rem % XCD_RUN) * 8 + rem / XCD_RUN;
+      e = G.item_base + sb * SB + (rem % run) * 8 + rem / run;
     }
   } else {
     for (int i = G.head_begin; i < G.head_end; ++i) {
