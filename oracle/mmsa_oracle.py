@@ -360,7 +360,7 @@ def estimate_head(cfg, qh, kh, segs, scale, scores_override=None):
         imax = int(rows.max())
         D = int(x[:imax + 1].max()) + 1
         v32 = ov.get('v', vx.astype(np.float32))
-        hi.extras.update(v=v32, D=D, n_rows=len(rows), stats=(mx, ssum))
+        hi.extras.update(v=v32, D=D, n_rows=len(rows), rows=rows, stats=(mx, ssum))
         hi.sigma, hi.phases = grid_rule(v32, D, len(rows), cfg.grid_clip or 8,
                                         cfg.stride_lo, cfg.stride_hi, cfg.grid_phases)
         hi.x = x

@@ -627,3 +627,110 @@ def test_segment_scores_and_tile_masks_by_loops():
 def test_permuted_equals_direct_vs_segment():
     segs = [(0, 100, 0), (100, 150, 1), (250, 37, 0), (287, 120, 1)]
     _check_perm(synth.vs(20, 9, 'q_segment'), 407, 16, segs, seed=7)
+
+
+# ---------------------------------------------------------------------------
+# Which side of the pooled logit is the query block ([MI] "Approach": each
+# 64-token query block attends to the mean-pooled key blocks).  The planted
+# directions live in dimensions the noise never touches, so every pooled
+# logit is exact and the expected selection follows from the construction.
+# ---------------------------------------------------------------------------
+def _planted_block_layer(nB=6, d=8, seed=0):
+    rng = np.random.default_rng(seed)
+    L = nB * TILE
+    q = np.zeros((L, d))
+    k = np.zeros((L, d))
+    q[:, 4:6] = rng.standard_normal((L, 2))          # noise only Q sees
+    k[:, 6:8] = rng.standard_normal((L, 2))          # noise only K sees
+    alpha = 2.0
+    # query block 4 aims at key block 1 along e0, query block 5 at key block 3
+    # along e1; every other query block points away from both (-e0 - e1)
+    for b in range(nB):
+        q[b * TILE:(b + 1) * TILE, 0:2] = -alpha / 2
+    q[4 * TILE:5 * TILE, 0:2] = (alpha, 0.0)
+    q[5 * TILE:6 * TILE, 0:2] = (0.0, alpha)
+    k[1 * TILE:2 * TILE, 0] = alpha
+    k[3 * TILE:4 * TILE, 1] = alpha
+    return q, k
+
+
+def test_block_selection_follows_the_query_block():
+    q, k = _planted_block_layer()
+    scale = 1 / math.sqrt(q.shape[1])
+    hi = O.estimate_head(synth.block(1), q, k, None, scale)
+    # rows 4 and 5 take their planted key block; every other row scores its
+    # reachable blocks 0 (plain) or below 0 (planted, pointing away) and takes
+    # the lowest tied block, 0
+    assert [list(b) for b in hi.blocks] == [[0], [0], [0], [0], [1], [3]]
+    z = hi.extras["z"]
+    assert z[4, 1] > 0 and z[5, 3] > 0
+    # the logit of (query block 1, key block 4) is the transposed entry: zero,
+    # since key block 4 carries no planted direction
+    assert z[1, 4] == 0.0
+    # top-2: row 4 keeps its planted block and the lowest plain one
+    hi2 = O.estimate_head(synth.block(2), q, k, None, scale)
+    assert list(hi2.blocks[4]) == [0, 1] and list(hi2.blocks[5]) == [0, 3]
+
+
+def test_block_selection_never_reaches_a_later_key_block():
+    # query block 2 aims at key block 4 (after it): causality c <= b keeps it out
+    q, k = _planted_block_layer()
+    q[2 * TILE:3 * TILE, 0:4] = (0.0, 0.0, 3.0, 0.0)
+    k[4 * TILE:5 * TILE, 2] = 3.0
+    hi = O.estimate_head(synth.block(1), q, k, None, 1 / math.sqrt(q.shape[1]))
+    assert list(hi.blocks[2]) == [0]
+    assert list(hi.blocks[4]) == [1]          # key block 4 attracts no other row either
+
+
+# ---------------------------------------------------------------------------
+# Grid estimation on the modality-grouped coordinate ([MMV] key_machinery:
+# stride and phase from the last 64 queries; core_discovery: modality-wise
+# permutation).  A period planted on video rank is evenly spaced only in the
+# grouped order (text first, then video): the text gap and the trailing text
+# are not multiples of it, so in original positions its phase jumps between
+# the two video segments, and the last 64 original positions are text rows
+# that carry no period at all.
+# ---------------------------------------------------------------------------
+def _grouped_period_layer(P=20, phi=7, seed=4, d=16, amp=3.0):
+    segs = [(0, 200, 1), (200, 37, 0), (237, 200, 1), (437, 90, 0)]
+    L = 527
+    rng = np.random.default_rng(seed)
+    q = rng.standard_normal((L, d)) * 0.5
+    k = rng.standard_normal((L, d)) * 0.5
+    u = np.zeros(d)
+    u[0] = 1.0
+    video = np.concatenate([np.arange(0, 200), np.arange(237, 437)])   # ascending = video rank order
+    planted = video[np.arange(video.size) % P == phi]
+    k[planted] += amp * u
+    q[video] += amp * u
+    return q, k, segs, video, planted
+
+
+def test_grouped_grid_recovers_a_period_across_text_gaps():
+    P, phi = 20, 7
+    q, k, segs, video, planted = _grouped_period_layer(P, phi)
+    n_text = 37 + 90
+    cfg = synth.grid(1, 16, 64, layout='modality_grouped')
+    hi = O.estimate_head(cfg, q, k, segs, 1 / math.sqrt(q.shape[1]))
+    # the estimation rows are the last 64 video queries (the last 64 of the
+    # grouped order), not the last 64 positions (text)
+    assert list(hi.extras["rows"]) == list(video[-64:])
+    # the grouped coordinate of video rank r is n_text + r
+    assert hi.sigma == P
+    assert list(hi.phases) == [(n_text + phi) % P]
+    line = np.isin(hi.x % hi.sigma, hi.phases)
+    assert sorted(video[line[video]]) == sorted(planted)      # among video keys: exactly the planted ones
+    # the line scores sit at the grouped coordinates of the planted keys
+    v = hi.extras["v"]
+    xs = n_text + np.arange(video.size)
+    top = np.argsort(-v.astype(np.float64), kind='stable')[:planted.size]
+    assert sorted(top) == sorted(xs[np.arange(video.size) % P == phi])
+
+
+def test_plain_grid_on_the_same_layer_sees_original_positions():
+    # without the grouping, the coordinate is the original position and the
+    # estimation rows are the last 64 positions: the text rows at the end
+    q, k, segs, video, planted = _grouped_period_layer()
+    hi = O.estimate_head(synth.grid(1, 16, 64), q, k, segs, 1 / math.sqrt(q.shape[1]))
+    assert list(hi.extras["rows"]) == list(range(527 - 64, 527))
+    assert list(hi.x) == list(range(527))
