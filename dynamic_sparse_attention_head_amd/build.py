@@ -48,7 +48,44 @@ def _compile(src, obj, extra):
     return obj
 
 
-def build(verbose=False, extra=()):
+ASAN_LIB = os.path.join(BUILD, "asan", "libmmsa_asan.so")
+
+
+def asan_runtime():
+    """Path of the compiler's AddressSanitizer runtime (to preload into the
+    host process that loads the ASan build), or None."""
+    r = subprocess.run([hipcc(), "-print-file-name=libclang_rt.asan-x86_64.so"], capture_output=True, text=True)
+    p = r.stdout.strip()
+    return p if r.returncode == 0 and os.path.isabs(p) and os.path.exists(p) else None
+
+
+def build_asan(objs, verbose=False):
+    """The same library with its host layer (argument validation, workspace
+    layout, table building: csrc/mmsa_api.hip) built under AddressSanitizer.
+    Only host code is instrumented (-Xarch_host); the kernels are the regular
+    objects.  Loaded by the ABI tests through MMSA_LIB with the ASan runtime
+    preloaded."""
+    os.makedirs(os.path.dirname(ASAN_LIB), exist_ok=True)
+    obj = os.path.join(os.path.dirname(ASAN_LIB), "mmsa_api_asan.o")
+    host_asan = "-Xarch_host -fsanitize=address -Xarch_host -fno-omit-frame-pointer".split()
+    cmd = [hipcc(), *HIPCC_FLAGS, "-g", *host_asan, "-c", os.path.join(CSRC, "mmsa_api.hip"), "-o", obj]
+    r = subprocess.run(cmd, capture_output=True, text=True)
+    if r.returncode != 0:
+        raise RuntimeError(f"hipcc (host ASan) failed:\n{r.stdout}\n{r.stderr}")
+    others = [o for o in objs if os.path.basename(o) != "mmsa_api.o"]
+    tmp = ASAN_LIB + ".tmp"
+    cmd = [hipcc(), f"--offload-arch={ARCH}", "-shared", "-fPIC", *"-Xarch_host -fsanitize=address".split(),
+           "-shared-libsan", "-o", tmp, obj, *others]
+    r = subprocess.run(cmd, capture_output=True, text=True)
+    if r.returncode != 0:
+        raise RuntimeError(f"link (host ASan) failed:\n{r.stdout}\n{r.stderr}")
+    os.replace(tmp, ASAN_LIB)
+    if verbose:
+        print(f"built {ASAN_LIB}")
+    return ASAN_LIB
+
+
+def build(verbose=False, extra=(), asan=True):
     os.makedirs(BUILD, exist_ok=True)
     srcs = sorted(f for f in os.listdir(CSRC) if f.endswith(".hip"))
     objs = []
@@ -67,6 +104,8 @@ def build(verbose=False, extra=()):
     os.replace(tmp, LIB)
     if verbose:
         print(f"built {LIB}")
+    if asan:
+        build_asan(objs, verbose=verbose)
     return LIB
 
 

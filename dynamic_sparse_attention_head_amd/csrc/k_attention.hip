@@ -204,11 +204,26 @@ __device__ __forceinline__ void attn_pair(AttnSmem<D>& sm, const Dims& dm, const
   // context block, 0 for its sink and question rows; other patterns: no bound
   // (INT_MIN).  Both are taken once here, through empty asm, so the chunk
   // loop neither recomputes them nor branches on the pattern per element.
+  // Grid heads with a sink or a local window: rows off the lines take the
+  // A-shape rule on the key tiles (klo = i - window + 1, or no window at all),
+  // line rows see every causal key (klo = INT_MIN).  Their gathered chunks hold
+  // line keys, of which those already inside the sink or the row's window sit
+  // in a listed tile too: there the rule is inverted (kept when j >= sink and
+  // j < klo), so each key counts once.
   const bool ashape = H.pattern == MMSA_ASHAPE, parallel = H.pattern == MMSA_PARALLEL;
-  int windowed = uniform((ashape || parallel) ? 1 : 0);
+  const bool gridwin = grid && (H.sink > 0 || H.window > 0);
+  int grid_line_row = 0;
+  if (gridwin) {
+    const int nline = wsp<const int32_t>(ws, cptr<GridTask>(ws, tb.off_grid)[H.grid_task].ws_out)[2];
+    grid_line_row = slot < ((nline + 63) & ~63);
+  }
+  int windowed = uniform((ashape || parallel || gridwin) ? 1 : 0);
   asm volatile("" : "+s"(windowed));
   const int sink = H.sink;
-  int klo = ashape ? qpos - H.window + 1 : parallel ? par_floor(H.sink, H.window, H.qstart, qpos) : INT_MIN;
+  int klo = ashape ? qpos - H.window + 1
+            : parallel ? par_floor(H.sink, H.window, H.qstart, qpos)
+            : gridwin ? (grid_line_row ? INT_MIN : H.window > 0 ? qpos - H.window + 1 : INT_MAX)
+            : INT_MIN;
   asm volatile("" : "+v"(klo));
   // the largest klo of the wave's rows: a chunk whose keys all lie at or past
   // it (and before the first row) needs no mask
@@ -248,9 +263,11 @@ __device__ __forceinline__ void attn_pair(AttnSmem<D>& sm, const Dims& dm, const
   auto dma_k = [&](const Chunk& c, int par, int ks) {
     char* dst = kbuf0 + par * BUFB + (w * PPW) * 1024;
     if (c.src < 0 && !grouped_idx) {
+      // the tile's row offset goes into the vector offset, which the buffer's
+      // range check covers: rows past the view's end read as zeros
       const uint32_t s0 = (uint32_t)(64 * c.idx) * rb_view;
 #pragma unroll
-      for (int p = 0; p < PPW; ++p) dma16(rk_view, dst + p * 1024, kro + lchk(p), s0 + (uint32_t)(p * RPI) * rb_view);
+      for (int p = 0; p < PPW; ++p) dma16(rk_view, dst + p * 1024, kro + lchk(p) + s0 + (uint32_t)(p * RPI) * rb_view, 0);
     } else {
       int gi[PPW];
 #pragma unroll
@@ -265,7 +282,7 @@ __device__ __forceinline__ void attn_pair(AttnSmem<D>& sm, const Dims& dm, const
     if (c.src < 0 && !grouped_idx) {
       const uint32_t s0 = (uint32_t)(64 * c.idx) * rbv_view;
 #pragma unroll
-      for (int p = 0; p < PPW; ++p) dma16(rv_view, dst + p * 1024, vro + lchk(p), s0 + (uint32_t)(p * RPI) * rbv_view);
+      for (int p = 0; p < PPW; ++p) dma16(rv_view, dst + p * 1024, vro + lchk(p) + s0 + (uint32_t)(p * RPI) * rbv_view, 0);
     } else {
       int gi[PPW];
 #pragma unroll
@@ -410,10 +427,11 @@ __device__ __forceinline__ void attn_pair(AttnSmem<D>& sm, const Dims& dm, const
   };
   // mask and running-max update of one chunk's logits (the part of the softmax
   // that may branch); returns the max to subtract
-  auto soft_a = [&](floatx16 (&sa)[2], int ks) -> float {
+  auto soft_a = [&](floatx16 (&sa)[2], int ks, bool inv) -> float {
     const int kmx = uniform(sm.kmax[ks]);
     bool full = kmx <= wave_qmin;
     if (windowed) full = full && (kmx < sink || uniform(sm.kmin[ks]) >= wave_klomax);
+    full = full && !inv;
     if (!full) {
       // one lane-dependent base, constant offsets per (kb, i)
       const char* kpb = reinterpret_cast<const char*>(sm.kp[0]) + ks * 256 + 16 * hh;
@@ -425,7 +443,7 @@ __device__ __forceinline__ void attn_pair(AttnSmem<D>& sm, const Dims& dm, const
           const int kpv[4] = {kk.x, kk.y, kk.z, kk.w};
 #pragma unroll
           for (int j = 0; j < 4; ++j) {
-            const bool ok = (kpv[j] <= qpos) & ((kpv[j] < sink) | (kpv[j] >= klo));
+            const bool ok = (kpv[j] <= qpos) & (((kpv[j] < sink) | (kpv[j] >= klo)) != inv);
             sa[kb][4 * i + j] = ok ? sa[kb][4 * i + j] : -INFINITY;
           }
         }
@@ -550,7 +568,7 @@ __device__ __forceinline__ void attn_pair(AttnSmem<D>& sm, const Dims& dm, const
     const bool doS = wave_has && has_n1 && (c1.memb & wbit);
     const bool doP = wave_has && (c0.memb & wbit);
     if (doP) {
-      const float m_use = soft_a(scur, n & 3);
+      const float m_use = soft_a(scur, n & 3, gridwin && c0.src >= 0);
       uint32_t pk[16];
       // The two branches compute the same probabilities; each takes the max
       // through its own (different) empty asm, so the compiler cannot hoist
@@ -600,6 +618,28 @@ __device__ __forceinline__ void attn_pair(AttnSmem<D>& sm, const Dims& dm, const
       const float val = l_tot > 0.f ? (m_run + log2f(l_tot)) * 0.69314718055994531f : -INFINITY;
       lse[((int64_t)H.b * dm.Hq + H.h) * dm.L + qpos] = val;
     }
+  }
+  if (dm.debug) {
+    // MMSA_FLAG_DEBUG: a non-finite output element (or a non-finite row sum,
+    // which makes the LSE +inf or NaN) sets bit 3 of the debug word.  This
+    // file is built without NaN semantics, under which the compiler may read
+    // an exponent test on a float's bits as "is infinite"; the bits therefore
+    // pass through an empty asm first, which hides where they came from.
+    const float inv = l_tot > 0.f ? 1.0f / l_tot : 0.f;
+    auto nonfinite = [](float x) {
+      uint32_t u = __float_as_uint(x);
+      asm volatile("" : "+v"(u));
+      return (u & 0x7f800000u) == 0x7f800000u;
+    };
+    bool bad = false;
+    if (qpos >= 0) {
+#pragma unroll
+      for (int db = 0; db < ND; ++db)
+#pragma unroll
+        for (int e = 0; e < 16; ++e) bad |= nonfinite(oacc[db][e] * inv);
+      bad |= nonfinite(l_tot);
+    }
+    if (__ballot(bad) != 0ull && lane == 0) atomicOr(wsp<uint32_t>(ws, dm.ws_flag), 8u);
   }
 }
 

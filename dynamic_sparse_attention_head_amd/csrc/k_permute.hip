@@ -327,8 +327,17 @@ __global__ __launch_bounds__(256) void k_plan(Dims dm, Tables tb, char* ws) {
     const int nl_pad = (grid_nline + 63) & ~63;
     grid_is_line = (64 * t) < nl_pad;
     grid_lines = wsp<const int32_t>(ws, H.ws_row_order);
-    if (grid_is_line) bm_set_range(bm, 0, qmax >> 6);
-    else g_cnt = count_le(grid_lines, grid_nline, qmax);
+    if (grid_is_line) {
+      bm_set_range(bm, 0, qmax >> 6);
+    } else {
+      // the line keys up to the tile's last row are gathered; a sink and a
+      // local window add their key tiles (line keys inside those tiles are
+      // masked out of the gathered chunks by the attention kernel)
+      g_cnt = count_le(grid_lines, grid_nline, qmax);
+      const int tmax = qmax >> 6;
+      if (H.sink > 0) bm_set_range(bm, 0, min((H.sink + 63) / 64, tmax + 1) - 1);
+      if (H.window > 0) bm_set_range(bm, max(0, qmin - H.window + 1) >> 6, tmax);
+    }
   } else {  // vertical-slash family
     const bool twod = H.layout == MMSA_BOUNDARY_2D;
     const bool grouped_rows = H.row_kind == ROW_GROUPED;
@@ -459,7 +468,20 @@ __global__ __launch_bounds__(256) void k_plan(Dims dm, Tables tb, char* ws) {
       const bool ctx = p >= H.sink && p < H.qstart;
       my_pairs = ctx ? (long long)H.sink + (p - par_floor(H.sink, H.window, H.qstart, p) + 1) : (long long)(p + 1);
     } else if (H.pattern == MMSA_GRID) {
-      my_pairs = grid_is_line ? (p + 1) : count_le(grid_lines, grid_nline, p);
+      const int lines_le_p = count_le(grid_lines, grid_nline, p);
+      my_pairs = grid_is_line ? (p + 1) : lines_le_p;
+      if (!grid_is_line && (H.sink > 0 || H.window > 0)) {
+        // keys of the sink [0, s_end) and the window [w0, p] that are not line keys
+        const int s_end = min(H.sink, p + 1);
+        const int w0 = H.window > 0 ? max(0, p - H.window + 1) : p + 1;
+        if (s_end >= w0) {
+          my_pairs += (p + 1) - lines_le_p;
+        } else {
+          const int lines_in = count_le(grid_lines, grid_nline, s_end - 1) + lines_le_p -
+                               count_le(grid_lines, grid_nline, w0 - 1);
+          my_pairs += s_end + (p - w0 + 1) - lines_in;
+        }
+      }
     } else if (H.view_kind == VIEW_IDENTITY) {
       const int cp = p >> 6;
       my_pairs = 64ll * bm_popc_below(bm, cp) + (bm_get(bm, cp) ? (p - 64 * cp + 1) : 0);

@@ -10,6 +10,7 @@
 #include <cstdarg>
 #include <cstdio>
 #include <cstring>
+#include <mutex>
 #include <string>
 #include <vector>
 
@@ -146,8 +147,13 @@ mmsa_status build_layout(const mmsa_layer_desc* desc, Layout& Lo) {
     set_err("head dimension d=%d is not supported (64 or 128)", D.d);
     return MMSA_UNSUPPORTED;
   }
-  if ((D.flags & ~MMSA_FLAG_MATERIALIZE) != 0) {
-    set_err("flags must be 0 or MMSA_FLAG_MATERIALIZE");
+  const uint32_t known = MMSA_FLAG_MATERIALIZE | MMSA_FLAG_DEBUG | MMSA_FLAG_KEYS_ASCENDING | MMSA_FLAG_KEYS_DESCENDING;
+  if ((D.flags & ~known) != 0) {
+    set_err("flags 0x%x hold bits outside the MMSA_FLAG_* set", D.flags);
+    return MMSA_INVALID_ARGUMENT;
+  }
+  if ((D.flags & MMSA_FLAG_KEYS_ASCENDING) && (D.flags & MMSA_FLAG_KEYS_DESCENDING)) {
+    set_err("MMSA_FLAG_KEYS_ASCENDING and MMSA_FLAG_KEYS_DESCENDING are exclusive");
     return MMSA_INVALID_ARGUMENT;
   }
   if (D.L >= (1 << 22)) {
@@ -247,6 +253,10 @@ mmsa_status build_layout(const mmsa_layer_desc* desc, Layout& Lo) {
       }
     }
     if (c.pattern == MMSA_GRID) {
+      if (c.sink < 0 || c.window < 0) {
+        set_err("head %d: grid needs sink >= 0 and window >= 0", h);
+        return MMSA_INVALID_ARGUMENT;
+      }
       if (c.grid_clip == 0) c.grid_clip = 8;
       if (c.grid_phases < 1 || c.grid_phases > MAX_PHASES || c.stride_lo < 16 || c.stride_hi < c.stride_lo ||
           c.stride_hi > MAX_STRIDE || c.grid_clip < 1 || c.grid_clip > 64) {
@@ -310,7 +320,9 @@ mmsa_status build_layout(const mmsa_layer_desc* desc, Layout& Lo) {
   // tokens: 3186 -> 3086 ms; at 128K-314K, and on the 256K block layer, the
   // highest-first order measured equal or faster).
   dm.chunk_asc = 4ll * D.L * D.d > (256ll << 20) ? 1 : 0;
-  dm._pad_dims = 0;
+  if (D.flags & MMSA_FLAG_KEYS_ASCENDING) dm.chunk_asc = 1;
+  if (D.flags & MMSA_FLAG_KEYS_DESCENDING) dm.chunk_asc = 0;
+  dm.debug = (D.flags & MMSA_FLAG_DEBUG) ? 1 : 0;
   dm.q_sb = D.q_strides[0];
   dm.q_sh = D.q_strides[1];
   dm.q_sl = D.q_strides[2];
@@ -910,6 +922,48 @@ mmsa_status hip_status(hipError_t e, const char* where) {
   return MMSA_HIP_ERROR;
 }
 
+// Architecture and compute-unit count of each device, looked up once.  The
+// kernels use gfx950-only instructions (32x32x16 bf16 MFMA, buffer-to-LDS
+// copies, LDS transpose reads, permlane swaps), so any other device is refused
+// before anything is enqueued.
+struct DevInfo {
+  int state = 0;   // 0 unknown, 1 gfx950, -1 another architecture
+  int n_cu = 0;
+  char arch[64] = {0};
+};
+
+mmsa_status check_device(int* n_cu_out = nullptr) {
+  static std::mutex mu;
+  static std::vector<DevInfo> info;
+  int dev = -1;
+  const hipError_t e = hipGetDevice(&dev);
+  if (e != hipSuccess || dev < 0) {
+    set_err("no gfx950 device: %s", hipGetErrorString(e));
+    return MMSA_UNSUPPORTED;
+  }
+  std::lock_guard<std::mutex> lock(mu);
+  if ((int)info.size() <= dev) info.resize(dev + 1);
+  DevInfo& di = info[dev];
+  if (di.state == 0) {
+    hipDeviceProp_t p;
+    const hipError_t e2 = hipGetDeviceProperties(&p, dev);
+    if (e2 != hipSuccess) {
+      set_err("device %d properties: %s", dev, hipGetErrorString(e2));
+      return MMSA_HIP_ERROR;
+    }
+    std::snprintf(di.arch, sizeof di.arch, "%s", p.gcnArchName);
+    const char* a = p.gcnArchName;
+    di.state = (std::strncmp(a, "gfx950", 6) == 0 && (a[6] == 0 || a[6] == ':')) ? 1 : -1;
+    di.n_cu = p.multiProcessorCount;
+  }
+  if (di.state < 0) {
+    set_err("device %d is %s; libmmsa runs on gfx950 only", dev, di.arch);
+    return MMSA_UNSUPPORTED;
+  }
+  if (n_cu_out) *n_cu_out = di.n_cu;
+  return MMSA_OK;
+}
+
 mmsa_status upload(const Layout& Lo, void* ws, hipStream_t s) {
   return hip_status(hipMemcpyAsync(ws, Lo.blob.data(), Lo.blob.size(), hipMemcpyHostToDevice, s), "table upload");
 }
@@ -1003,6 +1057,7 @@ mmsa_status mmsa_workspace_view(const mmsa_layer_desc* desc, int32_t buf, int32_
       if (J) *offset_bytes = J->ws_stats, *count = 2 * EST_ROWS;
       break;
     case MMSA_BUF_TILE_BITMAP: *offset_bytes = H.ws_bm, *count = (int64_t)H.nT_rows * H.bm_words; break;
+    case MMSA_BUF_DEBUG_FLAGS: *offset_bytes = Lo.dm.ws_flag, *count = 1; break;
     default: set_err("unknown buffer %d", buf); return MMSA_INVALID_ARGUMENT;
   }
   return MMSA_OK;
@@ -1049,6 +1104,7 @@ mmsa_status mmsa_estimate_vs(const mmsa_layer_desc* desc, const void* q, const v
   if (Lo.empty || Lo.jobs.empty()) return MMSA_OK;
   MMSA_TRY(check_ptr(q, "q"));
   MMSA_TRY(check_ptr(k, "k"));
+  MMSA_TRY(check_device());
   hipStream_t s = (hipStream_t)stream;
   char* w = (char*)ws;
   MMSA_TRY(upload(Lo, ws, s));
@@ -1068,6 +1124,7 @@ mmsa_status mmsa_estimate_blocks(const mmsa_layer_desc* desc, const void* q, con
   if (Lo.empty || !Lo.any_block) return MMSA_OK;
   MMSA_TRY(check_ptr(q, "q"));
   MMSA_TRY(check_ptr(k, "k"));
+  MMSA_TRY(check_device());
   hipStream_t s = (hipStream_t)stream;
   MMSA_TRY(upload(Lo, ws, s));
   MMSA_HIP(launch_block_estimate(Lo.dm, Lo.tb, (char*)ws, q, k, Lo.nB, s), "block estimation");
@@ -1082,9 +1139,14 @@ mmsa_status mmsa_permute(const mmsa_layer_desc* desc, const void* q, const void*
   MMSA_TRY(check_ptr(q, "q"));
   MMSA_TRY(check_ptr(k, "k"));
   MMSA_TRY(check_ptr(v, "v"));
+  MMSA_TRY(check_device());
   hipStream_t s = (hipStream_t)stream;
   char* w = (char*)ws;
   MMSA_TRY(upload(Lo, ws, s));
+  if (Lo.dm.debug) {
+    MMSA_HIP(launch_fill_u32(w + Lo.dm.ws_flag, 0u, 1, s), "debug word clear");
+    MMSA_HIP(launch_nonfinite_scan(Lo.dm, w, q, k, v, s), "non-finite scan");
+  }
   if (Lo.need_seg) MMSA_HIP(launch_seg_tables(Lo.dm, Lo.tb, w, s), "segment tables");
   if (Lo.gridrow_bytes > 0) {
     MMSA_HIP(launch_fill_u32(w + Lo.gridrow_off, 0xffffffffu, Lo.gridrow_bytes / 4, s), "row order clear");
@@ -1104,11 +1166,10 @@ mmsa_status mmsa_sparse_prefill(const mmsa_layer_desc* desc, const void* q, cons
   MMSA_TRY(check_ptr(k, "k"));
   MMSA_TRY(check_ptr(v, "v"));
   MMSA_TRY(check_ptr(o, "o"));
+  int n_cu = 0;
+  MMSA_TRY(check_device(&n_cu));
   hipStream_t s = (hipStream_t)stream;
   MMSA_TRY(upload(Lo, ws, s));
-  int dev = 0, n_cu = 0;
-  MMSA_HIP(hipGetDevice(&dev), "hipGetDevice");
-  MMSA_HIP(hipDeviceGetAttribute(&n_cu, hipDeviceAttributeMultiprocessorCount, dev), "CU count");
   // the pop counters start at zero on every call, so the call can be repeated
   MMSA_HIP(launch_queue_reset(Lo.dm, (char*)ws, s), "queue reset");
   // two resident workgroups per CU (the kernel's LDS and register budget)
@@ -1121,6 +1182,7 @@ mmsa_status mmsa_unpermute(const mmsa_layer_desc* desc, void* ws, size_t ws_byte
   MMSA_TRY(prepare(desc, ws, ws_bytes, Lo));
   if (Lo.empty) return MMSA_OK;
   MMSA_TRY(check_ptr(o, "o"));
+  MMSA_TRY(check_device());
   hipStream_t s = (hipStream_t)stream;
   MMSA_TRY(upload(Lo, ws, s));
   MMSA_HIP(launch_unpermute(Lo.dm, Lo.tb, (char*)ws, o, Lo.max_unperm_slots, s), "unpermute");

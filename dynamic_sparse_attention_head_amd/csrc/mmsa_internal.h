@@ -184,9 +184,9 @@ struct Dims {
   int64_t ws_enum_item;      // int32 [n_items]: (bh << 16) | pair in queue order
   int64_t ws_enum_cost;      // int32 [n_items]: cost of each queued item
   int64_t ws_ctr;            // int32 [N_XCD] pop counters of the attention queue
-  int64_t ws_flag;           // int32 debug / status word
+  int64_t ws_flag;           // uint32 debug word (MMSA_FLAG_DEBUG)
   int32_t chunk_asc;         // attention walks key tiles lowest first (else highest first)
-  int32_t _pad_dims;
+  int32_t debug;             // MMSA_FLAG_DEBUG: record non-finite inputs / outputs in the word at ws_flag
 };
 
 // ---------------------------------------------------------------------------
@@ -215,5 +215,10 @@ hipError_t launch_queue_reset(const Dims& dm, char* ws, hipStream_t s);
 hipError_t launch_attention(const Dims& dm, const Tables& tb, char* ws, const void* q, const void* k,
                             const void* v, void* o, float* lse, int n_workgroups, hipStream_t s);
 hipError_t launch_unpermute(const Dims& dm, const Tables& tb, char* ws, void* o, int max_slots, hipStream_t s);
+
+// MMSA_FLAG_DEBUG: OR into the word at ws_flag bit 0 / 1 / 2 when Q / K / V
+// holds a NaN or an infinity
+hipError_t launch_nonfinite_scan(const Dims& dm, char* ws, const void* q, const void* k, const void* v,
+                                 hipStream_t s);
 
 }  // namespace mmsa

@@ -13,18 +13,20 @@ import os
 import torch
 
 _HERE = os.path.dirname(os.path.abspath(__file__))
-LIB_PATH = os.path.join(_HERE, "libmmsa.so")
+# MMSA_LIB names another build of the same library (the host-AddressSanitizer
+# build the ABI tests run under); by default the in-tree libmmsa.so
+LIB_PATH = os.environ.get("MMSA_LIB") or os.path.join(_HERE, "libmmsa.so")
 
 TILE = 64
 OK, INVALID_ARGUMENT, UNSUPPORTED, WORKSPACE_TOO_SMALL, HIP_ERROR = range(5)
 PATTERNS = {"ashape": 0, "vs": 1, "block": 2, "grid": 3, "parallel": 4}
 LAYOUTS = {"plain": 0, "q_boundary": 1, "boundary_2d": 2, "modality_grouped": 3, "q_segment": 4}
 BUF = dict(v_scores=0, s_scores=1, v_index=2, s_index=3, nsel=4, grid=5, block_index=6, block_scores=7,
-           row_order=8, tile_pairs=9, tile_info=10, est_stats=11, tile_bitmap=12)
+           row_order=8, tile_pairs=9, tile_info=10, est_stats=11, tile_bitmap=12, debug_flags=13)
 BUF_DTYPE = dict(v_scores=torch.float32, s_scores=torch.float32, v_index=torch.int32, s_index=torch.int32,
                  nsel=torch.int32, grid=torch.int32, block_index=torch.int32, block_scores=torch.float32,
                  row_order=torch.int32, tile_pairs=torch.int64, tile_info=torch.int32, est_stats=torch.float32,
-                 tile_bitmap=torch.int64)
+                 tile_bitmap=torch.int64, debug_flags=torch.int32)
 
 
 class HeadCfg(ctypes.Structure):
@@ -38,7 +40,11 @@ class Segment(ctypes.Structure):
                 ("_pad", ctypes.c_int32)]
 
 
-FLAG_MATERIALIZE = 1   # mmsa_layer_desc.flags: explicit gathers and output scatter
+# mmsa_layer_desc.flags
+FLAG_MATERIALIZE = 1        # explicit gathers and output scatter
+FLAG_DEBUG = 2              # record non-finite inputs / outputs in the debug word
+FLAG_KEYS_ASCENDING = 4     # attention walks key tiles lowest first
+FLAG_KEYS_DESCENDING = 8    # attention walks key tiles highest (diagonal) first
 
 
 class LayerDesc(ctypes.Structure):
@@ -110,7 +116,7 @@ def head_cfg(d):
     c.pattern = PATTERNS[d["pattern"]]
     c.layout = LAYOUTS[d.get("layout", "plain")]
     c.sink = int(d.get("sink", 0))
-    c.window = int(d.get("window", 1))
+    c.window = int(d.get("window", 0 if d["pattern"] == "grid" else 1))
     c.k_vertical = int(d.get("k_vertical", 0))
     c.k_slash = int(d.get("k_slash", 0))
     c.k_blocks = int(d.get("k_blocks", 0))
@@ -138,10 +144,11 @@ class Layer:
     budgets per q head); segs: list of (start, len, modality) or None.
     materialize: copy permuted Q / grouped K,V into the workspace and scatter
     O back in unpermute (MMSA_FLAG_MATERIALIZE) instead of index-based loads
-    and stores inside the attention call."""
+    and stores inside the attention call.  flags: further MMSA_FLAG_* bits
+    (FLAG_DEBUG, FLAG_KEYS_ASCENDING, FLAG_KEYS_DESCENDING)."""
 
     def __init__(self, q, k, v, heads, segs=None, scale=None, kv_head_of=None, o_strides=None,
-                 shape=None, device=None, materialize=False):
+                 shape=None, device=None, materialize=False, flags=0):
         if q is not None:
             B, Hq, L, d = q.shape
             Hkv = k.shape[1]
@@ -167,7 +174,7 @@ class Layer:
         desc.v_strides[:] = _strides(v, B, Hkv, L, d)
         desc.o_strides[:] = o_strides if o_strides is not None else (Hq * L * d, L * d, d)
         desc.scale = float(scale) if scale is not None else 0.0
-        desc.flags = FLAG_MATERIALIZE if materialize else 0
+        desc.flags = (FLAG_MATERIALIZE if materialize else 0) | int(flags)
         desc.kv_head_of = self._kvmap
         desc.heads = self._cfg
         desc.segs = self._segs

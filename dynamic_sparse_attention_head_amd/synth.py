@@ -184,8 +184,11 @@ def block(kb):
     return dict(pattern='block', layout='plain', k_blocks=kb)
 
 
-def grid(w=1, lo=64, hi=512, clip=8, layout='plain'):
-    return dict(pattern='grid', layout=layout, grid_phases=w, stride_lo=lo, stride_hi=hi, grid_clip=clip)
+def grid(w=1, lo=64, hi=512, clip=8, layout='plain', sink=0, window=0):
+    """Grid head; sink / window > 0 add a sink and a local window to the rows
+    that are not on a line."""
+    return dict(pattern='grid', layout=layout, grid_phases=w, stride_lo=lo, stride_hi=hi, grid_clip=clip,
+                sink=sink, window=window)
 
 
 def parallel(sink, block, question):
@@ -225,7 +228,7 @@ def scene_cut(frames=40, per=196, text=512, cut=True, targets=64, amp=10.0, head
 
 
 def config(i, L=None, seed=None):
-    """The seven named workloads (1-based), optionally shortened to L tokens
+    """The eight named workloads (1-based), optionally shortened to L tokens
     (structure kept, sizes scaled) for parity tests the oracle finishes fast."""
     s = i if seed is None else seed
     if i == 1:
@@ -289,6 +292,14 @@ def config(i, L=None, seed=None):
             else:
                 heads.append(vs(kv, ks, 'plain'))
         return LayerSpec('mixed-1m', L_, 32, 8, 128, s, heads, segs=segs, period=per)
+    if i == 8:
+        # the video grid layer with its grid heads widened by a sink (the text
+        # prompt) and a local window of four frames on the rows off the lines
+        base = config(4, L=L, seed=s)
+        per = base.period
+        sink, window = (512, 4 * 196) if L is None else (64, 4 * per)
+        heads = [dict(h, sink=sink, window=window) if h['pattern'] == 'grid' else h for h in base.heads]
+        return replace(base, name='qwen2-7b-video-314k-window', heads=heads)
     if i == 7:
         # the 1M mixed layer with per-segment estimation in place of the
         # per-modality (Q-boundary) heads: 15 segments, 15 estimates per head

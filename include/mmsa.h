@@ -32,7 +32,11 @@
  *    on any error nothing is launched or written, and mmsa_last_error() gives
  *    a thread-local message.  No C++ exception crosses this interface.
  *  - Budgets above the number of candidates are clamped, not errors.
- *  - NaN or Inf in Q/K/V give undefined (but memory-safe) results.
+ *  - NaN or Inf in Q/K/V give undefined (but memory-safe) results; with
+ *    MMSA_FLAG_DEBUG the calls record that they met one (see below).
+ *  - Device: gfx950 only.  Every call that enqueues work first checks the
+ *    architecture of the current HIP device and returns MMSA_UNSUPPORTED, with
+ *    nothing enqueued, on any other device or when there is none.
  *  - Limits: L < 2^22 tokens (tile indices are packed in 16 bits), B*Hq <= 4096;
  *    BLOCK heads need L <= 2^20 (one pooled-logit row per query block in LDS).
  */
@@ -46,7 +50,7 @@
 extern "C" {
 #endif
 
-#define MMSA_ABI_VERSION 3
+#define MMSA_ABI_VERSION 4
 #define MMSA_TILE 64       /* query and key tile (the 64-token blocks)      */
 #define MMSA_EST_ROWS 64   /* estimation rows: the last 64 queries          */
 
@@ -54,7 +58,7 @@ typedef int32_t mmsa_status;
 enum {
   MMSA_OK = 0,
   MMSA_INVALID_ARGUMENT = 1,  /* null pointer, shape, stride, budget, segments, combination */
-  MMSA_UNSUPPORTED = 2,       /* d, alignment, size limits                                  */
+  MMSA_UNSUPPORTED = 2,       /* d, alignment, size limits, device architecture             */
   MMSA_WORKSPACE_TOO_SMALL = 3,
   MMSA_HIP_ERROR = 4          /* a launch failed; detail in mmsa_last_error()               */
 };
@@ -95,15 +99,34 @@ enum { MMSA_TEXT = 0, MMSA_VIDEO = 1 };
  *    scatters them into o.  The results are bit-identical; the workspace is
  *    larger (2*d bytes per row slot of each permuted head, twice, and 4*d
  *    bytes per grouped slot of each KV head a 2D-boundary head uses).
+ *  MMSA_FLAG_DEBUG: mmsa_permute clears the debug word (MMSA_BUF_DEBUG_FLAGS)
+ *    and scans every element of Q, K and V, setting bit 0 when Q holds a NaN
+ *    or an infinity, bit 1 for K and bit 2 for V; mmsa_sparse_prefill sets
+ *    bit 3 when it writes a non-finite output element or LSE value (an LSE
+ *    of -inf, for a row with no selected key, does not count).  The word can
+ *    be read once the stream has drained.  Without the flag the word is not
+ *    touched.
+ *  MMSA_FLAG_KEYS_ASCENDING / MMSA_FLAG_KEYS_DESCENDING: the order in which
+ *    the attention call walks the key tiles of a query tile, lowest first or
+ *    highest (diagonal) first.  Without either, the library picks by size:
+ *    lowest first once one KV head's K and V exceed 256 MB.  Outputs agree to
+ *    fp32 rounding (the online softmax sums in another order); index sets,
+ *    plans and pair counts are identical.  Setting both is an error.
  * Any other bit is an error. */
 #define MMSA_FLAG_MATERIALIZE 1u
+#define MMSA_FLAG_DEBUG 2u
+#define MMSA_FLAG_KEYS_ASCENDING 4u
+#define MMSA_FLAG_KEYS_DESCENDING 8u
 
 typedef struct {
   int32_t pattern;      /* MMSA_ASHAPE / VS / BLOCK / GRID / PARALLEL               */
   int32_t layout;       /* MMSA_PLAIN / Q_BOUNDARY / BOUNDARY_2D / MODALITY_GROUPED  */
-  int32_t sink;         /* A-shape: keys j < sink are kept; PARALLEL: sink block length */
+  int32_t sink;         /* A-shape: keys j < sink are kept; PARALLEL: sink block length;
+                           GRID: rows off the lines also keep keys j < sink (0: none) */
   int32_t window;       /* A-shape: keys with i - j < window are kept (>= 1);
-                           PARALLEL: context block length (>= 1)                     */
+                           PARALLEL: context block length (>= 1);
+                           GRID: rows off the lines also keep keys with i - j < window
+                           (0: none)                                                  */
   int32_t k_vertical;   /* VS: vertical columns kept (per index set)                 */
   int32_t k_slash;      /* VS: slash diagonals kept (per index set)                  */
   int32_t k_blocks;     /* BLOCK: key blocks kept per query block                    */
@@ -128,7 +151,7 @@ typedef struct {
                                        (L-1) * k/v row stride * 2 + 2d must stay below 2 GiB
                                        (MMSA_UNSUPPORTED otherwise)                     */
   float scale;                      /* softmax scale; 0 -> 1/sqrt(d)                 */
-  uint32_t flags;                   /* 0 or MMSA_FLAG_MATERIALIZE                    */
+  uint32_t flags;                   /* MMSA_FLAG_* bits                              */
   const int32_t* kv_head_of;        /* host [Hq] or NULL -> h / (Hq / Hkv)           */
   const mmsa_head_cfg* heads;       /* host [Hq]                                     */
   const mmsa_segment* segs;         /* host [n_segs]; NULL / 0 -> one text segment   */
@@ -164,9 +187,10 @@ enum {
                                cost, rows                                                    */
   MMSA_BUF_EST_STATS = 11,  /* float[2*64]   per estimation row: max of scale*log2(e)*q.k and
                                the sum of 2^(x - max) over its causal keys                   */
-  MMSA_BUF_TILE_BITMAP = 12 /* uint64[count] per query tile, words of a bitmap over the key
+  MMSA_BUF_TILE_BITMAP = 12,/* uint64[count] per query tile, words of a bitmap over the key
                                tiles of the head's key view (bit c of word w: key tile 64w+c);
                                count = tiles * words per tile                                */
+  MMSA_BUF_DEBUG_FLAGS = 13 /* uint32[1]     the debug word of MMSA_FLAG_DEBUG (any bh, part) */
 };
 mmsa_status mmsa_workspace_view(const mmsa_layer_desc* desc, int32_t buf, int32_t bh, int32_t part,
                                 int64_t* offset_bytes, int64_t* count);

@@ -62,8 +62,8 @@ Q24 = 1 << 24      # grid rule fixed-point quantum 2^-24
 class HeadCfg:
     pattern: str                 # 'ashape' | 'vs' | 'block' | 'grid' | 'parallel'
     layout: str = 'plain'        # 'plain' | 'q_boundary' | 'boundary_2d' | 'q_segment' | 'modality_grouped'
-    sink: int = 0
-    window: int = 1
+    sink: int = 0                # ashape / parallel / grid: sink keys (grid: 0, none)
+    window: int = 1              # ashape: local window; parallel: context block; grid: window (0, none)
     k_vertical: int = 0
     k_slash: int = 0
     k_blocks: int = 0
@@ -473,8 +473,10 @@ def row_mask(hi, i, cache=None):
         sel[hi.blocks[i // TILE]] = True
         return causal & sel[j // TILE]
     if cfg.pattern == 'grid':
+        # lines of both kinds, plus an optional sink and local window on the
+        # rows (R12 widened: window and sink default to 0, none)
         line = np.isin(hi.x % hi.sigma, hi.phases)
-        return causal & (line[i] | line)
+        return causal & (line[i] | line | (j < cfg.sink) | (i - j < cfg.window))
     # VS family
     if cache is None:
         cache = {}
@@ -628,7 +630,13 @@ def tile_plan(hi, tile_rows):
         if line[tile_rows].all():
             return tiles_orig(range(pmax // TILE + 1)), []
         keys = np.nonzero(line)[0]
-        return [], [keys[keys <= pmax]]
+        keys = keys[keys <= pmax]
+        # sink and window tiles; line keys inside them are not gathered again
+        t = pmax // TILE
+        ts = set(range(min(-(-cfg.sink // TILE), t + 1)))
+        if cfg.window > 0:
+            ts |= set(range(max(0, int(tile_rows.min()) - cfg.window + 1) // TILE, t + 1))
+        return tiles_orig(sorted(ts)), [keys[~np.isin(keys // TILE, sorted(ts))]]
     mtab, rtab, n = modality_tables(L, hi.segs)
     if cfg.layout in ('plain', 'q_boundary', 'q_segment'):
         V, S = hi.vs[_vs_key(hi, int(tile_rows[0]), mtab)]
@@ -670,8 +678,11 @@ def permuted_attention(hi, qh, kh, vh, scale):
         groups, gath = tile_plan(hi, rows)
         cand = [g for g in groups] + [g for g in gath if len(g)]
         keys = np.concatenate(cand) if cand else np.zeros(0, np.int64)
+        line = np.isin(hi.x % hi.sigma, hi.phases) if cfg.pattern == 'grid' else None
         for i in rows:
             kk = keys[keys <= i]
+            if cfg.pattern == 'grid' and not line[i]:
+                kk = kk[line[kk] | (kk < cfg.sink) | (i - kk < cfg.window)]
             if cfg.pattern == 'ashape':
                 kk = kk[(kk < cfg.sink) | (i - kk < cfg.window)]
             if cfg.pattern == 'parallel':

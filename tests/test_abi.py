@@ -97,7 +97,8 @@ def last_error():
 @pytest.mark.parametrize("mutate,code,needle", [
     (lambda D: setattr(D, "d", 96), UNSUPPORTED, "head dimension"),
     (lambda D: setattr(D, "L", -1), INVALID, "negative shape"),
-    (lambda D: setattr(D, "flags", 2), INVALID, "flags"),
+    (lambda D: setattr(D, "flags", 16), INVALID, "flags"),
+    (lambda D: setattr(D, "flags", 4 | 8), INVALID, "exclusive"),
     (lambda D: setattr(D, "L", 1 << 22), UNSUPPORTED, "2^22"),
     (lambda D: setattr(D, "Hkv", 3), INVALID, "multiple"),
     (lambda D: setattr(D, "scale", float("nan")), INVALID, "scale"),
@@ -279,3 +280,30 @@ def test_product_path_fails_loudly_without_library(monkeypatch, tmp_path):
     lay = host_layer([synth.vs(1, 2)], Lq=100)
     with pytest.raises(RuntimeError, match="missing"):
         lay.workspace_bytes()
+
+
+@pytest.mark.parametrize("flags", [1, 2, 4, 8, 1 | 2 | 4, 2 | 8])
+def test_flag_combinations_are_accepted(L, flags):
+    lay = host_layer([synth.vs(10, 20), synth.ashape(4, 64)], Hkv=1)
+    lay.desc.flags = flags
+    assert ws_status(lay) == OK
+
+
+def test_debug_word_is_viewable(L):
+    lay = host_layer([synth.vs(10, 20), synth.ashape(4, 64)], Hkv=1)
+    lay.desc.flags = 2
+    n = lay.workspace_bytes()
+    for bh, part in [(0, 0), (1, 0), (1, 3)]:
+        off, cnt = lay.view_offset("debug_flags", bh, part)
+        assert cnt == 1 and 0 < off and off % 4 == 0 and off + 4 <= n
+
+
+@pytest.mark.skipif(torch.cuda.is_available(), reason="checks the refusal on a host without a GPU")
+@pytest.mark.parametrize("name", CALLS)
+def test_valid_calls_refuse_a_host_without_gfx950(L, name):
+    # every argument is valid, so the device check is what answers: no work
+    # is enqueued and the pointers (host addresses here) are never touched
+    lay = host_layer([synth.vs(10, 20), synth.block(4)], Lq=1000, Hkv=1)
+    n = lay.workspace_bytes()
+    assert _call(name, lay, 1 << 20, n) == UNSUPPORTED
+    assert "gfx950" in last_error()

@@ -1,0 +1,116 @@
+"""GPU checks of the boundary's options (include/mmsa.h): the debug word of
+MMSA_FLAG_DEBUG, the forced key-tile walk orders, and tensors that are views
+into larger allocations whose bytes past the layer are NaN.  Parity against the
+CPU oracle uses the same bars as the other GPU tests."""
+import numpy as np
+import pytest
+import torch
+
+from dynamic_sparse_attention_head_amd import mmsa, synth
+from parity_util import full_check, run_gpu
+
+pytestmark = pytest.mark.gpu
+
+TEXT, VIDEO = 0, 1
+
+
+def debug_word(L):
+    return int(L.view("debug_flags", 0).cpu().item())
+
+
+def mixed_spec(L=1000, d=128, seed=51):
+    heads = [synth.vs(40, 90), synth.block(5), synth.ashape(64, 256), synth.grid(1, 16, 64)]
+    return synth.small_spec("dbg", L, 4, 2, d, heads, seed=seed, rope_base=1e4, strong_cols=16)
+
+
+def test_debug_word_is_zero_on_finite_inputs_and_changes_no_output_bit():
+    spec = mixed_spec()
+    L0, q, k, v, o0, lse0 = run_gpu(spec)
+    L1, _, _, _, o1, lse1 = run_gpu(spec, q=q, k=k, v=v, flags=mmsa.FLAG_DEBUG)
+    assert debug_word(L1) == 0
+    assert torch.equal(o0.view(torch.int16), o1.view(torch.int16))
+    assert torch.equal(lse0.view(torch.int32), lse1.view(torch.int32))
+
+
+@pytest.mark.parametrize("which,value,bit", [("q", float("nan"), 1), ("k", float("inf"), 2), ("v", float("nan"), 4),
+                                             ("v", float("-inf"), 4)])
+def test_debug_word_records_a_non_finite_input(which, value, bit):
+    # A-shape and parallel-encoding heads only: no estimation reads the bad value
+    heads = [synth.ashape(16, 100), synth.parallel(64, 50, 30)]
+    spec = synth.small_spec("dbg-nf", 700, 2, 1, 64, heads, seed=52)
+    lay = synth.make_layer(spec, "cuda")
+    t = {"q": lay["q"], "k": lay["k"], "v": lay["v"]}
+    t[which] = t[which].clone()
+    t[which][0, 0, 70, 5] = value      # row 70: every head's row 70 and its window see it
+    L, *_ = run_gpu(spec, q=t["q"], k=t["k"], v=t["v"], flags=mmsa.FLAG_DEBUG)
+    w = debug_word(L)
+    assert w & 7 == bit, hex(w)
+    assert w & 8, f"a non-finite output must set bit 3: {hex(w)}"
+
+
+def nan_padded(t, extra_rows, bl_layout=False):
+    """A copy of t [B, H, L, d] stored as a view at the front of a NaN-filled
+    allocation with `extra_rows` more rows per head ([B, H, L + extra, d]), or
+    with bl_layout as a [B, L + extra, H, d] allocation viewed as [B, H, L, d]."""
+    B, H, Lq, d = t.shape
+    if bl_layout:
+        buf = torch.full((B, Lq + extra_rows, H, d), float("nan"), dtype=t.dtype, device=t.device)
+        view = buf[:, :Lq].transpose(1, 2)
+    else:
+        buf = torch.full((B, H, Lq + extra_rows, d), float("nan"), dtype=t.dtype, device=t.device)
+        view = buf[:, :, :Lq]
+    view.copy_(t)
+    return view
+
+
+@pytest.mark.parametrize("bl_layout", [False, True])
+@pytest.mark.parametrize("Lq", [65, 1000, 3017])
+def test_ragged_layers_never_read_past_the_last_row(Lq, bl_layout):
+    # the rows after the layer's last one are NaN in every head's slice: a
+    # partial last key tile that read them would put NaN into the outputs
+    heads = [synth.vs(20, 40), synth.block(3), synth.ashape(8, 100), synth.grid(1, 16, 64),
+             synth.vs(10, 30, "boundary_2d"), synth.parallel(100, 64, 40)]
+    segs = [(0, Lq // 3, TEXT), (Lq // 3, Lq - Lq // 3, VIDEO)]
+    spec = synth.small_spec("nan-tail", Lq, 6, 2, 128, heads, seed=Lq, segs=segs, period=49)
+    lay = synth.make_layer(spec, "cuda")
+    q = nan_padded(lay["q"], 64, bl_layout)
+    k = nan_padded(lay["k"], 64, bl_layout)
+    v = nan_padded(lay["v"], 64, bl_layout)
+    L = full_check(spec, q=q, k=k, v=v, flags=mmsa.FLAG_DEBUG, rows_per_head=None if Lq < 2000 else 300)
+    assert debug_word(L) == 0
+
+
+def order_specs():
+    segs, Lb = synth.interleaved_segments(3, 4, 49, 77)
+    return {
+        "edge-65": synth.small_spec("edge", 65, 4, 4, 64, [synth.vs(3, 5), synth.block(2), synth.ashape(4, 16),
+                                                           synth.grid(1, 16, 64)], seed=65),
+        "edge-130": synth.small_spec("edge", 130, 4, 4, 64, [synth.vs(3, 5), synth.block(2), synth.ashape(4, 16),
+                                                             synth.grid(1, 16, 64)], seed=130),
+        "mixed": synth.small_spec("mixed", 1000, 8, 2, 128,
+                                  [synth.vs(40, 90), synth.vs(7, 300), synth.block(5), synth.ashape(64, 256),
+                                   synth.block(1000), synth.ashape(0, 1), synth.vs(0, 3), synth.block(1)],
+                                  seed=11, rope_base=1e4, strong_cols=16),
+        "boundary": synth.small_spec("boundary", Lb, 4, 1, 128,
+                                     [synth.grid(2, 16, 200, layout="modality_grouped"), synth.vs(20, 40, "q_boundary"),
+                                      synth.vs(25, 33, "boundary_2d"), synth.vs(15, 80, "plain")],
+                                     seed=9, segs=segs, period=49, period_amp=3.0),
+        "parallel": synth.small_spec("parallel", 3017, 4, 2, 128,
+                                     [synth.parallel(300, 517, 129), synth.parallel(0, 64, 0),
+                                      synth.parallel(236, 392, 64), synth.parallel(37, 5, 100)], seed=21),
+        "parallel-edge": synth.small_spec("parallel-edge", 130, 4, 4, 64,
+                                          [synth.parallel(40, 30, 20), synth.parallel(135, 3, 0),
+                                           synth.parallel(0, 1, 0), synth.parallel(10, 7, 139)], seed=230),
+    }
+
+
+@pytest.mark.parametrize("name", list(order_specs()))
+def test_both_key_walk_orders_match_the_oracle(name):
+    spec = order_specs()[name]
+    rows = None if spec.L <= 1000 else 300
+    La = full_check(spec, flags=mmsa.FLAG_KEYS_ASCENDING, rows_per_head=rows)
+    Ld = full_check(spec, flags=mmsa.FLAG_KEYS_DESCENDING, rows_per_head=rows)
+    # the plans are the same bits; only the summation order differs
+    for h in range(spec.Hq):
+        for buf in ("tile_bitmap", "tile_pairs", "tile_info"):
+            assert torch.equal(La.view(buf, h), Ld.view(buf, h)), (h, buf)

@@ -114,6 +114,12 @@ def test_video_grid_314k():
 
 
 @pytest.mark.timeout(600)
+def test_video_grid_314k_window():
+    # grid heads with the text prompt as sink and a four-frame local window
+    run_config(8)
+
+
+@pytest.mark.timeout(600)
 def test_mixed_1m():
     run_config(5, n_uniform=6, n_tiles=1)
 

@@ -44,6 +44,27 @@ def test_grid_plain_ragged():
     full_check(spec, rows_per_head=200)
 
 
+def test_grid_with_sink_and_window_ragged():
+    # grid heads whose rows off the lines also keep a sink and a local window
+    # (line keys inside the window come once), plain and modality-grouped
+    frames = 9
+    L = 70 + 196 * frames + 23
+    segs = [(0, 70, TEXT), (70, 196 * frames, VIDEO), (70 + 196 * frames, 23, TEXT)]
+    heads = [synth.grid(1, 16, 400, sink=64, window=300), synth.grid(2, 64, 512, window=1),
+             synth.grid(3, 100, 300, sink=100), synth.grid(1, 16, 128, layout="modality_grouped", sink=30, window=500),
+             synth.grid(1, 16, 400, window=5000)]
+    spec = synth.small_spec("grid-window", L, 5, 1, 128, heads, seed=7, segs=segs, period=196, period_amp=3.0)
+    full_check(spec, rows_per_head=300)
+
+
+def test_grid_with_window_d64_materialized():
+    segs, L = synth.interleaved_segments(3, 4, 49, 77)
+    heads = [synth.grid(2, 16, 200, layout="modality_grouped", sink=13, window=130),
+             synth.grid(1, 16, 100, window=64)]
+    spec = synth.small_spec("grid-window-mat", L, 2, 1, 64, heads, seed=17, segs=segs, period=49, period_amp=3.0)
+    full_check(spec, materialize=True)
+
+
 def test_boundary_layouts():
     full_check(boundary_spec())
 

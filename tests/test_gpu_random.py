@@ -3,14 +3,15 @@
 Each case draws a segment layout (1-5 text/video segments of uneven
 lengths), a ragged L, d in {64, 128}, a GQA head map and, per head, any
 pattern and layout the library supports with random budgets; some cases take
-the materialised permutation.  The checks are those of the fixed cases
+the materialised permutation, and odd seeds walk key tiles lowest first (the
+order the library picks by itself only for layers whose K/V pass 256 MB).  The checks are those of the fixed cases
 (index sets bit-exact on the GPU's scores, scores within 1e-3, attention
 within 2e-2 / 2e-3, exact per-tile pair counts).
 """
 import numpy as np
 import pytest
 
-from dynamic_sparse_attention_head_amd import synth
+from dynamic_sparse_attention_head_amd import mmsa, synth
 from parity_util import full_check
 
 pytestmark = pytest.mark.gpu
@@ -37,7 +38,11 @@ def random_head(rng, L, has_video):
         return synth.parallel(int(rng.integers(0, 300)), int(rng.integers(1, 400)), int(rng.integers(0, 300)))
     layout = "modality_grouped" if kind == "grid_grouped" else "plain"
     lo = int(rng.integers(16, 60))
-    return synth.grid(int(rng.integers(1, 4)), lo, lo + int(rng.integers(0, 120)), layout=layout)
+    sink, window = 0, 0
+    if rng.integers(0, 2):      # half the grid heads add a sink and a local window
+        sink, window = int(rng.integers(0, 100)), int(rng.integers(0, 400))
+    return synth.grid(int(rng.integers(1, 4)), lo, lo + int(rng.integers(0, 120)), layout=layout,
+                      sink=sink, window=window)
 
 
 def random_spec(seed):
@@ -62,4 +67,4 @@ def random_spec(seed):
 @pytest.mark.parametrize("seed", range(48))
 def test_random_layer(seed):
     spec, materialize = random_spec(seed)
-    full_check(spec, materialize=materialize)
+    full_check(spec, materialize=materialize, flags=mmsa.FLAG_KEYS_ASCENDING if seed % 2 else 0)

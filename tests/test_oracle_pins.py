@@ -734,3 +734,95 @@ def test_plain_grid_on_the_same_layer_sees_original_positions():
     hi = O.estimate_head(synth.grid(1, 16, 64), q, k, segs, 1 / math.sqrt(q.shape[1]))
     assert list(hi.extras["rows"]) == list(range(527 - 64, 527))
     assert list(hi.x) == list(range(527))
+
+
+# ---------------------------------------------------------------------------
+# Grid heads with a sink and a local window (R12 widened): the rows that are
+# not on a line also see keys j < sink and keys with i - j < window.
+# ---------------------------------------------------------------------------
+def _grid_head(L, sigma, phases, sink, window, x=None, layout='plain'):
+    cfg = O.HeadCfg.of(synth.grid(len(phases), 16, 64, layout=layout, sink=sink, window=window))
+    hi = O.HeadIndex(cfg=cfg, L=L, segs=[(0, L, 0)])
+    hi.sigma, hi.phases = sigma, np.array(sorted(phases), np.int64)
+    hi.x = np.arange(L, dtype=np.int64) if x is None else x
+    return hi
+
+
+def _lines_in(a, b, sigma, phases):
+    """Number of positions in [a, b] congruent to a phase mod sigma (plain
+    coordinate), by floor division."""
+    if b < a:
+        return 0
+    return sum((b - f) // sigma - (a - 1 - f) // sigma for f in phases)
+
+
+def grid_window_pairs_closed_form(L, sigma, phases, sink, window):
+    tot = 0
+    for i in range(L):
+        if i % sigma in phases:
+            tot += i + 1
+            continue
+        s_end = min(sink, i + 1)                       # sink keys [0, s_end)
+        w0 = max(0, i - window + 1) if window > 0 else i + 1
+        if s_end >= w0:                                # the two runs meet: [0, i]
+            size, lin = i + 1, _lines_in(0, i, sigma, phases)
+        else:
+            size = s_end + (i - w0 + 1)
+            lin = _lines_in(0, s_end - 1, sigma, phases) + _lines_in(w0, i, sigma, phases)
+        tot += _lines_in(0, i, sigma, phases) + size - lin
+    return tot
+
+
+@pytest.mark.parametrize("L,sigma,phases,sink,window", [
+    (700, 37, [3], 0, 0), (700, 37, [3], 0, 50), (700, 37, [3, 20], 64, 0), (700, 37, [3, 20], 64, 50),
+    (513, 64, [0], 70, 200), (300, 16, [15], 300, 1), (400, 50, [7], 5, 1000)])
+def test_grid_window_pair_count_closed_form(L, sigma, phases, sink, window):
+    hi = _grid_head(L, sigma, phases, sink, window)
+    assert O.pair_count(hi) == grid_window_pairs_closed_form(L, sigma, phases, sink, window)
+
+
+def test_grid_window_mask_matches_loops():
+    L, sigma, phases, sink, window = 400, 30, [4, 11], 20, 45
+    hi = _grid_head(L, sigma, phases, sink, window)
+    for i in [0, 4, 5, 19, 20, 44, 45, 46, 100, 101, 250, 399]:
+        ref = np.zeros(L, bool)
+        for j in range(i + 1):
+            on_i, on_j = (i % sigma) in phases, (j % sigma) in phases
+            ref[j] = on_i or on_j or j < sink or i - j < window
+        assert (O.row_mask(hi, i) == ref).all(), i
+
+
+def test_grid_window_on_the_grouped_coordinate_follows_original_positions():
+    # lines sit on the grouped coordinate, the window and the sink on original
+    # positions (the causal order the rows attend in)
+    segs = [(0, 50, 1), (50, 30, 0), (80, 70, 1)]
+    L = 150
+    x = O.grid_coordinate(L, segs, True)
+    hi = _grid_head(L, 20, [6], 10, 25, x=x, layout='modality_grouped')
+    hi.segs = segs
+    for i in [0, 30, 55, 79, 80, 120, 149]:
+        ref = np.array([j <= i and ((x[i] % 20 == 6) or (x[j] % 20 == 6) or j < 10 or i - j < 25)
+                        for j in range(L)])
+        assert (O.row_mask(hi, i) == ref).all(), i
+
+
+def test_grid_window_covering_the_layer_is_dense():
+    L, d = 300, 16
+    cfg = synth.grid(1, 16, 64, window=L)
+    q, k, v, _ = small_layer(L, d, [cfg], seed=8)
+    scale = 1 / math.sqrt(d)
+    hi = O.estimate_head(cfg, q[0], k[0], None, scale)
+    got, _ = O.head_attention(hi, q[0], k[0], v[0], scale)
+    ref = torch.nn.functional.scaled_dot_product_attention(
+        torch.from_numpy(q[0])[None], torch.from_numpy(k[0])[None], torch.from_numpy(v[0])[None],
+        is_causal=True, scale=scale)[0].numpy()
+    np.testing.assert_allclose(got, ref, atol=1e-10, rtol=0)
+
+
+@pytest.mark.parametrize("sink,window", [(0, 40), (30, 0), (70, 130)])
+def test_permuted_equals_direct_grid_window(sink, window):
+    segs = [(0, 40, 0), (40, 49 * 12, 1)]
+    _check_perm(synth.grid(1, 16, 100, sink=sink, window=window), 40 + 49 * 12, 16, segs, seed=2, period=49)
+    segs = [(0, 49 * 4, 1), (196, 30, 0), (226, 49 * 5, 1), (471, 20, 0)]
+    _check_perm(synth.grid(2, 16, 100, layout='modality_grouped', sink=sink, window=window), 491, 16, segs,
+                seed=3, period=49)
