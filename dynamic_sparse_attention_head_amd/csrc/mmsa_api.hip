@@ -18,6 +18,12 @@
 
 using namespace mmsa;
 
+// Device memory of mmsa_prefill_noalloc: the workspace of one layer whose
+// mmsa_workspace_bytes() is at most MMSA_NOALLOC_SCRATCH_BYTES.  Each device
+// the library runs on holds its own copy until the process ends; every
+// mmsa_prefill_noalloc call on a device reuses it.
+static __device__ __align__(256) char scratch[MMSA_NOALLOC_SCRATCH_BYTES];
+
 namespace {
 
 thread_local std::string g_err;
@@ -930,9 +936,10 @@ struct DevInfo {
   int state = 0;   // 0 unknown, 1 gfx950, -1 another architecture
   int n_cu = 0;
   char arch[64] = {0};
+  void* scratch = nullptr;   // this device's copy of `scratch` (mmsa_prefill_noalloc)
 };
 
-mmsa_status check_device(int* n_cu_out = nullptr) {
+mmsa_status check_device(int* n_cu_out = nullptr, void** scratch_out = nullptr) {
   static std::mutex mu;
   static std::vector<DevInfo> info;
   int dev = -1;
@@ -960,6 +967,20 @@ mmsa_status check_device(int* n_cu_out = nullptr) {
     set_err("device %d is %s; libmmsa runs on gfx950 only", dev, di.arch);
     return MMSA_UNSUPPORTED;
   }
+  if (scratch_out) {
+    // The array's name is only a host-side handle: its address on this
+    // device (the current one) comes from the runtime, once per device.
+    if (!di.scratch) {
+      void* p = nullptr;
+      const hipError_t e3 = hipGetSymbolAddress(&p, HIP_SYMBOL(scratch));
+      if (e3 != hipSuccess || !p) {
+        set_err("device %d: address of the static scratch: %s", dev, hipGetErrorString(e3));
+        return MMSA_HIP_ERROR;
+      }
+      di.scratch = p;
+    }
+    *scratch_out = di.scratch;
+  }
   if (n_cu_out) *n_cu_out = di.n_cu;
   return MMSA_OK;
 }
@@ -974,6 +995,58 @@ mmsa_status upload(const Layout& Lo, void* ws, hipStream_t s) {
     if (_st != MMSA_OK) return _st;          \
   } while (0)
 #define MMSA_HIP(expr, where) MMSA_TRY(hip_status((expr), where))
+
+// The five steps on a validated layout, a workspace `w` and a stream: shared
+// by the entry points (caller workspace) and mmsa_prefill_noalloc (static
+// scratch).  Each uploads the tables it reads first.
+mmsa_status run_estimate_vs(const Layout& Lo, const void* q, const void* k, char* w, hipStream_t s) {
+  MMSA_TRY(upload(Lo, w, s));
+  if (Lo.need_seg) MMSA_HIP(launch_seg_tables(Lo.dm, Lo.tb, w, s), "segment tables");
+  MMSA_HIP(launch_est_pass1(Lo.dm, Lo.tb, w, q, k, Lo.n_wg1, s), "estimation pass 1");
+  MMSA_HIP(launch_fill_u32(w + Lo.zero_off, 0u, Lo.zero_bytes / 4, s), "score clear");
+  MMSA_HIP(launch_est_pass2(Lo.dm, Lo.tb, w, q, k, Lo.n_wg2, Lo.max_ds, s), "estimation pass 2");
+  MMSA_HIP(launch_topk(Lo.tb, w, (int)Lo.max_topk_slices, s), "top-k");
+  MMSA_HIP(launch_grid(Lo.dm, Lo.tb, w, Lo.max_strides, s), "grid rule");
+  return MMSA_OK;
+}
+
+mmsa_status run_estimate_blocks(const Layout& Lo, const void* q, const void* k, char* w, hipStream_t s) {
+  MMSA_TRY(upload(Lo, w, s));
+  MMSA_HIP(launch_block_estimate(Lo.dm, Lo.tb, w, q, k, Lo.nB, s), "block estimation");
+  return MMSA_OK;
+}
+
+mmsa_status run_permute(const Layout& Lo, const void* q, const void* k, const void* v, char* w, hipStream_t s) {
+  MMSA_TRY(upload(Lo, w, s));
+  if (Lo.dm.debug) {
+    MMSA_HIP(launch_fill_u32(w + Lo.dm.ws_flag, 0u, 1, s), "debug word clear");
+    MMSA_HIP(launch_nonfinite_scan(Lo.dm, w, q, k, v, s), "non-finite scan");
+  }
+  if (Lo.need_seg) MMSA_HIP(launch_seg_tables(Lo.dm, Lo.tb, w, s), "segment tables");
+  if (Lo.gridrow_bytes > 0) {
+    MMSA_HIP(launch_fill_u32(w + Lo.gridrow_off, 0xffffffffu, Lo.gridrow_bytes / 4, s), "row order clear");
+    MMSA_HIP(launch_grid_rows(Lo.dm, Lo.tb, w, s), "grid row order");
+  }
+  MMSA_HIP(launch_gather(Lo.dm, Lo.tb, w, q, k, v, Lo.max_gather_slots, s), "gather");
+  MMSA_HIP(launch_plan(Lo.dm, Lo.tb, w, Lo.max_tiles, Lo.max_bm_words, s), "plan");
+  return MMSA_OK;
+}
+
+mmsa_status run_sparse_prefill(const Layout& Lo, const void* q, const void* k, const void* v, void* o, float* lse,
+                               int n_cu, char* w, hipStream_t s) {
+  MMSA_TRY(upload(Lo, w, s));
+  // the pop counters start at zero on every call, so the call can be repeated
+  MMSA_HIP(launch_queue_reset(Lo.dm, w, s), "queue reset");
+  // two resident workgroups per CU (the kernel's LDS and register budget)
+  MMSA_HIP(launch_attention(Lo.dm, Lo.tb, w, q, k, v, o, lse, 2 * std::max(n_cu, 1), s), "attention");
+  return MMSA_OK;
+}
+
+mmsa_status run_unpermute(const Layout& Lo, void* o, char* w, hipStream_t s) {
+  MMSA_TRY(upload(Lo, w, s));
+  MMSA_HIP(launch_unpermute(Lo.dm, Lo.tb, w, o, Lo.max_unperm_slots, s), "unpermute");
+  return MMSA_OK;
+}
 
 }  // namespace
 
@@ -1105,16 +1178,7 @@ mmsa_status mmsa_estimate_vs(const mmsa_layer_desc* desc, const void* q, const v
   MMSA_TRY(check_ptr(q, "q"));
   MMSA_TRY(check_ptr(k, "k"));
   MMSA_TRY(check_device());
-  hipStream_t s = (hipStream_t)stream;
-  char* w = (char*)ws;
-  MMSA_TRY(upload(Lo, ws, s));
-  if (Lo.need_seg) MMSA_HIP(launch_seg_tables(Lo.dm, Lo.tb, w, s), "segment tables");
-  MMSA_HIP(launch_est_pass1(Lo.dm, Lo.tb, w, q, k, Lo.n_wg1, s), "estimation pass 1");
-  MMSA_HIP(launch_fill_u32(w + Lo.zero_off, 0u, Lo.zero_bytes / 4, s), "score clear");
-  MMSA_HIP(launch_est_pass2(Lo.dm, Lo.tb, w, q, k, Lo.n_wg2, Lo.max_ds, s), "estimation pass 2");
-  MMSA_HIP(launch_topk(Lo.tb, w, (int)Lo.max_topk_slices, s), "top-k");
-  MMSA_HIP(launch_grid(Lo.dm, Lo.tb, w, Lo.max_strides, s), "grid rule");
-  return MMSA_OK;
+  return run_estimate_vs(Lo, q, k, (char*)ws, (hipStream_t)stream);
 }
 
 mmsa_status mmsa_estimate_blocks(const mmsa_layer_desc* desc, const void* q, const void* k, void* ws,
@@ -1125,10 +1189,7 @@ mmsa_status mmsa_estimate_blocks(const mmsa_layer_desc* desc, const void* q, con
   MMSA_TRY(check_ptr(q, "q"));
   MMSA_TRY(check_ptr(k, "k"));
   MMSA_TRY(check_device());
-  hipStream_t s = (hipStream_t)stream;
-  MMSA_TRY(upload(Lo, ws, s));
-  MMSA_HIP(launch_block_estimate(Lo.dm, Lo.tb, (char*)ws, q, k, Lo.nB, s), "block estimation");
-  return MMSA_OK;
+  return run_estimate_blocks(Lo, q, k, (char*)ws, (hipStream_t)stream);
 }
 
 mmsa_status mmsa_permute(const mmsa_layer_desc* desc, const void* q, const void* k, const void* v, void* ws,
@@ -1140,21 +1201,7 @@ mmsa_status mmsa_permute(const mmsa_layer_desc* desc, const void* q, const void*
   MMSA_TRY(check_ptr(k, "k"));
   MMSA_TRY(check_ptr(v, "v"));
   MMSA_TRY(check_device());
-  hipStream_t s = (hipStream_t)stream;
-  char* w = (char*)ws;
-  MMSA_TRY(upload(Lo, ws, s));
-  if (Lo.dm.debug) {
-    MMSA_HIP(launch_fill_u32(w + Lo.dm.ws_flag, 0u, 1, s), "debug word clear");
-    MMSA_HIP(launch_nonfinite_scan(Lo.dm, w, q, k, v, s), "non-finite scan");
-  }
-  if (Lo.need_seg) MMSA_HIP(launch_seg_tables(Lo.dm, Lo.tb, w, s), "segment tables");
-  if (Lo.gridrow_bytes > 0) {
-    MMSA_HIP(launch_fill_u32(w + Lo.gridrow_off, 0xffffffffu, Lo.gridrow_bytes / 4, s), "row order clear");
-    MMSA_HIP(launch_grid_rows(Lo.dm, Lo.tb, w, s), "grid row order");
-  }
-  MMSA_HIP(launch_gather(Lo.dm, Lo.tb, w, q, k, v, Lo.max_gather_slots, s), "gather");
-  MMSA_HIP(launch_plan(Lo.dm, Lo.tb, w, Lo.max_tiles, Lo.max_bm_words, s), "plan");
-  return MMSA_OK;
+  return run_permute(Lo, q, k, v, (char*)ws, (hipStream_t)stream);
 }
 
 mmsa_status mmsa_sparse_prefill(const mmsa_layer_desc* desc, const void* q, const void* k, const void* v, void* ws,
@@ -1168,13 +1215,7 @@ mmsa_status mmsa_sparse_prefill(const mmsa_layer_desc* desc, const void* q, cons
   MMSA_TRY(check_ptr(o, "o"));
   int n_cu = 0;
   MMSA_TRY(check_device(&n_cu));
-  hipStream_t s = (hipStream_t)stream;
-  MMSA_TRY(upload(Lo, ws, s));
-  // the pop counters start at zero on every call, so the call can be repeated
-  MMSA_HIP(launch_queue_reset(Lo.dm, (char*)ws, s), "queue reset");
-  // two resident workgroups per CU (the kernel's LDS and register budget)
-  MMSA_HIP(launch_attention(Lo.dm, Lo.tb, (char*)ws, q, k, v, o, lse, 2 * std::max(n_cu, 1), s), "attention");
-  return MMSA_OK;
+  return run_sparse_prefill(Lo, q, k, v, o, lse, n_cu, (char*)ws, (hipStream_t)stream);
 }
 
 mmsa_status mmsa_unpermute(const mmsa_layer_desc* desc, void* ws, size_t ws_bytes, void* o, void* stream) {
@@ -1183,10 +1224,37 @@ mmsa_status mmsa_unpermute(const mmsa_layer_desc* desc, void* ws, size_t ws_byte
   if (Lo.empty) return MMSA_OK;
   MMSA_TRY(check_ptr(o, "o"));
   MMSA_TRY(check_device());
+  return run_unpermute(Lo, o, (char*)ws, (hipStream_t)stream);
+}
+
+mmsa_status mmsa_prefill_noalloc(const mmsa_layer_desc* desc, const void* q, const void* k, const void* v, void* o,
+                                 float* lse, void* stream) {
+  Layout Lo;
+  MMSA_TRY(build_layout(desc, Lo));
+  if (Lo.empty) return MMSA_OK;
+  if (Lo.ws_total > (int64_t)MMSA_NOALLOC_SCRATCH_BYTES) {
+    set_err("this layer needs %lld bytes of workspace; the static scratch of mmsa_prefill_noalloc holds %lld "
+            "(use the five calls with a caller workspace)",
+            (long long)Lo.ws_total, (long long)MMSA_NOALLOC_SCRATCH_BYTES);
+    return MMSA_WORKSPACE_TOO_SMALL;
+  }
+  MMSA_TRY(check_ptr(q, "q"));
+  MMSA_TRY(check_ptr(k, "k"));
+  MMSA_TRY(check_ptr(v, "v"));
+  MMSA_TRY(check_ptr(o, "o"));
+  int n_cu = 0;
+  void* sp = nullptr;
+  MMSA_TRY(check_device(&n_cu, &sp));
+  char* w = (char*)sp;
   hipStream_t s = (hipStream_t)stream;
-  MMSA_TRY(upload(Lo, ws, s));
-  MMSA_HIP(launch_unpermute(Lo.dm, Lo.tb, (char*)ws, o, Lo.max_unperm_slots, s), "unpermute");
-  return MMSA_OK;
+  // the five steps in their order, on the static scratch; each step rebuilds
+  // what it reads (tables, cleared scores and counters), so nothing left there
+  // by an earlier call is used
+  if (!Lo.jobs.empty()) MMSA_TRY(run_estimate_vs(Lo, q, k, w, s));
+  if (Lo.any_block) MMSA_TRY(run_estimate_blocks(Lo, q, k, w, s));
+  MMSA_TRY(run_permute(Lo, q, k, v, w, s));
+  MMSA_TRY(run_sparse_prefill(Lo, q, k, v, o, lse, n_cu, w, s));
+  return run_unpermute(Lo, o, w, s);
 }
 
 }  // extern "C"

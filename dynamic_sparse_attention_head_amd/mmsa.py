@@ -66,7 +66,8 @@ class MMSAError(RuntimeError):
 _lib = None
 _SYMBOLS = ("mmsa_workspace_bytes", "mmsa_workspace_view", "mmsa_index_meta", "mmsa_estimate_vs",
             "mmsa_estimate_blocks", "mmsa_permute", "mmsa_sparse_prefill", "mmsa_unpermute",
-            "mmsa_status_string", "mmsa_last_error", "mmsa_abi_version")
+            "mmsa_prefill_noalloc", "mmsa_status_string", "mmsa_last_error", "mmsa_abi_version")
+NOALLOC_SCRATCH_BYTES = 64 << 20   # MMSA_NOALLOC_SCRATCH_BYTES
 
 
 def lib():
@@ -95,6 +96,8 @@ def lib():
     L.mmsa_sparse_prefill.restype = i32
     L.mmsa_unpermute.argtypes = [P, vp, sz, vp, vp]
     L.mmsa_unpermute.restype = i32
+    L.mmsa_prefill_noalloc.argtypes = [P, vp, vp, vp, vp, vp, vp]
+    L.mmsa_prefill_noalloc.restype = i32
     L.mmsa_status_string.argtypes = [i32]
     L.mmsa_status_string.restype = ctypes.c_char_p
     L.mmsa_last_error.argtypes = []
@@ -249,6 +252,13 @@ class Layer:
     def unpermute(self, o):
         _check(lib().mmsa_unpermute(ctypes.byref(self.desc), self._ws_ptr(), self.workspace_bytes(), o.data_ptr(),
                                     self._stream()))
+
+    def forward_noalloc(self, q, k, v, o, lse=None):
+        """The whole path through mmsa_prefill_noalloc (the library's static
+        scratch instead of this layer's workspace, which is left untouched)."""
+        _check(lib().mmsa_prefill_noalloc(ctypes.byref(self.desc), q.data_ptr(), k.data_ptr(), v.data_ptr(),
+                                          o.data_ptr(), None if lse is None else lse.data_ptr(), self._stream()))
+        return o
 
     def forward(self, q, k, v, o=None, lse=None):
         """All five calls in order; returns O [B, Hq, L, d] bf16."""

@@ -251,6 +251,25 @@ mmsa_status mmsa_sparse_prefill(const mmsa_layer_desc* desc, const void* q, cons
 mmsa_status mmsa_unpermute(const mmsa_layer_desc* desc, void* ws, size_t ws_bytes, void* o,
                            void* stream);
 
+/* For callers that cannot allocate device memory (code under stream capture,
+ * tight serving loops, harnesses that forbid hipMalloc): the five calls above
+ * in order, on a workspace the library holds itself, a static device array of
+ * MMSA_NOALLOC_SCRATCH_BYTES per GPU that stays allocated until the process
+ * ends.  q, k, v, o, lse and the descriptor as for the five calls; nothing
+ * else is needed and nothing is allocated.  A layer whose
+ * mmsa_workspace_bytes() exceeds MMSA_NOALLOC_SCRATCH_BYTES is refused with
+ * MMSA_WORKSPACE_TOO_SMALL before anything is enqueued (64 MiB holds, for
+ * example, a 32K-token layer of 32 q / 8 KV heads with d = 128 and
+ * vertical-slash, block and A-shape heads).  Every call on one GPU uses the
+ * same array, so calls that overlap on one GPU (two streams, two threads)
+ * race and give undefined results; calls in one stream are ordered and safe.
+ * The outputs equal those of the five calls bit for bit.  The index sets,
+ * plan and debug word of MMSA_FLAG_DEBUG stay in the library's array and
+ * cannot be viewed. */
+#define MMSA_NOALLOC_SCRATCH_BYTES (64ull << 20)
+mmsa_status mmsa_prefill_noalloc(const mmsa_layer_desc* desc, const void* q, const void* k, const void* v,
+                                 void* o, float* lse, void* stream);
+
 const char* mmsa_status_string(mmsa_status s);
 const char* mmsa_last_error(void);
 int32_t mmsa_abi_version(void);

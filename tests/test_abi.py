@@ -307,3 +307,23 @@ def test_valid_calls_refuse_a_host_without_gfx950(L, name):
     n = lay.workspace_bytes()
     assert _call(name, lay, 1 << 20, n) == UNSUPPORTED
     assert "gfx950" in last_error()
+
+
+def test_noalloc_refusals_before_any_launch(L):
+    big = host_layer([synth.vs(1000, 4096)] * 32, Lq=65536, Hkv=8)
+    assert big.workspace_bytes() > mmsa.NOALLOC_SCRATCH_BYTES
+    p = 1 << 20
+    assert L.mmsa_prefill_noalloc(ctypes.byref(big.desc), p, p, p, p, None, None) == TOO_SMALL
+    assert "static scratch" in last_error()
+    small = host_layer([synth.vs(10, 20), synth.block(4)], Lq=1000, Hkv=1)
+    assert L.mmsa_prefill_noalloc(ctypes.byref(small.desc), None, p, p, p, None, None) == INVALID
+    assert L.mmsa_prefill_noalloc(ctypes.byref(small.desc), p + 8, p, p, p, None, None) == UNSUPPORTED
+    assert L.mmsa_prefill_noalloc(None, p, p, p, p, None, None) == INVALID
+
+
+@pytest.mark.skipif(torch.cuda.is_available(), reason="checks the refusal on a host without a GPU")
+def test_noalloc_refuses_a_host_without_gfx950(L):
+    small = host_layer([synth.vs(10, 20), synth.block(4)], Lq=1000, Hkv=1)
+    p = 1 << 20
+    assert L.mmsa_prefill_noalloc(ctypes.byref(small.desc), p, p, p, p, None, None) == UNSUPPORTED
+    assert "gfx950" in last_error()
