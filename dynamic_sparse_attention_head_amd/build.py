@@ -3,7 +3,9 @@
     python -m dynamic_sparse_attention_head_amd.build
 
 Each .hip source under csrc/ is compiled to an object in parallel, then the
-objects are linked into dynamic_sparse_attention_head_amd/libmmsa.so.
+objects are linked into dynamic_sparse_attention_head_amd/libmmsa.so.  Also
+built: the host-AddressSanitizer variant of the library (_build/asan/) and
+the peak microbenchmarks (libmmsa_probe.so, probe/peaks.hip).
 """
 from __future__ import annotations
 
@@ -49,6 +51,22 @@ def _compile(src, obj, extra):
 
 
 ASAN_LIB = os.path.join(BUILD, "asan", "libmmsa_asan.so")
+PROBE_SRC = os.path.join(PKG, "probe", "peaks.hip")
+PROBE_LIB = os.path.join(PKG, "libmmsa_probe.so")
+
+
+def build_probe(verbose=False):
+    """The peak microbenchmarks (an MFMA loop and a streaming copy) that
+    bench.py --peaks times; a library of their own, outside libmmsa."""
+    tmp = PROBE_LIB + ".tmp"
+    cmd = [hipcc(), *HIPCC_FLAGS, "-shared", "-o", tmp, PROBE_SRC]
+    r = subprocess.run(cmd, capture_output=True, text=True)
+    if r.returncode != 0:
+        raise RuntimeError(f"hipcc failed for {PROBE_SRC}:\n{r.stdout}\n{r.stderr}")
+    os.replace(tmp, PROBE_LIB)
+    if verbose:
+        print(f"built {PROBE_LIB}")
+    return PROBE_LIB
 
 
 def asan_runtime():
@@ -106,6 +124,7 @@ def build(verbose=False, extra=(), asan=True):
         print(f"built {LIB}")
     if asan:
         build_asan(objs, verbose=verbose)
+    build_probe(verbose=verbose)
     return LIB
 
 

@@ -342,8 +342,7 @@ def estimate_head(cfg, qh, kh, segs, scale, scores_override=None):
     if cfg.pattern in ('ashape', 'parallel') or L == 0:
         return hi
     if cfg.pattern == 'block':
-        qp, kp = pool_blocks(qh), pool_blocks(kh)
-        z = ov.get('z', block_logits(qp, kp, scale))
+        z = ov['z'] if 'z' in ov else block_logits(pool_blocks(qh), pool_blocks(kh), scale)
         hi.extras['z'] = z
         hi.blocks = block_select(z, cfg.k_blocks)
         return hi
@@ -354,12 +353,15 @@ def estimate_head(cfg, qh, kh, segs, scale, scores_override=None):
         order = grouped_positions(L, segs) if grouped else np.arange(L)
         rows = estimation_rows(order)
         rows = np.sort(rows)
-        a, mx, ssum = last_rows_attention(qh[rows], kh, rows, scale)
-        vx = np.zeros(L, np.float64)
-        vx[x] = a.sum(axis=0)
         imax = int(rows.max())
         D = int(x[:imax + 1].max()) + 1
-        v32 = ov.get('v', vx.astype(np.float32))
+        if 'v' in ov:            # selection replayed on given scores: nothing to compute
+            v32, mx, ssum = ov['v'], None, None
+        else:
+            a, mx, ssum = last_rows_attention(qh[rows], kh, rows, scale)
+            vx = np.zeros(L, np.float64)
+            vx[x] = a.sum(axis=0)
+            v32 = vx.astype(np.float32)
         hi.extras.update(v=v32, D=D, n_rows=len(rows), rows=rows, stats=(mx, ssum))
         hi.sigma, hi.phases = grid_rule(v32, D, len(rows), cfg.grid_clip or 8,
                                         cfg.stride_lo, cfg.stride_hi, cfg.grid_phases)
@@ -376,13 +378,19 @@ def estimate_head(cfg, qh, kh, segs, scale, scores_override=None):
     else:
         regions = [(mod, _region_rows_for_modality(mtab, mod)) for mod in (TEXT, VIDEO) if n[mod] > 0]
     for key, rows in regions:
-        a, mx, ssum = last_rows_attention(qh[rows], kh, rows, scale)
-        hi.extras[('stats', key)] = (mx, ssum)
+        given = cfg.layout != 'boundary_2d' and ('v', key) in ov and ('s', key) in ov
+        if given:                # selection replayed on given scores: nothing to compute
+            hi.extras[('stats', key)] = (None, None)
+        else:
+            a, mx, ssum = last_rows_attention(qh[rows], kh, rows, scale)
+            hi.extras[('stats', key)] = (mx, ssum)
         if cfg.layout in ('plain', 'q_boundary', 'q_segment'):
-            v, s = vs_scores_original(a, rows, L)
             vc, sc = vs_candidates_original(rows)
-            v32 = ov.get(('v', key), v.astype(np.float32))
-            s32 = ov.get(('s', key), s.astype(np.float32))
+            if given:
+                v32, s32 = ov[('v', key)], ov[('s', key)]
+            else:
+                v, s = vs_scores_original(a, rows, L)
+                v32, s32 = v.astype(np.float32), s.astype(np.float32)
             hi.extras[('v', key)], hi.extras[('s', key)] = v32, s32
             hi.extras[('cand', key)] = (vc, sc)
             hi.vs[key] = (topk_select(v32, cfg.k_vertical, *vc), topk_select(s32, cfg.k_slash, *sc))

@@ -2,12 +2,17 @@
 benchmark times (the same five calls on the same generated layer), checked
 on outputs the oracle can compute one by one:
 
-  * for one head of every (pattern, layout) present: the GPU's scores against
-    the oracle's own (relative 1e-3), the index sets bit-exact when the
-    oracle selects on the GPU's scores, and the grid stride/phases;
-  * attention on sampled rows of those heads (first/last rows, seeded
-    uniform rows, rows at segment edges) within max-abs 2e-2 / mean-abs 2e-3;
-  * exact selected-pair counts of sampled query tiles;
+  * for every head: the GPU's scores against the oracle's own (relative
+    1e-3) and the index sets bit-exact when the oracle selects on the GPU's
+    scores (vertical and slash sets, block sets, grid stride and phases);
+  * the generator's sanity check on layers with grid heads: the planted
+    period (196 tokens per frame) is detected on at least 90 % of them;
+  * for one head of every (pattern, layout) present, attention on sampled
+    rows within max-abs 2e-2 / mean-abs 2e-3: first and last rows, seeded
+    uniform rows, rows at segment edges, the last 64 rows of each modality
+    for boundary heads, and 32 line rows (the longest rows: every causal
+    key) for grid heads;
+  * exact selected-pair counts of sampled query tiles of those heads;
   * for every head: finite outputs, and the per-tile pair counts summing to
     no more than the causal total.
 
@@ -51,10 +56,34 @@ def rows_for(spec, h, n_uniform, seed, extra=()):
     rows |= set(int(x) for x in rng.integers(0, L, n_uniform))
     for s, n, m in (spec.segs or []):
         rows |= {s, s + 1, s + n - 1}
-    return np.array(sorted(r for r in rows if 0 <= r < L), np.int64)
+    return rows
 
 
-def run_config(i, n_uniform=10, n_tiles=2, extra_rows=(), whole_layer_check=None, layouts=None):
+def modality_tails(spec, n=64):
+    """The last n positions of each modality (the rows a per-modality
+    estimate extrapolates from)."""
+    out = set()
+    segs = spec.segs or [(0, spec.L, 0)]
+    for m in (0, 1):
+        pos = [np.arange(s, s + ln) for s, ln, mm in segs if mm == m]
+        if pos:
+            out |= set(int(p) for p in np.concatenate(pos)[-n:])
+    return out
+
+
+def line_rows(Lg, h, n, rng):
+    """n line rows of a grid head (from its row order: line rows first,
+    ascending), the last 8 of them (the longest rows) included."""
+    nline = int(Lg.view("grid", h)[2].item())
+    order = Lg.view("row_order", h)[:nline].cpu().numpy()
+    if nline == 0:
+        return set()
+    pick = rng.choice(nline, min(n - 8, nline), replace=False)
+    return set(int(r) for r in order[pick]) | set(int(r) for r in order[-8:])
+
+
+def run_config(i, n_uniform=10, n_tiles=2, extra_rows=(), whole_layer_check=None, layouts=None,
+               index_heads="all", n_line=32):
     spec = synth.config(i)
     t0 = time.time()
     Lg, q, k, v, o, lse = run_gpu(spec)
@@ -67,15 +96,43 @@ def run_config(i, n_uniform=10, n_tiles=2, extra_rows=(), whole_layer_check=None
     for h in range(spec.Hq):
         tp = Lg.view("tile_pairs", h)
         assert 0 <= int(tp.sum().item()) <= causal
-    rng = np.random.default_rng(i)
-    for h in representative_heads(spec):
-        if layouts is not None and spec.heads[h].get("layout", "plain") not in layouts:
+    rep = [h for h in representative_heads(spec)
+           if layouts is None or spec.heads[h].get("layout", "plain") in layouts]
+    # index sets of every head (or of the representative ones), bit-exact
+    his = {}
+    t1 = time.time()
+    for h in (range(spec.Hq) if index_heads == "all" else rep):
+        if spec.heads[h]["pattern"] in ("ashape", "parallel"):
+            if h in rep:   # static masks: nothing is estimated
+                his[h] = O.estimate_head(spec.heads[h], np.zeros((spec.L, 1)), None, spec.segs, scale)
             continue
+        qh, kh = f64(q[0, h]), f64(k[0, gmap[h]])
+        hi = check_head_indices(Lg, h, spec.heads[h], qh, kh, spec.segs, scale)
+        if h in rep:
+            his[h] = hi
+        del qh, kh, hi
+    say(f"{spec.name}: index sets of {len(range(spec.Hq)) if index_heads == 'all' else len(rep)} heads "
+        f"bit-exact in {time.time() - t1:.1f} s")
+    # the generator's planted period is found on (nearly) every grid head
+    grid_heads = [h for h in range(spec.Hq) if spec.heads[h]["pattern"] == "grid"]
+    if grid_heads and spec.period:
+        sig = [int(Lg.view("grid", h)[0].item()) for h in grid_heads]
+        share = sum(s == spec.period for s in sig) / len(sig)
+        say(f"{spec.name}: stride {spec.period} detected on {share:.0%} of {len(sig)} grid heads")
+        assert share >= 0.9, f"strides {sig}"
+    rng = np.random.default_rng(i)
+    for h in rep:
         t1 = time.time()
         g = gmap[h]
+        c = spec.heads[h]
+        hi = his[h]
         qh, kh, vh = f64(q[0, h]), f64(k[0, g]), f64(v[0, g])
-        hi = check_head_indices(Lg, h, spec.heads[h], qh, kh, spec.segs, scale)
         rows = rows_for(spec, h, n_uniform, 1000 * i + h, extra_rows)
+        if c.get("layout", "plain") in ("q_boundary", "boundary_2d", "q_segment"):
+            rows |= modality_tails(spec)
+        if c["pattern"] == "grid":
+            rows |= line_rows(Lg, h, n_line, rng)
+        rows = np.array(sorted(r for r in rows if 0 <= r < spec.L), np.int64)
         og = f64(o[0, h][torch.as_tensor(rows, device=o.device)])
         lg = lse[0, h][torch.as_tensor(rows, device=o.device)].cpu().numpy().astype(np.float64)
         # check_attention indexes og/lse by row, so scatter the sampled rows back
@@ -83,18 +140,17 @@ def run_config(i, n_uniform=10, n_tiles=2, extra_rows=(), whole_layer_check=None
         lfull = np.zeros(spec.L)
         ofull[rows], lfull[rows] = og, lg
         check_attention(hi, qh, kh, vh, ofull, lfull, scale, rows,
-                        name=f"{spec.name} head {h} ({spec.heads[h]['pattern']}/"
-                             f"{spec.heads[h].get('layout', 'plain')})")
+                        name=f"{spec.name} head {h} ({c['pattern']}/{c.get('layout', 'plain')})")
         nT = -(-spec.L // 64)
         tiles = sorted({0, nT - 1} | set(int(t) for t in rng.integers(0, nT, n_tiles))
                        | {int(r) // 64 for r in extra_rows if 0 <= r < spec.L})
         check_tile_pairs(Lg, h, hi, tiles)
-        say(f"{spec.name}: head {h} {spec.heads[h]['pattern']}/{spec.heads[h].get('layout', 'plain')} ok "
+        say(f"{spec.name}: head {h} {c['pattern']}/{c.get('layout', 'plain')} ok "
             f"({len(rows)} rows, tiles {tiles}) in {time.time() - t1:.1f} s")
-        del qh, kh, vh, hi
+        del qh, kh, vh
     if whole_layer_check is not None:
         whole_layer_check(spec, Lg)
-    del Lg, q, k, v, o, lse
+    del Lg, q, k, v, o, lse, his
     torch.cuda.empty_cache()
 
 
@@ -115,8 +171,10 @@ def test_video_grid_314k():
 
 @pytest.mark.timeout(600)
 def test_video_grid_314k_window():
-    # grid heads with the text prompt as sink and a four-frame local window
-    run_config(8)
+    # grid heads with the text prompt as sink and a four-frame local window;
+    # the index sets are those of the plain 314K layer (same inputs), so only
+    # the representative heads' sets are rechecked here
+    run_config(8, index_heads="representative")
 
 
 @pytest.mark.timeout(600)
@@ -166,5 +224,6 @@ def test_pevlm_video_101k():
 @pytest.mark.timeout(600)
 def test_mixed_1m_segments():
     # per-segment estimation on the 15-segment 1M layer: rows at every segment
-    # edge (run_config adds them) of the per-segment heads
-    run_config(7, n_uniform=6, n_tiles=1, layouts=("q_segment",))
+    # edge (run_config adds them) of the per-segment heads; the other heads
+    # are those of the 1M layer checked above
+    run_config(7, n_uniform=6, n_tiles=1, layouts=("q_segment",), index_heads="representative")
