@@ -148,12 +148,14 @@ __device__ __forceinline__ void attn_pair(AttnSmem<D>& sm, const Dims& dm, const
   {
     const bf16_t* qrow = (H.ws_qperm >= 0) ? wsp<const bf16_t>(ws, H.ws_qperm) + (int64_t)slot * D
                                            : q + H.q_off + (int64_t)(qpos < 0 ? 0 : qpos) * dm.q_sl;
+    // all fragments in flight at once: a row without a token reads the head's
+    // row 0 (or its padding slot) and is zeroed afterwards
     uint4 u[NS];
 #pragma unroll
-    for (int s = 0; s < NS; ++s) {
-      u[s] = make_uint4(0, 0, 0, 0);
-      if (qpos >= 0) u[s] = ld16(qrow + 16 * s + 8 * hh);
-    }
+    for (int s = 0; s < NS; ++s) u[s] = ld16(qrow + 16 * s + 8 * hh);
+#pragma unroll
+    for (int s = 0; s < NS; ++s)
+      if (qpos < 0) u[s] = make_uint4(0, 0, 0, 0);
     // Consume the fragments here, once: afterwards they are plain register values,
     // not loads in flight, so the chunk loop never has to wait for them.
 #pragma unroll

@@ -18,7 +18,7 @@
 // gathered key positions that no listed tile holds, the exact number of
 // selected (query, key) pairs, and a cost (tiles + gathered chunks) used to
 // order the attention work queue from most to least expensive.
-#include "mmsa_device.h"
+#include "block_scan.h"
 
 namespace mmsa {
 
@@ -192,15 +192,6 @@ __device__ __forceinline__ void bm_set_range(uint64_t* bm, int a, int b) {
   }
 }
 
-// number of set bits strictly below `bit`
-__device__ __forceinline__ int bm_popc_below(const uint64_t* bm, int bit) {
-  int c = 0;
-  const int wl = bit >> 6;
-  for (int w = 0; w < wl; ++w) c += __popcll(bm[w]);
-  if (bit & 63) c += __popcll(bm[wl] & ((1ull << (bit & 63)) - 1));
-  return c;
-}
-
 __device__ __forceinline__ int count_le(const int32_t* a, int n, int p) {   // entries <= p of an ascending array
   int lo = 0, hi = n;
   while (lo < hi) {
@@ -211,31 +202,42 @@ __device__ __forceinline__ int count_le(const int32_t* a, int n, int p) {   // e
   return lo;
 }
 
-// Plain vertical-slash heads: a selected diagonal at offset o = 64q + r
-// crosses key tile t - q of a full query tile t (rows 64t .. 64t+63), and tile
-// t - q - 1 too when r > 0.  Bit q of this per-head bitmap says whether some
-// selected diagonal reaches key tile t - q; a full tile's key tiles are then a
-// reversed shift of it (k_plan).  grid (heads), block 256, dynamic LDS =
-// bitmap words.
+// Index sets in original coordinates (plain, Q-boundary and per-segment
+// vertical-slash heads): a selected diagonal at offset o = 64q + r crosses key
+// tile t0 - q of a full query tile whose rows are 64t0 .. 64t0+63, and tile
+// t0 - q - 1 too when r > 0.  Bit q of this per-index-set bitmap says whether
+// some selected diagonal reaches key tile t0 - q; such a tile's key tiles are
+// then a reversed shift of it (k_plan).  grid (estimation jobs), block 256,
+// dynamic LDS = bitmap words.
+//
+// 2D-boundary index sets work in compacted coordinates (ranks within each
+// modality) with signed offsets o = S - (n_k - 1) >= -(n_k - 1): the bitmap is
+// taken over o + 64 * ceil((n_k - 1) / 64) >= 0, one per key modality (pair),
+// and k_plan shifts by that many tiles more.
 __global__ __launch_bounds__(256) void k_vs_shift(Tables tb, char* ws) {
-  const HeadDev& H = wsp<const HeadDev>(ws, tb.off_heads)[blockIdx.x];
-  if (H.ws_shift < 0) return;
+  const EstJob& J = wsp<const EstJob>(ws, tb.off_jobs)[blockIdx.x];
+  if (J.kind != JOB_VS_ORIG && J.kind != JOB_VS_2D) return;
   extern __shared__ uint64_t mb[];
-  const int W = H.bm_words, tid = threadIdx.x;
-  for (int w = tid; w < W; w += 256) mb[w] = 0ull;
-  __syncthreads();
-  const EstJob& J = wsp<const EstJob>(ws, tb.off_jobs)[H.job[0]];
-  const PairDev& Pd = J.pair[0];
-  const int ns = min(max(wsp<const int32_t>(ws, Pd.ws_nsel)[1], 0), Pd.ks);
-  const int32_t* S = wsp<const int32_t>(ws, Pd.ws_sidx);
-  for (int e = tid; e < ns; e += 256) {
-    const int o = max(S[e], 0), q = o >> 6;
-    if (q < 64 * W) bm_set(mb, q);
-    if ((o & 63) && q + 1 < 64 * W) bm_set(mb, q + 1);
+  const int tid = threadIdx.x;
+  for (int pi = 0; pi < J.n_pairs; ++pi) {
+    const PairDev& Pd = J.pair[pi];
+    if (Pd.ws_shift < 0) continue;
+    const int SW = Pd.shift_words;
+    for (int w = tid; w < SW; w += 256) mb[w] = 0ull;
+    __syncthreads();
+    const int ns = min(max(wsp<const int32_t>(ws, Pd.ws_nsel)[1], 0), Pd.ks);
+    const int32_t* S = wsp<const int32_t>(ws, Pd.ws_sidx);
+    const int shift = J.kind == JOB_VS_2D ? 64 * ((Pd.n_k - 1 + 63) >> 6) - (Pd.n_k - 1) : 0;
+    for (int e = tid; e < ns; e += 256) {
+      const int o = max(S[e] + shift, 0), q = o >> 6;
+      if (q < 64 * SW) bm_set(mb, q);
+      if ((o & 63) && q + 1 < 64 * SW) bm_set(mb, q + 1);
+    }
+    __syncthreads();
+    uint64_t* out = wsp<uint64_t>(ws, Pd.ws_shift);
+    for (int w = tid; w < SW; w += 256) out[w] = mb[w];
+    __syncthreads();
   }
-  __syncthreads();
-  uint64_t* out = wsp<uint64_t>(ws, H.ws_shift);
-  for (int w = tid; w < W; w += 256) out[w] = mb[w];
 }
 
 __global__ __launch_bounds__(256) void k_plan(Dims dm, Tables tb, char* ws) {
@@ -377,20 +379,74 @@ __global__ __launch_bounds__(256) void k_plan(Dims dm, Tables tb, char* ws) {
     }
     __syncthreads();
     const int nruns = sh_nruns;
-    // a full tile of a plain head (rows 64t .. 64t+63): its key tiles are the
-    // per-head shift bitmap reversed and shifted by t (no per-diagonal work)
-    const bool shifted = H.ws_shift >= 0 && nrows == 64 && nruns == 1 && sh_run_r0[0] == 64 * t;
+    // a full tile whose rows are one run starting on a tile boundary (rows
+    // 64t0 .. 64t0+63): its key tiles are the index set's shift bitmap
+    // reversed and shifted by t0 (no per-diagonal work)
+    const int64_t shift_off = twod ? -1 : J.pair[0].ws_shift;
+    const bool shifted = shift_off >= 0 && nrows == 64 && nruns == 1 && (sh_run_r0[0] & 63) == 0;
     if (shifted) {
-      const uint64_t* M = wsp<const uint64_t>(ws, H.ws_shift);
+      const uint64_t* M = wsp<const uint64_t>(ws, shift_off);
+      const int SW = J.pair[0].shift_words;
+      const int t0 = sh_run_r0[0] >> 6;
       for (int w = tid; w < W; w += 256) {
-        const int base = t - 64 * w - 63;   // bit b of word w (key tile 64w + b) <- shift bit t - 64w - b
+        const int base = t0 - 64 * w - 63;   // bit b of word w (key tile 64w + b) <- shift bit t0 - 64w - b
         const int wi = base >> 6, sh = base & 63;
-        uint64_t X = (wi >= 0 && wi < W) ? M[wi] >> sh : 0ull;
-        if (sh && wi + 1 >= 0 && wi + 1 < W) X |= M[wi + 1] << (64 - sh);
+        uint64_t X = (wi >= 0 && wi < SW) ? M[wi] >> sh : 0ull;
+        if (sh && wi + 1 >= 0 && wi + 1 < SW) X |= M[wi + 1] << (64 - sh);
         bm[w] = __builtin_bitreverse64(X);
       }
     }
-    for (int pi = 0; pi < (shifted ? 0 : J.n_pairs); ++pi) {
+    // a full 2D-boundary tile (64 consecutive ranks from a multiple of 64):
+    // per key modality, the pair's shift bitmap reversed and shifted by the
+    // tile's rank tile plus the offset shift, clipped to that modality's
+    // key tiles of the grouped view
+    bool shifted2 = twod && nrows == 64 && (sh_run_r0[0] & 63) == 0;
+    for (int pi = 0; pi < J.n_pairs; ++pi) shifted2 = shifted2 && J.pair[pi].ws_shift >= 0;
+    if (shifted2) {
+      const int tr = sh_run_r0[0] >> 6;
+      for (int pi = 0; pi < J.n_pairs; ++pi) {
+        const PairDev& Pd = J.pair[pi];
+        const uint64_t* M = wsp<const uint64_t>(ws, Pd.ws_shift);
+        const int SW = Pd.shift_words;
+        const int tb0 = (Pd.m_k == MMSA_VIDEO ? dm.video_base : dm.text_base) >> 6;
+        const int ntk = (Pd.n_k + 63) >> 6;
+        const int T = tr + ((Pd.n_k - 1 + 63) >> 6) + tb0;   // shift bit of view tile v: T - v
+        for (int w = tid; w < W; w += 256) {
+          const int lo = max(tb0, 64 * w), hi = min(tb0 + ntk, 64 * w + 64);
+          if (lo >= hi) continue;
+          const int base = T - 64 * w - 63;
+          const int wi = base >> 6, sh = base & 63;
+          uint64_t X = (wi >= 0 && wi < SW) ? M[wi] >> sh : 0ull;
+          if (sh && wi + 1 >= 0 && wi + 1 < SW) X |= M[wi + 1] << (64 - sh);
+          const uint64_t keep = (hi - 64 * w == 64 ? ~0ull : ((1ull << (hi - 64 * w)) - 1)) & ~((1ull << (lo - 64 * w)) - 1);
+          bm[w] |= __builtin_bitreverse64(X) & keep;
+        }
+      }
+      __syncthreads();
+      // A partial last key tile of a modality: the bitmap cannot tell whether a
+      // diagonal enters it before or after its last real key, so its bit is
+      // decided from the diagonals themselves.
+      for (int pi = 0; pi < J.n_pairs; ++pi) {
+        const PairDev& Pd = J.pair[pi];
+        if ((Pd.n_k & 63) == 0) continue;
+        const int ns = min(max(wsp<const int32_t>(ws, Pd.ws_nsel)[1], 0), Pd.ks);
+        const int32_t* S = wsp<const int32_t>(ws, Pd.ws_sidx);
+        const int r_lo = Pd.n_k & ~63, r_hi = Pd.n_k - 1, a = sh_run_r0[0];
+        int hit = 0;
+        for (int e = tid; e < ns; e += 256) {
+          const int o = S[e] - (Pd.n_k - 1);
+          hit |= (a - o <= r_hi) && (a + 63 - o >= r_lo);
+        }
+        hit = __syncthreads_or(hit);
+        if (tid == 0) {
+          const int v = ((Pd.m_k == MMSA_VIDEO ? dm.video_base : dm.text_base) >> 6) + (Pd.n_k >> 6);
+          if (hit) bm[v >> 6] |= 1ull << (v & 63);
+          else bm[v >> 6] &= ~(1ull << (v & 63));
+        }
+        __syncthreads();
+      }
+    }
+    for (int pi = 0; pi < ((shifted || shifted2) ? 0 : J.n_pairs); ++pi) {
       const PairDev& Pd = J.pair[pi];
       const int32_t* nsel = wsp<const int32_t>(ws, Pd.ws_nsel);
       const int ns = min(max(nsel[1], 0), Pd.ks);
@@ -457,6 +513,35 @@ __global__ __launch_bounds__(256) void k_plan(Dims dm, Tables tb, char* ws) {
   }
   __syncthreads();
 
+  // popcount prefix of the bitmap words (wpre[w]: set bits in words < w), so
+  // a row's count of listed tiles below its own is one lookup, not a walk
+  // over up to L/4096 words
+  int* wpre = reinterpret_cast<int*>(bm + W);
+  const bool use_pre = W > 16;   // short bitmaps: the walk is cheaper than the scan's barriers
+  if (use_pre) {
+    int carry = 0;
+    for (int base = 0; base < W; base += 256) {
+      const int w = base + tid;
+      const int c = w < W ? __popcll(bm[w]) : 0;
+      int tot;
+      const int ex = block_excl_sum(c, red, &tot);
+      if (w < W) wpre[w] = carry + ex;
+      carry += tot;
+    }
+    if (tid == 0) wpre[W] = carry;
+  }
+  __syncthreads();
+  auto popc_below = [&](int bit) -> int {   // set bits strictly below `bit`
+    const int wl = bit >> 6;
+    int c = 0;
+    if (use_pre) {
+      c = wpre[wl];
+    } else {
+      for (int w = 0; w < wl; ++w) c += __popcll(bm[w]);
+    }
+    return c + ((bit & 63) ? __popcll(bm[wl] & ((1ull << (bit & 63)) - 1)) : 0);
+  };
+
   // exact selected pairs of each row
   long long my_pairs = 0;
   if (tid < 64 && pos >= 0) {
@@ -484,7 +569,7 @@ __global__ __launch_bounds__(256) void k_plan(Dims dm, Tables tb, char* ws) {
       }
     } else if (H.view_kind == VIEW_IDENTITY) {
       const int cp = p >> 6;
-      my_pairs = 64ll * bm_popc_below(bm, cp) + (bm_get(bm, cp) ? (p - 64 * cp + 1) : 0);
+      my_pairs = 64ll * popc_below(cp) + (bm_get(bm, cp) ? (p - 64 * cp + 1) : 0);
       if (H.pattern == MMSA_VS) my_pairs += count_le(gl, g_cnt, p);
     } else {  // grouped key view (2D boundary)
       const int slot = wsp<const int32_t>(ws, dm.ws_gslot)[p];
@@ -497,13 +582,13 @@ __global__ __launch_bounds__(256) void k_plan(Dims dm, Tables tb, char* ws) {
       long long c = 0;
       if (kt > 0) {
         const int ct = kt >> 6;
-        c += 64ll * (bm_popc_below(bm, tb0 + ct) - bm_popc_below(bm, tb0));
+        c += 64ll * (popc_below(tb0 + ct) - popc_below(tb0));
         if ((kt & 63) && ct < ntt && bm_get(bm, tb0 + ct)) c += kt & 63;
       }
       if (kv > 0) {
         const int ntv = (dm.n_video + 63) >> 6;
         const int cv = kv >> 6;
-        c += 64ll * (bm_popc_below(bm, vb0 + cv) - bm_popc_below(bm, vb0));
+        c += 64ll * (popc_below(vb0 + cv) - popc_below(vb0));
         if ((kv & 63) && cv < ntv && bm_get(bm, vb0 + cv)) c += kv & 63;
       }
       const int gp = sh_gpart;
@@ -623,10 +708,12 @@ __global__ __launch_bounds__(64) void k_queue_reset(Dims dm, char* ws) {
 }
 
 hipError_t launch_plan(const Dims& dm, const Tables& tb, char* ws, int max_tiles, int max_bm_words,
-                       hipStream_t s) {
+                       int max_shift_words, hipStream_t s) {
   if (max_tiles > 0 && tb.n_heads > 0) {
-    k_vs_shift<<<(unsigned)tb.n_heads, 256, (size_t)max_bm_words * 8, s>>>(tb, ws);
-    k_plan<<<dim3(max_tiles, (unsigned)tb.n_heads), 256, (size_t)max_bm_words * 8, s>>>(dm, tb, ws);
+    if (tb.n_jobs > 0 && max_shift_words > 0)
+      k_vs_shift<<<(unsigned)tb.n_jobs, 256, (size_t)max_shift_words * 8, s>>>(tb, ws);
+    // dynamic LDS: the bitmap words, then their popcount prefix
+    k_plan<<<dim3(max_tiles, (unsigned)tb.n_heads), 256, (size_t)max_bm_words * 12 + 4, s>>>(dm, tb, ws);
     k_queue_enum<<<dim3((max_tiles / 2 + 64) / 64, (unsigned)tb.n_heads), 64, 0, s>>>(dm, tb, ws);
   }
   return hipGetLastError();

@@ -77,7 +77,7 @@ struct Layout {
   std::vector<char> blob;
   int64_t ws_total = 0;
   int n_chunks1 = 0, n_wg1 = 0, n_chunks2 = 0, n_wg2 = 0, max_ds = 0, max_strides = 0, nB = 0, max_tiles = 0, max_bm_words = 0;
-  int max_gather_slots = 0, max_unperm_slots = 0;
+  int max_gather_slots = 0, max_unperm_slots = 0, max_shift_words = 0;
   int64_t max_items = 0;
   int64_t max_topk_slices = 0;
   int64_t zero_off = 0, zero_bytes = 0;       // vertical scores and slash accumulators
@@ -777,6 +777,17 @@ mmsa_status build_layout(const mmsa_layer_desc* desc, Layout& Lo) {
       PairDev& P = J.pair[pi];
       if (J.kind == JOB_VS_ORIG || J.kind == JOB_VS_2D) {
         P.ws_s = bp.take(4ll * P.Ds);
+        // shift bitmap of the index set: bits up to the last query tile of
+        // the region's modality plus the shift that makes 2D-boundary offsets
+        // non-negative (a diagonal further out reaches no key tile), and two
+        // more
+        {
+          const int64_t n_q = J.kind == JOB_VS_2D ? Lo.n_mod[J.m_q] : L;
+          const int64_t offt = J.kind == JOB_VS_2D ? (P.n_k - 1 + 63) / 64 : 0;
+          P.shift_words = (int)(((n_q + 63) / 64 + offt + 2 + 63) / 64);
+          P.ws_shift = bp.take(8ll * P.shift_words);
+          Lo.max_shift_words = std::max(Lo.max_shift_words, P.shift_words);
+        }
         P.ws_vidx = bp.take(4ll * std::max(P.kv, 1));
         P.ws_sidx = bp.take(4ll * std::max(P.ks, 1));
         P.ws_nsel = bp.take(8);
@@ -788,7 +799,8 @@ mmsa_status build_layout(const mmsa_layer_desc* desc, Layout& Lo) {
         Lo.max_topk_slices = std::max<int64_t>(Lo.max_topk_slices, std::max(topk_slices(P.v_hi - P.v_lo),
                                                                             topk_slices(P.s_hi - P.s_lo)));
       } else {
-        P.ws_s = P.ws_vidx = P.ws_sidx = P.ws_nsel = -1;
+        P.ws_s = P.ws_vidx = P.ws_sidx = P.ws_nsel = P.ws_shift = -1;
+        P.shift_words = 0;
       }
     }
   }
@@ -858,7 +870,6 @@ mmsa_status build_layout(const mmsa_layer_desc* desc, Layout& Lo) {
   // plans
   for (HeadDev& H : Lo.heads) {
     H.ws_bm = bp.take(8ll * H.nT_rows * H.bm_words);
-    H.ws_shift = (H.pattern == MMSA_VS && H.layout == MMSA_PLAIN) ? bp.take(8ll * H.bm_words) : -1;
     H.ws_info = bp.take(16ll * H.nT_rows);
     H.ws_pairs = bp.take(8ll * H.nT_rows);
     if (H.gcap > 0) H.ws_gather = bp.take(4ll * H.nT_rows * H.gcap);
@@ -1028,7 +1039,7 @@ mmsa_status run_permute(const Layout& Lo, const void* q, const void* k, const vo
     MMSA_HIP(launch_grid_rows(Lo.dm, Lo.tb, w, s), "grid row order");
   }
   MMSA_HIP(launch_gather(Lo.dm, Lo.tb, w, q, k, v, Lo.max_gather_slots, s), "gather");
-  MMSA_HIP(launch_plan(Lo.dm, Lo.tb, w, Lo.max_tiles, Lo.max_bm_words, s), "plan");
+  MMSA_HIP(launch_plan(Lo.dm, Lo.tb, w, Lo.max_tiles, Lo.max_bm_words, Lo.max_shift_words, s), "plan");
   return MMSA_OK;
 }
 

@@ -68,8 +68,6 @@ struct HeadDev {
   int64_t ws_gather;         // int32 [nT_rows][gcap]
   int64_t ws_blk_idx;        // int32 [nB][k_blocks]
   int64_t ws_qp, ws_kp, ws_z;// BLOCK: pooled Q (fp32 [nB][d]), pooled K of (b,g), logits [nB][nB]
-  int64_t ws_shift;          // plain VS: uint64 [bm_words], bit q = some selected diagonal reaches
-                             // key tile t - q from a full query tile t, else -1
 };
 
 // One score pair of an estimation job: the vectors a region produces for one
@@ -80,8 +78,13 @@ struct PairDev {
   int32_t kv, ks;            // budgets after clamping
   int32_t v_lo, v_hi, s_lo, s_hi;  // candidate ranges
   int32_t n_k;               // keys of m_k (2D), else L
+  int32_t shift_words;       // uint64 words of ws_shift
+  int32_t _pad_pair;
   int64_t ws_v, ws_s, ws_sacc;     // float[Dv], float[Ds], int64[Ds]
   int64_t ws_vidx, ws_sidx, ws_nsel; // int32[kv], int32[ks], int32[2]
+  int64_t ws_shift;          // uint64 [shift_words], bit q = some selected diagonal reaches key tile
+                             // t0 - q from a full query tile whose rows (ranks, for 2D pairs, with the
+                             // offsets shifted to be non-negative) start at 64 * t0; else -1
 };
 
 // One estimation region: up to 64 rows of one head.
@@ -209,7 +212,7 @@ hipError_t launch_grid_rows(const Dims& dm, const Tables& tb, char* ws, hipStrea
 hipError_t launch_gather(const Dims& dm, const Tables& tb, char* ws, const void* q, const void* k,
                          const void* v, int max_slots, hipStream_t s);
 hipError_t launch_plan(const Dims& dm, const Tables& tb, char* ws, int max_tiles, int max_bm_words,
-                       hipStream_t s);
+                       int max_shift_words, hipStream_t s);
 
 hipError_t launch_queue_reset(const Dims& dm, char* ws, hipStream_t s);
 hipError_t launch_attention(const Dims& dm, const Tables& tb, char* ws, const void* q, const void* k,

@@ -65,6 +65,26 @@ def test_grid_with_window_d64_materialized():
     full_check(spec, materialize=True)
 
 
+def test_boundary_layouts_on_tile_aligned_segments():
+    # segments on 64-token boundaries: the full tiles of Q-boundary and
+    # per-segment heads take the shifted-bitmap plan, as plain heads do
+    segs = [(0, 128, TEXT), (128, 640, VIDEO), (768, 192, TEXT), (960, 576, VIDEO), (1536, 37, TEXT)]
+    heads = [synth.vs(20, 60, "q_boundary"), synth.vs(12, 90, "q_segment"), synth.vs(15, 80),
+             synth.vs(25, 33, "boundary_2d")]
+    full_check(synth.small_spec("aligned", 1573, 4, 2, 128, heads, seed=71, segs=segs, period=64, period_amp=3.0))
+
+
+def test_boundary_long_single_modality_runs():
+    # a 7K-token video run: same-modality 2D pairs reach more query plus key
+    # tiles than the head's tile bitmap has bits (the plan's shift bitmaps
+    # must cover both)
+    segs = [(0, 640, TEXT), (640, 7040, VIDEO), (7680, 93, TEXT)]
+    heads = [synth.vs(30, 200, "boundary_2d"), synth.vs(30, 200, "q_boundary"), synth.vs(9, 700, "boundary_2d"),
+             synth.vs(9, 700)]
+    full_check(synth.small_spec("long-runs", 7773, 4, 2, 128, heads, seed=73, segs=segs, period=64,
+                                period_amp=3.0), rows_per_head=400)
+
+
 def test_boundary_layouts():
     full_check(boundary_spec())
 
