@@ -336,7 +336,8 @@ def main():
     ap.add_argument("--config", type=int, default=5)
     ap.add_argument("--no-cpu", action="store_true")
     ap.add_argument("--no-peaks", action="store_true")
-    ap.add_argument("--cpu-rows", type=int, default=24)
+    ap.add_argument("--cpu-rows", type=int, default=0,
+                    help="oracle rows per head kind (default: 24 at 1M tokens, more for shorter layers)")
     ap.add_argument("--copy-calibration", action="store_true")
     ap.add_argument("--peaks", action="store_true", help="measure the MFMA and copy peaks only")
     ap.add_argument("--materialize", action="store_true",
@@ -479,7 +480,9 @@ def main():
         del L
         torch.cuda.empty_cache()
         log("[bench] timing the CPU oracle on a bounded sample")
-        out["cpu_baseline"] = cpu_baseline(spec, lay, eff_flops, rows_per_head=args.cpu_rows)
+        # about the same oracle time at any length: a row costs ~ its causal length
+        rows = args.cpu_rows or max(24, min(768, int(24 * 1017856 / max(spec.L, 1))))
+        out["cpu_baseline"] = cpu_baseline(spec, lay, eff_flops, rows_per_head=rows)
     print(json.dumps(out), flush=True)
 
 
