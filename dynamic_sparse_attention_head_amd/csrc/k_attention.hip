@@ -21,7 +21,10 @@
 // d column.  The pipeline runs K one chunk ahead of V: while chunk n's softmax
 // and P.V run, S^T of chunk n+1 is computed (its MFMAs interleaved with the
 // softmax arithmetic), and the copies of K for chunk n+2 and V for chunk n+1
-// are in flight.  Masking is element-wise on original positions (causal,
+// are in flight.  Each wave issues the copies of its own rows, except in a
+// step that only one tile of the pair computes: there the other tile's waves
+// issue all of them, since a burst of copies stalls the issuing wave for
+// hundreds of cycles.  Masking is element-wise on original positions (causal,
 // A-shape window, parallel-encoding blocks) and runs only for chunks holding
 // a key that some row of the wave does not see.  The running max moves only when a row's max grows by more than
 // 2^LAZY, so rescales of O are rare.
@@ -254,7 +257,6 @@ __device__ __forceinline__ void attn_pair(AttnSmem<D>& sm, const Dims& dm, const
   const int srow0 = w * PPW * RPI + lane / CPR;
   const uint32_t lchk0 = 16u * (uint32_t)((lane % CPR) ^ swz<D>(srow0));
   auto lchk = [&](int p) -> uint32_t { return lchk0 ^ (16u * (uint32_t)swz<D>(p * RPI)); };
-  const uint32_t kro = (uint32_t)srow0 * rb_view, vro = (uint32_t)srow0 * rbv_view;
   char* const kbuf0 = reinterpret_cast<char*>(sm.K[0]);
   char* const vbuf0 = reinterpret_cast<char*>(sm.V[0]);
   constexpr uint32_t BUFB = 64u * D * 2u;   // bytes of one K or V stage
@@ -262,33 +264,40 @@ __device__ __forceinline__ void attn_pair(AttnSmem<D>& sm, const Dims& dm, const
   // View tiles are contiguous rows of the view; gathered columns, and tiles of
   // an index-read grouped view, are rows listed by original position, read
   // from the chunk's key positions (KPOS_NONE: no token, copied as zeros).
-  auto dma_k = [&](const Chunk& c, int par, int ks) {
-    char* dst = kbuf0 + par * BUFB + (w * PPW) * 1024;
+  // A wave may also copy the rows of another wave slot ws: the slot moves the
+  // row by a multiple of 16, which leaves the swizzle (row bits 0-3) alone.
+  static_assert(PPW * RPI == 16, "16 rows per wave slot");
+  auto dma_k = [&](const Chunk& c, int par, int ks, int ws) {
+    char* dst = kbuf0 + par * BUFB + (ws * PPW) * 1024;
+    const int srow = srow0 + 16 * (ws - w);
     if (c.src < 0 && !grouped_idx) {
       // the tile's row offset goes into the vector offset, which the buffer's
       // range check covers: rows past the view's end read as zeros
       const uint32_t s0 = (uint32_t)(64 * c.idx) * rb_view;
+      const uint32_t ro = (uint32_t)srow * rb_view;
 #pragma unroll
-      for (int p = 0; p < PPW; ++p) dma16(rk_view, dst + p * 1024, kro + lchk(p) + s0 + (uint32_t)(p * RPI) * rb_view, 0);
+      for (int p = 0; p < PPW; ++p) dma16(rk_view, dst + p * 1024, ro + lchk(p) + s0 + (uint32_t)(p * RPI) * rb_view, 0);
     } else {
       int gi[PPW];
 #pragma unroll
-      for (int p = 0; p < PPW; ++p) gi[p] = sm.kp[ks][srow0 + p * RPI];
+      for (int p = 0; p < PPW; ++p) gi[p] = sm.kp[ks][srow + p * RPI];
 #pragma unroll
       for (int p = 0; p < PPW; ++p)
         dma16(rk, dst + p * 1024, gi[p] != KPOS_NONE ? (uint32_t)gi[p] * rbk + lchk(p) : OOB, 0);
     }
   };
-  auto dma_v = [&](const Chunk& c, int par, int ks) {
-    char* dst = vbuf0 + par * BUFB + (w * PPW) * 1024;
+  auto dma_v = [&](const Chunk& c, int par, int ks, int ws) {
+    char* dst = vbuf0 + par * BUFB + (ws * PPW) * 1024;
+    const int srow = srow0 + 16 * (ws - w);
     if (c.src < 0 && !grouped_idx) {
       const uint32_t s0 = (uint32_t)(64 * c.idx) * rbv_view;
+      const uint32_t ro = (uint32_t)srow * rbv_view;
 #pragma unroll
-      for (int p = 0; p < PPW; ++p) dma16(rv_view, dst + p * 1024, vro + lchk(p) + s0 + (uint32_t)(p * RPI) * rbv_view, 0);
+      for (int p = 0; p < PPW; ++p) dma16(rv_view, dst + p * 1024, ro + lchk(p) + s0 + (uint32_t)(p * RPI) * rbv_view, 0);
     } else {
       int gi[PPW];
 #pragma unroll
-      for (int p = 0; p < PPW; ++p) gi[p] = sm.kp[ks][srow0 + p * RPI];
+      for (int p = 0; p < PPW; ++p) gi[p] = sm.kp[ks][srow + p * RPI];
 #pragma unroll
       for (int p = 0; p < PPW; ++p)
         dma16(rv, dst + p * 1024, gi[p] != KPOS_NONE ? (uint32_t)gi[p] * rbv + lchk(p) : OOB, 0);
@@ -319,6 +328,11 @@ __device__ __forceinline__ void attn_pair(AttnSmem<D>& sm, const Dims& dm, const
       if (lane == 0) sm.kmin[par] = mn;
     }
   };
+  // A tile of an ungrouped key view holds the keys 64 idx .. 64 idx + 63 in
+  // order (those past the end are masked as later than every row), so its
+  // positions, their max and their min are arithmetic: nothing goes through
+  // LDS for it, and wave 0 neither loads nor stores its positions.
+  auto arith = [&](const Chunk& c) -> bool { return c.src < 0 && !grouped_view; };
 
   // Chunk sequence (uniform across the workgroup): the union of both tiles'
   // key tiles, then the gathered columns.  Key tiles go highest first --
@@ -429,19 +443,23 @@ __device__ __forceinline__ void attn_pair(AttnSmem<D>& sm, const Dims& dm, const
   };
   // mask and running-max update of one chunk's logits (the part of the softmax
   // that may branch); returns the max to subtract
-  auto soft_a = [&](floatx16 (&sa)[2], int ks, bool inv) -> float {
-    const int kmx = uniform(sm.kmax[ks]);
+  auto soft_a = [&](floatx16 (&sa)[2], int ks, bool inv, const Chunk& c) -> float {
+    const bool ar = arith(c);
+    const int kmx = ar ? 64 * c.idx + 63 : uniform(sm.kmax[ks]);
     bool full = kmx <= wave_qmin;
-    if (windowed) full = full && (kmx < sink || uniform(sm.kmin[ks]) >= wave_klomax);
+    if (windowed) full = full && (kmx < sink || (ar ? 64 * c.idx : uniform(sm.kmin[ks])) >= wave_klomax);
     full = full && !inv;
     if (!full) {
       // one lane-dependent base, constant offsets per (kb, i)
       const char* kpb = reinterpret_cast<const char*>(sm.kp[0]) + ks * 256 + 16 * hh;
+      const int kp0 = 64 * c.idx + 4 * hh;
 #pragma unroll
       for (int kb = 0; kb < 2; ++kb) {
 #pragma unroll
         for (int i = 0; i < 4; ++i) {
-          const int4 kk = *reinterpret_cast<const int4*>(kpb + 4 * (32 * kb + 8 * i));
+          const int e = 32 * kb + 8 * i;   // slot of kpv[0]
+          const int4 kk = ar ? make_int4(kp0 + e, kp0 + e + 1, kp0 + e + 2, kp0 + e + 3)
+                             : *reinterpret_cast<const int4*>(kpb + 4 * e);
           const int kpv[4] = {kk.x, kk.y, kk.z, kk.w};
 #pragma unroll
           for (int j = 0; j < 4; ++j) {
@@ -529,9 +547,10 @@ __device__ __forceinline__ void attn_pair(AttnSmem<D>& sm, const Dims& dm, const
   };
 
   // ---- prologue: positions of chunks 0-2; K, V of chunk 0; K of chunk 1 ----
-  // Key positions of chunk m live in LDS slot m % 4 from the end of step m-3
-  // (chunks 0-2: the prologue) until step m: the copies of K (step m-2) and V
-  // (step m-1) read their rows there, so no copy waits on a global load.
+  // Key positions of chunk m (other than an arithmetic view tile) live in LDS
+  // slot m % 4 from the end of step m-3 (chunks 0-2: the prologue) until step
+  // m: the copies of K (step m-2) and V (step m-1) read their rows there, so
+  // no copy waits on a global load.
   Chunk c0 = next_chunk(0), c1 = next_chunk(1), c2 = next_chunk(2), c3 = next_chunk(3);
   int kpreg = -1;
   bool kpval = false;
@@ -542,14 +561,14 @@ __device__ __forceinline__ void attn_pair(AttnSmem<D>& sm, const Dims& dm, const
       const int a = load_kp(c0, va);
       const int b = n_chunks > 1 ? load_kp(c1, vb) : -1;
       const int cc = n_chunks > 2 ? load_kp(c2, vc) : -1;
-      store_kp(a, va, 0);
-      if (n_chunks > 1) store_kp(b, vb, 1);
-      if (n_chunks > 2) store_kp(cc, vc, 2);
+      if (!arith(c0)) store_kp(a, va, 0);
+      if (n_chunks > 1 && !arith(c1)) store_kp(b, vb, 1);
+      if (n_chunks > 2 && !arith(c2)) store_kp(cc, vc, 2);
     }
     __syncthreads();
-    dma_k(c0, 0, 0);
-    dma_v(c0, 0, 0);
-    if (n_chunks > 1) dma_k(c1, 1, 1);
+    dma_k(c0, 0, 0, w);
+    dma_v(c0, 0, 0, w);
+    if (n_chunks > 1) dma_k(c1, 1, 1, w);
     asm volatile("s_waitcnt vmcnt(0)" ::: "memory");
     __syncthreads();
     launder();
@@ -562,15 +581,29 @@ __device__ __forceinline__ void attn_pair(AttnSmem<D>& sm, const Dims& dm, const
   auto step = [&](floatx16 (&scur)[2], floatx16 (&snxt)[2], int n, int par) {
     const bool has_n1 = n + 1 < n_chunks, has_n2 = n + 2 < n_chunks, has_n3 = n + 3 < n_chunks;
     launder();
-    // positions of chunk n+3, stored at the end of this step into the slot of
-    // chunk n-1 (read for the last time in the previous step)
-    if (has_n3 && w == 0) kpreg = load_kp(c3, kpval);
-    if (has_n2) dma_k(c2, par, (n + 2) & 3);       // K of n+2 replaces K of n (read by the previous step)
-    if (has_n1) dma_v(c1, par ^ 1, (n + 1) & 3);   // V of n+1 replaces V of n-1
+    // positions of chunk n+3 (unless arithmetic), stored at the end of this
+    // step into the slot of chunk n-1 (read for the last time in the previous
+    // step)
+    const bool kp3 = has_n3 && w == 0 && !arith(c3);
+    if (kp3) kpreg = load_kp(c3, kpval);
     const bool doS = wave_has && has_n1 && (c1.memb & wbit);
     const bool doP = wave_has && (c0.memb & wbit);
+    // Copies of K(n+2) over K(n) (read by the previous step) and of V(n+1)
+    // over V(n-1).  Each wave copies its own rows, except when only one tile
+    // of the pair computes chunk n: then the other tile's waves, which have
+    // at most S^T(n+1) to do, also copy the rows of the busy waves (slot w^2).
+    const bool other_busy = (w < 2 ? use1 : use0) && (c0.memb & (w < 2 ? 2 : 1));
+    const bool give = doP && !other_busy, take = !doP && other_busy;
+    if (has_n2) {
+      if (!give) dma_k(c2, par, (n + 2) & 3, w);
+      if (take) dma_k(c2, par, (n + 2) & 3, w ^ 2);
+    }
+    if (has_n1) {
+      if (!give) dma_v(c1, par ^ 1, (n + 1) & 3, w);
+      if (take) dma_v(c1, par ^ 1, (n + 1) & 3, w ^ 2);
+    }
     if (doP) {
-      const float m_use = soft_a(scur, n & 3, gridwin && c0.src >= 0);
+      const float m_use = soft_a(scur, n & 3, gridwin && c0.src >= 0, c0);
       uint32_t pk[16];
       // The two branches compute the same probabilities; each takes the max
       // through its own (different) empty asm, so the compiler cannot hoist
@@ -588,7 +621,7 @@ __device__ __forceinline__ void attn_pair(AttnSmem<D>& sm, const Dims& dm, const
       s_chunk(snxt, par ^ 1);
     }
     asm volatile("s_waitcnt vmcnt(0)" ::: "memory");
-    if (has_n3 && w == 0) store_kp(kpreg, kpval, (n + 3) & 3);
+    if (kp3) store_kp(kpreg, kpval, (n + 3) & 3);
     __syncthreads();
     c0 = c1;
     c1 = c2;
