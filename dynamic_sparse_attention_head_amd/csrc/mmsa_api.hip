@@ -2,14 +2,17 @@
 // kernels read, and the five ABI entry points declared in include/mmsa.h.
 //
 // Everything here runs on the host before any HIP call, so an invalid
-// descriptor is rejected without touching the device.  The per-call tables
-// (heads, estimation regions, tasks) are rebuilt from the descriptor by every
-// call and uploaded with one asynchronous copy to the start of the workspace.
+// descriptor is rejected without touching the device.  The tables (heads,
+// estimation regions, tasks) are built from the descriptor once and kept in a
+// small cache keyed by the descriptor's contents, so the five calls of a layer
+// build them once; every call uploads them with one asynchronous copy to the
+// start of the workspace.
 #include <algorithm>
 #include <cmath>
 #include <cstdarg>
 #include <cstdio>
 #include <cstring>
+#include <memory>
 #include <mutex>
 #include <string>
 #include <vector>
@@ -902,6 +905,81 @@ mmsa_status build_layout(const mmsa_layer_desc* desc, Layout& Lo) {
   return MMSA_OK;
 }
 
+// Layouts of recently seen descriptors.  A layout is a pure function of the
+// descriptor's values and of the arrays it points to (head configurations,
+// segments, KV-head map), so the key is those bytes; equal keys give the same
+// layout.  Descriptors the key cannot be read from safely (NULL arrays, sizes
+// out of range) and invalid descriptors are not cached: build_layout reports
+// them.  Entries are shared: one that is evicted stays alive for the calls
+// still holding it.
+constexpr int LAYOUT_CACHE_SIZE = 16;
+
+bool layout_key(const mmsa_layer_desc* desc, std::string& key) {
+  if (!desc) return false;
+  const mmsa_layer_desc& D = *desc;
+  if (D.Hq < 0 || D.Hq > 4096 || D.n_segs < 0 || D.n_segs > (1 << 20)) return false;
+  if (D.Hq > 0 && !D.heads) return false;
+  if (D.n_segs > 0 && !D.segs) return false;
+  key.clear();
+  key.reserve(128 + sizeof(mmsa_head_cfg) * D.Hq + 24ll * D.n_segs + 4ll * D.Hq);
+  auto put = [&](const void* p, size_t n) { key.append(static_cast<const char*>(p), n); };
+  const int32_t dims[6] = {D.B, D.Hq, D.Hkv, D.L, D.d, D.n_segs};
+  put(dims, sizeof dims);
+  put(D.q_strides, sizeof D.q_strides);
+  put(D.k_strides, sizeof D.k_strides);
+  put(D.v_strides, sizeof D.v_strides);
+  put(D.o_strides, sizeof D.o_strides);
+  put(&D.scale, sizeof D.scale);
+  put(&D.flags, sizeof D.flags);
+  if (D.Hq > 0) put(D.heads, sizeof(mmsa_head_cfg) * (size_t)D.Hq);   // twelve int32, no padding
+  for (int i = 0; i < D.n_segs; ++i) {
+    put(&D.segs[i].start, sizeof(int64_t));
+    put(&D.segs[i].len, sizeof(int64_t));
+    put(&D.segs[i].modality, sizeof(int32_t));
+  }
+  const char has_map = D.kv_head_of ? 1 : 0;
+  put(&has_map, 1);
+  if (D.kv_head_of && D.Hq > 0) put(D.kv_head_of, sizeof(int32_t) * (size_t)D.Hq);
+  return true;
+}
+
+mmsa_status get_layout(const mmsa_layer_desc* desc, std::shared_ptr<const Layout>& out) {
+  struct Entry {
+    std::string key;
+    std::shared_ptr<const Layout> lo;
+    uint64_t used;
+  };
+  static std::mutex mu;
+  static std::vector<Entry> cache;
+  static uint64_t clock = 0;
+  std::string key;
+  const bool keyed = layout_key(desc, key);
+  if (keyed) {
+    std::lock_guard<std::mutex> lock(mu);
+    for (Entry& e : cache)
+      if (e.key == key) {
+        e.used = ++clock;
+        out = e.lo;
+        return MMSA_OK;
+      }
+  }
+  auto lo = std::make_shared<Layout>();
+  const mmsa_status st = build_layout(desc, *lo);
+  if (st != MMSA_OK) return st;
+  out = lo;
+  if (keyed) {
+    std::lock_guard<std::mutex> lock(mu);
+    if ((int)cache.size() < LAYOUT_CACHE_SIZE) {
+      cache.push_back(Entry{std::move(key), out, ++clock});
+    } else {
+      auto lru = std::min_element(cache.begin(), cache.end(),
+                                  [](const Entry& a, const Entry& b) { return a.used < b.used; });
+      *lru = Entry{std::move(key), out, ++clock};
+    }
+  }
+  return MMSA_OK;
+}
+
 mmsa_status check_ptr(const void* p, const char* name) {
   if (!p) {
     set_err("%s is NULL", name);
@@ -914,9 +992,10 @@ mmsa_status check_ptr(const void* p, const char* name) {
   return MMSA_OK;
 }
 
-mmsa_status prepare(const mmsa_layer_desc* desc, void* ws, size_t ws_bytes, Layout& Lo) {
-  mmsa_status st = build_layout(desc, Lo);
+mmsa_status prepare(const mmsa_layer_desc* desc, void* ws, size_t ws_bytes, std::shared_ptr<const Layout>& lo) {
+  mmsa_status st = get_layout(desc, lo);
   if (st != MMSA_OK) return st;
+  const Layout& Lo = *lo;
   if (Lo.empty) return MMSA_OK;
   if (!ws) {
     set_err("workspace is NULL");
@@ -1079,9 +1158,9 @@ const char* mmsa_status_string(mmsa_status s) {
 const char* mmsa_last_error(void) { return g_err.c_str(); }
 
 size_t mmsa_workspace_bytes(const mmsa_layer_desc* desc) {
-  Layout Lo;
-  if (build_layout(desc, Lo) != MMSA_OK) return 0;
-  return (size_t)Lo.ws_total;
+  std::shared_ptr<const Layout> lo;
+  if (get_layout(desc, lo) != MMSA_OK) return 0;
+  return (size_t)lo->ws_total;
 }
 
 mmsa_status mmsa_workspace_view(const mmsa_layer_desc* desc, int32_t buf, int32_t bh, int32_t part,
@@ -1090,8 +1169,9 @@ mmsa_status mmsa_workspace_view(const mmsa_layer_desc* desc, int32_t buf, int32_
     set_err("offset_bytes/count is NULL");
     return MMSA_INVALID_ARGUMENT;
   }
-  Layout Lo;
-  MMSA_TRY(build_layout(desc, Lo));
+  std::shared_ptr<const Layout> lo;
+  MMSA_TRY(get_layout(desc, lo));
+  const Layout& Lo = *lo;
   *offset_bytes = 0;
   *count = 0;
   if (Lo.empty) return MMSA_OK;
@@ -1152,8 +1232,9 @@ mmsa_status mmsa_index_meta(const mmsa_layer_desc* desc, int32_t bh, int32_t par
     set_err("out is NULL");
     return MMSA_INVALID_ARGUMENT;
   }
-  Layout Lo;
-  MMSA_TRY(build_layout(desc, Lo));
+  std::shared_ptr<const Layout> lo;
+  MMSA_TRY(get_layout(desc, lo));
+  const Layout& Lo = *lo;
   for (int i = 0; i < 8; ++i) out[i] = 0;
   if (Lo.empty) return MMSA_OK;
   if (bh < 0 || bh >= Lo.BH || part < 0 || part >= (int)Lo.set_of[bh].size()) {
@@ -1183,8 +1264,9 @@ mmsa_status mmsa_index_meta(const mmsa_layer_desc* desc, int32_t bh, int32_t par
 
 mmsa_status mmsa_estimate_vs(const mmsa_layer_desc* desc, const void* q, const void* k, void* ws, size_t ws_bytes,
                              void* stream) {
-  Layout Lo;
-  MMSA_TRY(prepare(desc, ws, ws_bytes, Lo));
+  std::shared_ptr<const Layout> lo;
+  MMSA_TRY(prepare(desc, ws, ws_bytes, lo));
+  const Layout& Lo = *lo;
   if (Lo.empty || Lo.jobs.empty()) return MMSA_OK;
   MMSA_TRY(check_ptr(q, "q"));
   MMSA_TRY(check_ptr(k, "k"));
@@ -1194,8 +1276,9 @@ mmsa_status mmsa_estimate_vs(const mmsa_layer_desc* desc, const void* q, const v
 
 mmsa_status mmsa_estimate_blocks(const mmsa_layer_desc* desc, const void* q, const void* k, void* ws,
                                  size_t ws_bytes, void* stream) {
-  Layout Lo;
-  MMSA_TRY(prepare(desc, ws, ws_bytes, Lo));
+  std::shared_ptr<const Layout> lo;
+  MMSA_TRY(prepare(desc, ws, ws_bytes, lo));
+  const Layout& Lo = *lo;
   if (Lo.empty || !Lo.any_block) return MMSA_OK;
   MMSA_TRY(check_ptr(q, "q"));
   MMSA_TRY(check_ptr(k, "k"));
@@ -1205,8 +1288,9 @@ mmsa_status mmsa_estimate_blocks(const mmsa_layer_desc* desc, const void* q, con
 
 mmsa_status mmsa_permute(const mmsa_layer_desc* desc, const void* q, const void* k, const void* v, void* ws,
                          size_t ws_bytes, void* stream) {
-  Layout Lo;
-  MMSA_TRY(prepare(desc, ws, ws_bytes, Lo));
+  std::shared_ptr<const Layout> lo;
+  MMSA_TRY(prepare(desc, ws, ws_bytes, lo));
+  const Layout& Lo = *lo;
   if (Lo.empty) return MMSA_OK;
   MMSA_TRY(check_ptr(q, "q"));
   MMSA_TRY(check_ptr(k, "k"));
@@ -1217,8 +1301,9 @@ mmsa_status mmsa_permute(const mmsa_layer_desc* desc, const void* q, const void*
 
 mmsa_status mmsa_sparse_prefill(const mmsa_layer_desc* desc, const void* q, const void* k, const void* v, void* ws,
                                 size_t ws_bytes, void* o, float* lse, void* stream) {
-  Layout Lo;
-  MMSA_TRY(prepare(desc, ws, ws_bytes, Lo));
+  std::shared_ptr<const Layout> lo;
+  MMSA_TRY(prepare(desc, ws, ws_bytes, lo));
+  const Layout& Lo = *lo;
   if (Lo.empty) return MMSA_OK;
   MMSA_TRY(check_ptr(q, "q"));
   MMSA_TRY(check_ptr(k, "k"));
@@ -1230,8 +1315,9 @@ mmsa_status mmsa_sparse_prefill(const mmsa_layer_desc* desc, const void* q, cons
 }
 
 mmsa_status mmsa_unpermute(const mmsa_layer_desc* desc, void* ws, size_t ws_bytes, void* o, void* stream) {
-  Layout Lo;
-  MMSA_TRY(prepare(desc, ws, ws_bytes, Lo));
+  std::shared_ptr<const Layout> lo;
+  MMSA_TRY(prepare(desc, ws, ws_bytes, lo));
+  const Layout& Lo = *lo;
   if (Lo.empty) return MMSA_OK;
   MMSA_TRY(check_ptr(o, "o"));
   MMSA_TRY(check_device());
@@ -1240,8 +1326,9 @@ mmsa_status mmsa_unpermute(const mmsa_layer_desc* desc, void* ws, size_t ws_byte
 
 mmsa_status mmsa_prefill_noalloc(const mmsa_layer_desc* desc, const void* q, const void* k, const void* v, void* o,
                                  float* lse, void* stream) {
-  Layout Lo;
-  MMSA_TRY(build_layout(desc, Lo));
+  std::shared_ptr<const Layout> lo;
+  MMSA_TRY(get_layout(desc, lo));
+  const Layout& Lo = *lo;
   if (Lo.empty) return MMSA_OK;
   if (Lo.ws_total > (int64_t)MMSA_NOALLOC_SCRATCH_BYTES) {
     set_err("this layer needs %lld bytes of workspace; the static scratch of mmsa_prefill_noalloc holds %lld "

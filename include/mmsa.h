@@ -22,7 +22,10 @@
  *  - Ownership: the caller owns all device memory (Q, K, V, O, LSE and the
  *    workspace).  The library never allocates or frees device memory and keeps
  *    no pointer after a call returns.  Host arrays named in the descriptor are
- *    read only during the call.
+ *    read only during the call.  The tables derived from a descriptor are kept
+ *    in a small host-side cache (16 layouts, least recently used out), keyed by
+ *    the values of the descriptor and of its host arrays, so the five calls of
+ *    one layer build them once; a changed descriptor or array is a new key.
  *  - Asynchrony: every call enqueues work on `stream` (a hipStream_t; NULL is
  *    the null stream) and returns without waiting for the device.
  *  - Tensors: bf16, element strides (batch, head, row) with the last (head

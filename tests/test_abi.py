@@ -327,3 +327,60 @@ def test_noalloc_refuses_a_host_without_gfx950(L):
     p = 1 << 20
     assert L.mmsa_prefill_noalloc(ctypes.byref(small.desc), p, p, p, p, None, None) == UNSUPPORTED
     assert "gfx950" in last_error()
+
+
+def test_layout_cache_follows_the_descriptor_contents(L):
+    # The host tables are cached by the descriptor's contents: changing a head
+    # budget, a segment or a flag in place, or the KV-head map, must give the
+    # new layout, and returning to an earlier descriptor its old one.
+    lay = host_layer([synth.vs(10, 20), synth.block(4)], Lq=2000, Hkv=1)
+    assert lay.view_offset("v_index", 0)[1] == 10
+    lay._cfg[0].k_vertical = 25                       # in-place change of a host array
+    assert lay.view_offset("v_index", 0)[1] == 25
+    lay._cfg[1].k_blocks = 7
+    assert lay.view_offset("block_index", 1)[1] == 32 * 7
+    lay._cfg[0].k_vertical = 10
+    lay._cfg[1].k_blocks = 4
+    assert lay.view_offset("v_index", 0)[1] == 10
+    assert lay.view_offset("block_index", 1)[1] == 32 * 4
+
+    n_plain = lay.workspace_bytes()
+    lay.desc.flags = mmsa.FLAG_MATERIALIZE
+    lay2 = host_layer([synth.vs(10, 20, layout="boundary_2d"), synth.block(4)], Lq=2000, Hkv=1,
+                      segs=[(0, 500, 0), (500, 1500, 1)])
+    n2 = lay2.workspace_bytes()
+    lay2.desc.flags = mmsa.FLAG_MATERIALIZE
+    assert lay2.workspace_bytes() > n2                # grouped K/V copies are added
+    lay2.desc.flags = 0
+    assert lay2.workspace_bytes() == n2
+    lay.desc.flags = 0
+    assert lay.workspace_bytes() == n_plain
+
+    # a moved segment boundary moves the candidate ranges of the 2D pairs
+    m_before = lay2.meta(0, 2 * 1 + 1)                # (video rows, video keys)
+    lay2._segs[0].len = 700
+    lay2._segs[1].start, lay2._segs[1].len = 700, 1300
+    m_after = lay2.meta(0, 2 * 1 + 1)
+    assert m_before != m_after
+    lay2._segs[0].len = 500
+    lay2._segs[1].start, lay2._segs[1].len = 500, 1500
+    assert lay2.meta(0, 2 * 1 + 1) == m_before
+
+    # an invalid descriptor is reported every time, also after a valid one
+    lay.desc.heads = None
+    assert status_of(lay) != OK and "heads is NULL" in last_error()
+    lay.desc.heads = lay._cfg
+    assert status_of(lay) == OK
+
+    # the KV-head map is part of the key: a map that breaks the grouping is
+    # rejected although the same descriptor with the default map was cached
+    lay3 = host_layer([synth.vs(10, 20), synth.vs(10, 20)], Lq=2000, Hkv=2)
+    assert status_of(lay3) == OK
+    bad = (ctypes.c_int32 * 2)(0, 5)
+    lay3.desc.kv_head_of = bad
+    assert ws_status(lay3) == INVALID
+    good = (ctypes.c_int32 * 2)(1, 0)
+    lay3.desc.kv_head_of = good
+    assert status_of(lay3) == OK
+    good[1] = 7                                       # in-place change of the map
+    assert ws_status(lay3) == INVALID

@@ -225,6 +225,39 @@ def test_block_topk_breaks_exact_ties_to_the_lower_block():
         check_attention(hi, qn[h], kn[0], vn[0], on[h], ln[h], scale, np.arange(spec.L), name=f"ties head {h}")
 
 
+def test_vertical_topk_breaks_exact_ties_to_the_lower_key():
+    # key rows 300..420 are copies of row 100, made the strongest key of the
+    # estimation rows: their vertical scores tie exactly.  Head 0 keeps 40 of
+    # the 122 tied keys (the threshold inside the group: the lowest positions
+    # are kept), head 1 keeps 150 (the whole group and the next largest)
+    import math
+    from parity_util import check_attention, check_head_indices, f64
+    L_ = 64 * 20
+    spec = synth.small_spec("vties", L_, 2, 1, 128, [synth.vs(40, 64), synth.vs(150, 64)], seed=43)
+    lay = synth.make_layer(spec, "cuda")
+    q, k, v = lay["q"], lay["k"].clone(), lay["v"]
+    rows = q[0, :, L_ - 64:].float().sum(dim=(0, 1))
+    k[0, 0, 100] = (4.0 * rows / rows.norm() * math.sqrt(spec.d)).to(torch.bfloat16)
+    k[0, 0, 300:421] = k[0, 0, 100]
+    L, q, k, v, o, lse = run_gpu(spec, q=q, k=k, v=v)
+    scale = 1.0 / math.sqrt(spec.d)
+    qn, kn, vn, on = f64(q[0]), f64(k[0]), f64(v[0]), f64(o[0])
+    ln = lse[0].cpu().numpy().astype(np.float64)
+    tied = [100] + list(range(300, 421))
+    for h in range(spec.Hq):
+        vsc = L.view("v_scores", h, 0).cpu().numpy()
+        assert (vsc[tied] == vsc[100]).all()                    # the ties are exact
+        assert (vsc[tied[0]] >= np.delete(vsc, tied)).all()     # and they are the largest scores
+        hi = check_head_indices(L, h, spec.heads[h], qn[h], kn[0], spec.segs, scale)
+        V = hi.vs["all"][0]
+        kv = spec.heads[h]["k_vertical"]
+        if kv <= len(tied):   # the threshold inside the tied group: its lowest positions
+            assert list(V) == tied[:kv], f"head {h}: {list(V)[:8]}"
+        else:                 # the whole group, then the next largest scores
+            assert len(V) == kv and set(tied) <= set(V.tolist()), f"head {h}"
+        check_attention(hi, qn[h], kn[0], vn[0], on[h], ln[h], scale, np.arange(spec.L), name=f"vties head {h}")
+
+
 def test_empty_layer_is_noop():
     spec = synth.small_spec("empty", 0, 2, 1, 128, [synth.vs(3, 5), synth.ashape(4, 8)], seed=0)
     q = torch.empty((1, 2, 0, 128), dtype=torch.bfloat16, device="cuda")
