@@ -167,10 +167,11 @@ def attn_source_digest():
     return h.hexdigest()
 
 
-def read_traffic(workload):
-    """HBM bytes per attention launch from the committed counter summary of
-    this workload, or None when it is missing or was taken on other sources."""
-    path = os.path.join(PROFILES, f"k_attn_{workload}_traffic.md")
+def read_summary(workload, what):
+    """The machine-readable lines ("- key: value") of a committed counter
+    summary of the attention kernel on this workload, or None when it is
+    missing or was taken on other sources."""
+    path = os.path.join(PROFILES, f"k_attn_{workload}_{what}.md")
     if not os.path.exists(path):
         return None
     kv = {}
@@ -181,8 +182,25 @@ def read_traffic(workload):
                 kv[k.strip()] = v.strip().strip("`")
     if kv.get("attention sources sha256") != attn_source_digest():
         return None
+    return kv
+
+
+def read_traffic(workload):
+    """HBM bytes per attention launch (FETCH_SIZE + WRITE_SIZE, scaled)."""
+    kv = read_summary(workload, "traffic")
     try:
-        return int(float(kv["traffic bytes per launch"]))
+        return int(float(kv["traffic bytes per launch"])) if kv else None
+    except (KeyError, ValueError):
+        return None
+
+
+def read_mfma_busy(workload):
+    """Share of the launch's SIMD cycles in which the matrix cores were busy
+    (SQ_VALU_MFMA_BUSY_CYCLES over GRBM_GUI_ACTIVE), and the clock it ran at."""
+    kv = read_summary(workload, "mfma")
+    try:
+        return {"fraction": float(kv["mfma busy fraction"]), "clock_ghz": float(kv["clock ghz"]),
+                "counters": "rocprofv3 --pmc SQ_VALU_MFMA_BUSY_CYCLES GRBM_GUI_ACTIVE"} if kv else None
     except (KeyError, ValueError):
         return None
 
@@ -396,8 +414,6 @@ def main():
         torch.cuda.synchronize()
         log(f"[bench] warm-up step {i + 1}/{args.warmup} done")
     torch.cuda.synchronize()
-    pairs, tiles, staged = plan_totals(L, spec)
-    log(f"[bench] selected pairs {pairs:.4e}, computed 64x64 tiles {tiles}, staged chunks {staged}")
     # timed region: exactly K steps between two synchronisations
     evs = [[torch.cuda.Event(enable_timing=True) for _ in range(6)] for _ in range(args.steps)]
     torch.cuda.synchronize()
@@ -406,6 +422,10 @@ def main():
         step(evs[i])
     torch.cuda.synchronize()
     wall = time.perf_counter() - t0
+    # the plan every step rebuilt (read after the timed region, so that a run
+    # without warm-up steps reads a built plan too)
+    pairs, tiles, staged = plan_totals(L, spec)
+    log(f"[bench] selected pairs {pairs:.4e}, computed 64x64 tiles {tiles}, staged chunks {staged}")
     per = np.array([[e[c].elapsed_time(e[c + 1]) for c in range(5)] for e in evs])   # [steps, calls] ms
     per_step = per.sum(axis=1)
     mean_call = per.mean(axis=0)
@@ -421,7 +441,7 @@ def main():
     tile_flops = 4.0 * spec.d * 64 * 64 * tiles
     attn_roof = roof("mfma", tile_flops, attn_ms, PEAK_BF16_TFLOPS, "TFLOP/s")
     attn_roof.update({"traffic": read_traffic(spec.name), "kernel": "k_attn (mmsa_sparse_prefill)",
-                      "launch_ms": round(attn_ms, 3)})
+                      "launch_ms": round(attn_ms, 3), "mfma_busy": read_mfma_busy(spec.name)})
     if peaks:
         attn_roof["frac_of_measured_peak"] = round(attn_roof["achieved"] / peaks["mfma_bf16_tflops"], 4)
     # the other calls, each against the roof that bounds it
@@ -432,6 +452,8 @@ def main():
         calls_roof["estimate_vs"] = (roof("mfma", ef, mean_call[0], PEAK_BF16_TFLOPS, "TFLOP/s") if kind == "mfma"
                                      else roof("hbm", eb, mean_call[0], PEAK_HBM_GBPS, "GB/s"))
         calls_roof["estimate_vs"]["flop_per_byte"] = round(ef / eb, 1)
+        calls_roof["estimate_vs"]["hbm_gbps"] = round(eb / (mean_call[0] * 1e-3) / 1e9, 1)
+        calls_roof["estimate_vs"]["hbm_frac"] = round(eb / (mean_call[0] * 1e-3) / 1e9 / PEAK_HBM_GBPS, 4)
     bf, bb = block_work(spec)
     if bb > 0 and mean_call[1] > 0:
         calls_roof["estimate_blocks"] = roof("hbm", bb, mean_call[1], PEAK_HBM_GBPS, "GB/s")
