@@ -605,7 +605,7 @@ __global__ __launch_bounds__(TK_T) void k_topk_hist(Tables tb, char* ws, int rou
 #pragma unroll
   for (int j = 0; j < TK_E; ++j) {
     const int i = s0 + j * TK_T + tid;
-    if (i < s1 && (key[j] & st.mask) == st.pref) atomicAdd(&wh[wv][(key[j] >> shift) & 255u], 1u);
+    wave_hist_add(wh[wv], (key[j] >> shift) & 255u, i < s1 && (key[j] & st.mask) == st.pref);
   }
   __syncthreads();
   if (tid < 256) {
