@@ -114,3 +114,46 @@ def test_both_key_walk_orders_match_the_oracle(name):
     for h in range(spec.Hq):
         for buf in ("tile_bitmap", "tile_pairs", "tile_info"):
             assert torch.equal(La.view(buf, h), Ld.view(buf, h)), (h, buf)
+
+
+def test_layers_interleaved_on_one_stream_keep_their_own_tables():
+    # The host tables are cached by descriptor contents and uploaded by every
+    # call: two layers of different shape and patterns whose calls alternate
+    # on one stream (each with its own workspace), and a third layer that
+    # differs from the first only in one head's slash budget, must each produce the
+    # output they produce alone, bit for bit.
+    specs = [mixed_spec(L=1000, seed=61),
+             synth.small_spec("other", 777, 2, 1, 64, [synth.vs(20, 40), synth.ashape(32, 128)], seed=62)]
+    alone = []
+    for sp in specs:
+        L_, q, k, v, o, lse = run_gpu(sp)
+        alone.append((q, k, v, o))
+    heads3 = [dict(h) for h in specs[0].heads]
+    heads3[0]["k_slash"] = 3          # few slashes: head 0 keeps far fewer tiles
+    spec3 = synth.with_heads(specs[0], heads3)
+    q0, k0, v0, _ = alone[0]
+    _, _, _, _, o3_alone, _ = run_gpu(spec3, q=q0, k=k0, v=v0)
+    lay = [mmsa.Layer(alone[i][0], alone[i][1], alone[i][2], specs[i].heads, segs=specs[i].segs) for i in range(2)]
+    lay.append(mmsa.Layer(q0, k0, v0, spec3.heads, segs=spec3.segs))
+    ins = [alone[0][:3], alone[1][:3], (q0, k0, v0)]
+    outs = [torch.full_like(alone[0][3], float("nan")), torch.full_like(alone[1][3], float("nan")),
+            torch.full_like(o3_alone, float("nan"))]
+    for L_ in lay:
+        L_.alloc_workspace()
+    for _ in range(2):
+        for call in ("estimate_vs", "estimate_blocks", "permute"):
+            for i in (0, 1, 2):
+                q, k, v = ins[i]
+                if call == "permute":
+                    lay[i].permute(q, k, v)
+                else:
+                    getattr(lay[i], call)(q, k)
+        for i in (2, 0, 1):
+            q, k, v = ins[i]
+            lay[i].sparse_prefill(q, k, v, outs[i], None)
+            lay[i].unpermute(outs[i])
+    torch.cuda.synchronize()
+    want = [alone[0][3], alone[1][3], o3_alone]
+    for i in range(3):
+        assert torch.equal(outs[i].view(torch.int16), want[i].view(torch.int16)), f"layer {i}"
+    assert not torch.equal(outs[2].view(torch.int16), outs[0].view(torch.int16))   # the budget matters
