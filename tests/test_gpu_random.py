@@ -64,7 +64,7 @@ def random_spec(seed):
     return spec, bool(rng.integers(0, 4) == 0)
 
 
-@pytest.mark.parametrize("seed", range(48))
+@pytest.mark.parametrize("seed", range(160))
 def test_random_layer(seed):
     spec, materialize = random_spec(seed)
     full_check(spec, materialize=materialize, flags=mmsa.FLAG_KEYS_ASCENDING if seed % 2 else 0)
