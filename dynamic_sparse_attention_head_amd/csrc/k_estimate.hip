@@ -745,7 +745,22 @@ __global__ __launch_bounds__(1024) void k_grid_sum(Tables tb, char* ws) {
   int32_t* u = wsp<int32_t>(ws, T.ws_u);
   __shared__ long long part[1024];
   long long s = 0;
-  for (int x = threadIdx.x; x < T.D; x += blockDim.x) {
+  // eight loads in flight per thread (the sums are exact integers, so their
+  // order does not matter)
+  const int step = (int)blockDim.x;
+  int x = threadIdx.x;
+  for (; x + 7 * step < T.D; x += 8 * step) {
+    float vv[8];
+#pragma unroll
+    for (int j = 0; j < 8; ++j) vv[j] = v[x + j * step];
+#pragma unroll
+    for (int j = 0; j < 8; ++j) {
+      const int64_t ux = grid_u(vv[j], T.cap);
+      u[x + j * step] = (int32_t)ux;
+      s += ux;
+    }
+  }
+  for (; x < T.D; x += step) {
     const int64_t ux = grid_u(v[x], T.cap);
     u[x] = (int32_t)ux;
     s += ux;
@@ -787,8 +802,19 @@ __global__ __launch_bounds__(1024) void k_grid_scan(Tables tb, char* ws) {
   {
     const int S = MAX_STRIDE / sig, ph = f % sig, sl = f / sig;
     long long F = 0;
-    if (sl < S)
-      for (int64_t x = ph + (int64_t)sl * sig; x < T.D; x += (int64_t)S * sig) F += u[x];
+    if (sl < S) {
+      // eight loads in flight per thread (exact integer sums: any order)
+      const int64_t st = (int64_t)S * sig;
+      int64_t x = ph + (int64_t)sl * sig;
+      for (; x + 7 * st < T.D; x += 8 * st) {
+        int32_t uu[8];
+#pragma unroll
+        for (int j = 0; j < 8; ++j) uu[j] = u[x + j * st];
+#pragma unroll
+        for (int j = 0; j < 8; ++j) F += uu[j];
+      }
+      for (; x < T.D; x += st) F += u[x];
+    }
     part[f] = F;
   }
   __syncthreads();
