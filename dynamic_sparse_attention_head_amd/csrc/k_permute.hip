@@ -470,17 +470,37 @@ __global__ __launch_bounds__(256) void k_plan(Dims dm, Tables tb, char* ws) {
     }
     __syncthreads();
     if (twod) {
-      // drop view tiles whose first key comes after the tile's last row
-      for (int w = tid; w < W; w += 256) {
-        uint64_t bits = bm[w], keep = bits;
-        while (bits) {
-          const int b = __ffsll((unsigned long long)bits) - 1;
-          bits &= bits - 1;
-          const int first = pgrp[(int64_t)(64 * w + b) * 64];
-          if (first < 0 || first > qmax) keep &= ~(1ull << b);
+      // Drop view tiles whose first key comes after the tile's last row.  The
+      // tiles of a modality part of the grouped view hold that modality's keys
+      // by rank, so the first key of its k-th tile is the key of rank 64 k and
+      // the kept tiles are the first ceil(n / 64), n = keys of the modality at
+      // or before the last row, counted over the segments by wave 0.
+      if (wv == 0) {
+        const SegDev* segs = wsp<const SegDev>(ws, tb.off_segs);
+        long long n_m[2] = {0, 0};
+        for (int i = lane; i < (int)tb.n_segs; i += 64) {
+          const SegDev sg = segs[i];
+          const long long c = min((long long)sg.len, max(0ll, (long long)qmax + 1 - sg.start));
+          n_m[sg.modality == MMSA_VIDEO ? 1 : 0] += c;
         }
-        bm[w] = keep;
+        for (int m = 1; m < 64; m <<= 1) {
+          n_m[0] += __shfl_xor(n_m[0], m, 64);
+          n_m[1] += __shfl_xor(n_m[1], m, 64);
+        }
+        if (lane == 0) {
+          red[4] = (int)((n_m[0] + 63) >> 6);
+          red[5] = (int)((n_m[1] + 63) >> 6);
+        }
       }
+      __syncthreads();
+      const int tt0 = dm.text_base >> 6, tv0 = dm.video_base >> 6;
+      const int tt1 = tt0 + red[4], tv1 = tv0 + red[5];
+      auto range_bits = [](int w, int a, int b) -> uint64_t {   // bits of word w in [a, b)
+        const int lo = max(a, 64 * w) - 64 * w, hi = min(b, 64 * w + 64) - 64 * w;
+        if (lo >= hi) return 0ull;
+        return (hi == 64 ? ~0ull : ((1ull << hi) - 1)) & ~((1ull << lo) - 1);
+      };
+      for (int w = tid; w < W; w += 256) bm[w] &= range_bits(w, tt0, tt1) | range_bits(w, tv0, tv1);
       __syncthreads();
     }
     // gathered verticals not held by a listed tile, ascending per key modality
