@@ -163,6 +163,38 @@ def test_segment_layout_single_segment():
                                 seed=33, segs=[(0, 333, VIDEO)]))
 
 
+def many_segments_spec(n_seg=640, seed=41):
+    # 640 segments of 1-40 tokens with modalities drawn at random (an
+    # interleaved image-text document): hundreds of per-segment estimates per
+    # head, more estimation batches than one wave of workgroups, hundreds of
+    # segment-padded query tiles, and modality parts split into many runs
+    rng = np.random.default_rng(seed)
+    segs, pos = [], 0
+    for _ in range(n_seg):
+        n = int(rng.integers(1, 41))
+        segs.append((pos, n, int(rng.integers(0, 2))))
+        pos += n
+    heads = [synth.vs(20, 40, "q_segment"), synth.vs(12, 60, "q_segment"), synth.vs(20, 40, "boundary_2d"),
+             synth.vs(10, 30, "q_boundary"), synth.grid(1, 16, 64, layout="modality_grouped"), synth.block(6),
+             synth.vs(9, 50, "q_segment"), synth.grid(2, 16, 80, sink=30, window=200)]
+    return synth.small_spec("many-segments", pos, 8, 2, 64, heads, seed=seed, segs=segs, period=49, period_amp=3.0)
+
+
+def test_many_short_segments():
+    # every tile's pair count, attention on 400 sampled rows per head
+    full_check(many_segments_spec(), rows_per_head=400)
+
+
+def test_uneven_kv_head_map():
+    # a GQA map that is neither contiguous nor even: KV head 2 serves three q
+    # heads, KV head 0 two, KV head 1 one and KV head 3 none
+    segs = [(0, 300, TEXT), (300, 49 * 14, VIDEO), (986, 77, TEXT), (1063, 49 * 9, VIDEO)]
+    heads = [synth.vs(20, 40, "boundary_2d"), synth.block(5), synth.grid(1, 16, 64, layout="modality_grouped"),
+             synth.vs(15, 60), synth.ashape(32, 200), synth.vs(10, 30, "q_segment")]
+    spec = synth.small_spec("kv-map", 1504, 6, 4, 128, heads, seed=43, segs=segs, period=49, period_amp=3.0)
+    full_check(spec, kv_head_of=[2, 0, 2, 1, 0, 2])
+
+
 def test_parallel_encoding_ragged():
     # sink, context and question blocks off the 64-token tiles, a partial last
     # context block, a head with no sink or question, and 5-token blocks
