@@ -19,11 +19,11 @@ pytestmark = pytest.mark.gpu
 TEXT, VIDEO = 0, 1
 
 
-def random_head(rng, L, has_video):
+def random_head(rng, L, has_video, scale=1):
     kind = rng.choice(["ashape", "vs", "vs_qb", "vs_2d", "vs_seg", "block", "grid", "grid_grouped", "parallel"])
-    kv, ks = int(rng.integers(0, 80)), int(rng.integers(0, 200))
+    kv, ks = int(rng.integers(0, 80 * scale)), int(rng.integers(0, 200 * scale))
     if kind == "ashape":
-        return synth.ashape(int(rng.integers(0, 200)), int(rng.integers(1, 600)))
+        return synth.ashape(int(rng.integers(0, 200 * scale)), int(rng.integers(1, 600 * scale)))
     if kind == "vs":
         return synth.vs(kv, ks)
     if kind == "vs_qb":
@@ -33,14 +33,15 @@ def random_head(rng, L, has_video):
     if kind == "vs_seg":
         return synth.vs(kv, ks, "q_segment")
     if kind == "block":
-        return synth.block(int(rng.integers(0, 12)))
+        return synth.block(int(rng.integers(0, 12 * scale)))
     if kind == "parallel":
-        return synth.parallel(int(rng.integers(0, 300)), int(rng.integers(1, 400)), int(rng.integers(0, 300)))
+        return synth.parallel(int(rng.integers(0, 300 * scale)), int(rng.integers(1, 400 * scale)),
+                              int(rng.integers(0, 300 * scale)))
     layout = "modality_grouped" if kind == "grid_grouped" else "plain"
     lo = int(rng.integers(16, 60))
     sink, window = 0, 0
     if rng.integers(0, 2):      # half the grid heads add a sink and a local window
-        sink, window = int(rng.integers(0, 100)), int(rng.integers(0, 400))
+        sink, window = int(rng.integers(0, 100 * scale)), int(rng.integers(0, 400 * scale))
     return synth.grid(int(rng.integers(1, 4)), lo, lo + int(rng.integers(0, 120)), layout=layout,
                       sink=sink, window=window)
 
@@ -68,3 +69,32 @@ def random_spec(seed):
 def test_random_layer(seed):
     spec, materialize = random_spec(seed)
     full_check(spec, materialize=materialize, flags=mmsa.FLAG_KEYS_ASCENDING if seed % 2 else 0)
+
+
+def random_medium_spec(seed):
+    """4K-30K tokens: key-tile bitmaps of 2-8 words (the small layers above
+    fit one), 1-8 segments, budgets scaled up with the length."""
+    rng = np.random.default_rng(10_000 + seed)
+    L = int(rng.integers(4100, 30_000))
+    n_seg = int(rng.integers(1, 9))
+    cuts = np.sort(rng.choice(np.arange(1, L), n_seg - 1, replace=False)) if n_seg > 1 else np.array([], int)
+    bounds = [0, *[int(c) for c in cuts], L]
+    segs = [(bounds[i], bounds[i + 1] - bounds[i], int(rng.integers(0, 2))) for i in range(n_seg)]
+    d = int(rng.choice([64, 128]))
+    Hkv = int(rng.integers(1, 3))
+    Hq = Hkv * int(rng.integers(1, 4))
+    has_video = any(m == VIDEO for _, _, m in segs)
+    heads = [random_head(rng, L, has_video, scale=4) for _ in range(Hq)]
+    spec = synth.small_spec(f"random-medium{seed}", L, Hq, Hkv, d, heads, seed=2000 + seed, segs=segs,
+                            period=49, period_amp=3.0)
+    return spec
+
+
+@pytest.mark.parametrize("seed", range(8))
+def test_random_medium_layer(seed):
+    spec = random_medium_spec(seed)
+    rng = np.random.default_rng(seed)
+    n_tiles = -(-spec.L // 64)
+    tiles = sorted({0, n_tiles - 1} | set(int(t) for t in rng.integers(0, n_tiles, 40)))
+    full_check(spec, rows_per_head=256, pair_tiles=tiles, seed=seed,
+               flags=mmsa.FLAG_KEYS_ASCENDING if seed % 2 else 0)
