@@ -229,35 +229,76 @@ class Layer:
     def _stream():
         return ctypes.c_void_p(torch.cuda.current_stream().cuda_stream)
 
+    def _on_device(self, t):
+        dev = torch.device(self.device)
+        if dev.type == "cuda" and dev.index is None:
+            dev = torch.device("cuda", torch.cuda.current_device())
+        return t.device == dev
+
+    def _arg(self, t, name, heads, strides):
+        """A tensor handed to the library as a raw pointer must be what the
+        descriptor says it is: bf16 on the layer's device, [B, heads, L, d]
+        with the descriptor's strides (the library reads it through those)."""
+        shape = (self.B, heads, self.L, self.d)
+        if t.dtype != torch.bfloat16 or not self._on_device(t) or tuple(t.shape) != shape:
+            raise ValueError(f"{name}: expected bf16 {shape} on {self.device}, got {t.dtype} "
+                             f"{tuple(t.shape)} on {t.device}")
+        if t.numel() and (t.stride(3) != 1 or tuple(t.stride()[:3]) != tuple(strides)):
+            raise ValueError(f"{name}: strides {tuple(t.stride())} differ from the descriptor's "
+                             f"{tuple(strides)} (+1); build the Layer from tensors of this layout")
+        return t.data_ptr()
+
+    def _q(self, q):
+        return self._arg(q, "q", self.Hq, self.desc.q_strides)
+
+    def _k(self, k):
+        return self._arg(k, "k", self.Hkv, self.desc.k_strides)
+
+    def _v(self, v):
+        return self._arg(v, "v", self.Hkv, self.desc.v_strides)
+
+    def _o(self, o):
+        return self._arg(o, "o", self.Hq, self.desc.o_strides)
+
+    def _lse(self, lse):
+        if lse is None:
+            return None
+        shape = (self.B, self.Hq, self.L)
+        if (lse.dtype != torch.float32 or not self._on_device(lse) or tuple(lse.shape) != shape
+                or not lse.is_contiguous()):
+            raise ValueError(f"lse: expected contiguous float32 {shape} on {self.device}, got {lse.dtype} "
+                             f"{tuple(lse.shape)} on {lse.device}")
+        return lse.data_ptr()
+
     def estimate_vs(self, q, k):
         self.alloc_workspace()
-        _check(lib().mmsa_estimate_vs(ctypes.byref(self.desc), q.data_ptr(), k.data_ptr(), self._ws_ptr(),
+        _check(lib().mmsa_estimate_vs(ctypes.byref(self.desc), self._q(q), self._k(k), self._ws_ptr(),
                                       self.workspace_bytes(), self._stream()))
 
     def estimate_blocks(self, q, k):
         self.alloc_workspace()
-        _check(lib().mmsa_estimate_blocks(ctypes.byref(self.desc), q.data_ptr(), k.data_ptr(), self._ws_ptr(),
+        _check(lib().mmsa_estimate_blocks(ctypes.byref(self.desc), self._q(q), self._k(k), self._ws_ptr(),
                                           self.workspace_bytes(), self._stream()))
 
     def permute(self, q, k, v):
         self.alloc_workspace()
-        _check(lib().mmsa_permute(ctypes.byref(self.desc), q.data_ptr(), k.data_ptr(), v.data_ptr(),
+        _check(lib().mmsa_permute(ctypes.byref(self.desc), self._q(q), self._k(k), self._v(v),
                                   self._ws_ptr(), self.workspace_bytes(), self._stream()))
 
     def sparse_prefill(self, q, k, v, o, lse=None):
-        _check(lib().mmsa_sparse_prefill(ctypes.byref(self.desc), q.data_ptr(), k.data_ptr(), v.data_ptr(),
-                                         self._ws_ptr(), self.workspace_bytes(), o.data_ptr(),
-                                         None if lse is None else lse.data_ptr(), self._stream()))
+        _check(lib().mmsa_sparse_prefill(ctypes.byref(self.desc), self._q(q), self._k(k), self._v(v),
+                                         self._ws_ptr(), self.workspace_bytes(), self._o(o), self._lse(lse),
+                                         self._stream()))
 
     def unpermute(self, o):
-        _check(lib().mmsa_unpermute(ctypes.byref(self.desc), self._ws_ptr(), self.workspace_bytes(), o.data_ptr(),
+        _check(lib().mmsa_unpermute(ctypes.byref(self.desc), self._ws_ptr(), self.workspace_bytes(), self._o(o),
                                     self._stream()))
 
     def forward_noalloc(self, q, k, v, o, lse=None):
         """The whole path through mmsa_prefill_noalloc (the library's static
         scratch instead of this layer's workspace, which is left untouched)."""
-        _check(lib().mmsa_prefill_noalloc(ctypes.byref(self.desc), q.data_ptr(), k.data_ptr(), v.data_ptr(),
-                                          o.data_ptr(), None if lse is None else lse.data_ptr(), self._stream()))
+        _check(lib().mmsa_prefill_noalloc(ctypes.byref(self.desc), self._q(q), self._k(k), self._v(v),
+                                          self._o(o), self._lse(lse), self._stream()))
         return o
 
     def forward(self, q, k, v, o=None, lse=None):

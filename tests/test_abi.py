@@ -384,3 +384,25 @@ def test_layout_cache_follows_the_descriptor_contents(L):
     assert status_of(lay3) == OK
     good[1] = 7                                       # in-place change of the map
     assert ws_status(lay3) == INVALID
+
+
+def test_binding_rejects_tensors_that_differ_from_the_descriptor():
+    # The binding hands raw pointers to the library, which reads them through
+    # the descriptor's shape and strides: a tensor of another dtype, shape or
+    # layout is refused in Python before any call.  (CPU tensors: the checks
+    # come first, so nothing reaches the library.)
+    import torch
+    B, Hq, Hkv, Lq, d = 1, 2, 1, 100, 64
+    q = torch.zeros(B, Hq, Lq, d, dtype=torch.bfloat16)
+    k = torch.zeros(B, Hkv, Lq, d, dtype=torch.bfloat16)
+    lay = mmsa.Layer(q, k, k, [synth.vs(1, 2)] * Hq)
+    with pytest.raises(ValueError, match="q: expected bf16"):
+        lay.estimate_vs(q.float(), k)
+    with pytest.raises(ValueError, match="k: expected bf16"):
+        lay.estimate_vs(q, k[:, :, :50])
+    with pytest.raises(ValueError, match="strides"):
+        lay.estimate_vs(q.transpose(1, 2).contiguous().transpose(1, 2), k)
+    o = torch.zeros(B, Hq, Lq, d, dtype=torch.bfloat16)
+    with pytest.raises(ValueError, match="lse: expected contiguous float32"):
+        lay._lse(torch.zeros(B, Hq, Lq, dtype=torch.float64))
+    assert lay._o(o) == o.data_ptr() and lay._lse(None) is None
