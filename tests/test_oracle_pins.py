@@ -5,6 +5,7 @@ brute-force recomputation by a different route, a closed form, an invariant of
 the mathematics, or a special case that reduces to plain causal attention.
 """
 import math
+import os
 
 import numpy as np
 import pytest
@@ -826,3 +827,36 @@ def test_permuted_equals_direct_grid_window(sink, window):
     segs = [(0, 49 * 4, 1), (196, 30, 0), (226, 49 * 5, 1), (471, 20, 0)]
     _check_perm(synth.grid(2, 16, 100, layout='modality_grouped', sink=sink, window=window), 491, 16, segs,
                 seed=3, period=49)
+
+
+# ---------------------------------------------------------------------------
+# Golden pair counts (tests/golden/pair_counts.txt, written from closed forms
+# by tests/golden/make_pair_counts.py, which uses neither the oracle nor the GPU)
+# ---------------------------------------------------------------------------
+def _golden_pair_counts():
+    path = os.path.join(os.path.dirname(os.path.abspath(__file__)), "golden", "pair_counts.txt")
+    rows = []
+    with open(path) as f:
+        for line in f:
+            if line.strip() and not line.startswith("#"):
+                kind, *nums = line.split()
+                rows.append((kind, *[int(x) for x in nums]))
+    return rows
+
+
+@pytest.mark.parametrize("row", [r for r in _golden_pair_counts() if r[1] <= 8192], ids=str)
+def test_golden_pair_counts(row):
+    kind, L, s, w, n, q, pairs = row
+    if kind == "ashape":
+        hi = O.HeadIndex(cfg=O.HeadCfg.of(synth.ashape(s, w)), L=L, segs=[(0, L, 0)])
+    else:
+        assert L == s + n * w + q
+        hi = _parallel_head(L, synth.parallel(s, w, q))
+    assert O.pair_count(hi) == pairs
+
+
+def test_golden_pair_counts_cover_the_128k_layer():
+    # the 128K layer's A-shape heads: too long for the oracle's row loop here,
+    # so the fixture's value is checked against the row-by-row sum of the rule
+    (row,) = [r for r in _golden_pair_counts() if r[0] == "ashape" and r[1] == 131072]
+    assert row[-1] == ashape_pairs_closed_form(131072, row[2], row[3])
