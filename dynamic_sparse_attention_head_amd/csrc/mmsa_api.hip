@@ -1075,8 +1075,24 @@ mmsa_status check_device(int* n_cu_out = nullptr, void** scratch_out = nullptr) 
   return MMSA_OK;
 }
 
+// The descriptor tables go up with every call.  A copy enqueued while the
+// stream is being captured into a graph reads its host source again at each
+// replay, and the layout cache may by then have evicted and freed the
+// layout's own tables: under capture the copy reads from a private copy of
+// them that is kept until the process ends (a few KB per captured call).
 mmsa_status upload(const Layout& Lo, void* ws, hipStream_t s) {
-  return hip_status(hipMemcpyAsync(ws, Lo.blob.data(), Lo.blob.size(), hipMemcpyHostToDevice, s), "table upload");
+  const void* src = Lo.blob.data();
+  hipStreamCaptureStatus cs = hipStreamCaptureStatusNone;
+  const mmsa_status st = hip_status(hipStreamIsCapturing(s, &cs), "capture status");
+  if (st != MMSA_OK) return st;
+  if (cs == hipStreamCaptureStatusActive) {
+    static std::mutex mu;
+    static std::vector<std::unique_ptr<const std::vector<char>>> kept;
+    std::lock_guard<std::mutex> lock(mu);
+    kept.push_back(std::make_unique<const std::vector<char>>(Lo.blob));
+    src = kept.back()->data();
+  }
+  return hip_status(hipMemcpyAsync(ws, src, Lo.blob.size(), hipMemcpyHostToDevice, s), "table upload");
 }
 
 #define MMSA_TRY(expr)                       \

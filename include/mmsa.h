@@ -28,6 +28,11 @@
  *    one layer build them once; a changed descriptor or array is a new key.
  *  - Asynchrony: every call enqueues work on `stream` (a hipStream_t; NULL is
  *    the null stream) and returns without waiting for the device.
+ *  - Graph capture: the calls, and mmsa_prefill_noalloc, may be captured into
+ *    a HIP graph.  Each call uploads its tables (a few KB) from host memory;
+ *    under capture it uploads them from a private copy kept until the process
+ *    ends, so replays stay valid after the cache above has dropped the layout.
+ *    No call records a memset.
  *  - Tensors: bf16, element strides (batch, head, row) with the last (head
  *    dimension) contiguous; base pointers 16-byte aligned; row strides a
  *    multiple of 8 elements.  d is 64 or 128.

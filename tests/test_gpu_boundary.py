@@ -157,3 +157,51 @@ def test_layers_interleaved_on_one_stream_keep_their_own_tables():
     for i in range(3):
         assert torch.equal(outs[i].view(torch.int16), want[i].view(torch.int16)), f"layer {i}"
     assert not torch.equal(outs[2].view(torch.int16), outs[0].view(torch.int16))   # the budget matters
+
+
+def test_graph_capture_replays_match_eager():
+    # The five calls, and the allocation-free call, captured into graphs.
+    # Every replay gives the eager output bit for bit, with other layers run
+    # eagerly in between (the allocation-free one through the same static
+    # scratch) and the host layout cache cycled past its 16 entries, which
+    # frees the captured layer's own copy of its tables.
+    spec = mixed_spec()
+    lay = synth.make_layer(spec, "cuda")
+    q, k, v = lay["q"], lay["k"], lay["v"]
+    L = mmsa.Layer(q, k, v, spec.heads, segs=spec.segs)
+    shape = (1, spec.Hq, spec.L, spec.d)
+    o_e = torch.zeros(shape, dtype=torch.bfloat16, device="cuda")
+    l_e = torch.zeros(shape[:3], dtype=torch.float32, device="cuda")
+    L.forward(q, k, v, o_e, l_e)
+    torch.cuda.synchronize()
+    outs = {}
+    graphs = {}
+    for name in ("five", "noalloc"):
+        o = torch.zeros_like(o_e)
+        lse = torch.zeros_like(l_e)
+        g = torch.cuda.CUDAGraph()
+        with torch.cuda.graph(g):
+            if name == "five":
+                L.forward(q, k, v, o, lse)
+            else:
+                L.forward_noalloc(q, k, v, o, lse)
+        outs[name], graphs[name] = (o, lse), g
+    spec2 = synth.config(2, L=8192)
+    lay2 = synth.make_layer(spec2, "cuda")
+    L2 = mmsa.Layer(lay2["q"], lay2["k"], lay2["v"], spec2.heads)
+    o2 = torch.zeros((1, spec2.Hq, spec2.L, spec2.d), dtype=torch.bfloat16, device="cuda")
+    for r in range(3):
+        for name in ("five", "noalloc"):
+            o, lse = outs[name]
+            o.zero_()
+            lse.zero_()
+            graphs[name].replay()
+            torch.cuda.synchronize()
+            assert torch.equal(o.view(torch.int16), o_e.view(torch.int16)), f"{name} replay {r}: output"
+            assert torch.equal(lse, l_e), f"{name} replay {r}: lse"
+        L2.forward_noalloc(lay2["q"], lay2["k"], lay2["v"], o2)
+        L2.forward(lay2["q"], lay2["k"], lay2["v"], o2)
+        for i in range(20):   # 20 other layouts through the host-only size query
+            mmsa.Layer(None, None, None, [synth.vs(1 + i + 20 * r, 2)], shape=(1, 1, 1, 4096, 64),
+                       device="cuda").workspace_bytes()
+        torch.cuda.synchronize()
