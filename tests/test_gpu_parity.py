@@ -10,7 +10,7 @@ import numpy as np
 import pytest
 import torch
 
-from dynamic_sparse_attention_head_amd import synth
+from dynamic_sparse_attention_head_amd import mmsa, synth
 from parity_util import full_check, run_gpu
 
 pytestmark = pytest.mark.gpu
@@ -319,3 +319,33 @@ def test_strided_inputs_and_batch():
             hi = check_head_indices(Lh, b * 4 + h, spec.heads[h], qn, kn, None, 1 / np.sqrt(128))
             check_attention(hi, qn, kn, vn, f64(o[b, h]), None, 1 / np.sqrt(128), np.arange(300),
                             name=f"b{b} h{h}")
+
+
+def test_batch_of_two_with_segments_and_every_layout():
+    # B = 2 with modality segments: two independent layers (different seeds)
+    # in one call, every pattern and layout, each batch element with its own
+    # estimates, plans, LSE and exact per-tile pair counts
+    from dataclasses import replace
+    from parity_util import check_attention, check_head_indices, check_tile_pairs, f64
+    import oracle.mmsa_oracle as O
+    segs = [(0, 200, TEXT), (200, 49 * 10, VIDEO), (690, 60, TEXT), (750, 49 * 8, VIDEO)]
+    heads = [synth.vs(20, 40, "q_boundary"), synth.vs(15, 50, "boundary_2d"), synth.vs(10, 30, "q_segment"),
+             synth.grid(1, 16, 64, layout="modality_grouped"), synth.grid(1, 16, 64, sink=20, window=100),
+             synth.block(4), synth.parallel(100, 98, 50), synth.ashape(16, 128)]
+    spec = synth.small_spec("batch-segs", 1142, 8, 2, 128, heads, seed=47, segs=segs, period=49, period_amp=3.0)
+    lays = [synth.make_layer(spec, "cuda"), synth.make_layer(replace(spec, seed=48), "cuda")]
+    q, k, v = (torch.cat([lay[n] for lay in lays]).contiguous() for n in ("q", "k", "v"))
+    Lh = mmsa.Layer(q, k, v, spec.heads, segs=spec.segs)
+    o = torch.full((2, spec.Hq, spec.L, spec.d), float("nan"), dtype=torch.bfloat16, device="cuda")
+    lse = torch.full((2, spec.Hq, spec.L), float("nan"), dtype=torch.float32, device="cuda")
+    Lh.forward(q, k, v, o, lse)
+    torch.cuda.synchronize()
+    gmap = O.kv_head_map(spec.Hq, spec.Hkv)
+    scale = 1 / np.sqrt(spec.d)
+    for b in range(2):
+        for h in range(spec.Hq):
+            qn, kn, vn = f64(q[b, h]), f64(k[b, gmap[h]]), f64(v[b, gmap[h]])
+            hi = check_head_indices(Lh, b * spec.Hq + h, spec.heads[h], qn, kn, spec.segs, scale)
+            check_attention(hi, qn, kn, vn, f64(o[b, h]), lse[b, h].cpu().numpy().astype(np.float64), scale,
+                            np.arange(spec.L), name=f"b{b} h{h}")
+            check_tile_pairs(Lh, b * spec.Hq + h, hi)
