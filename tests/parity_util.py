@@ -24,11 +24,13 @@ def f64(t):
     return t.detach().float().cpu().numpy().astype(np.float64)
 
 
-def run_gpu(spec, device="cuda", q=None, k=None, v=None, lse=True, materialize=False, flags=0, kv_head_of=None):
+def run_gpu(spec, device="cuda", q=None, k=None, v=None, lse=True, materialize=False, flags=0, kv_head_of=None,
+            scale=None):
     if q is None:
         lay = synth.make_layer(spec, device)
         q, k, v = lay["q"], lay["k"], lay["v"]
-    L = mmsa.Layer(q, k, v, spec.heads, segs=spec.segs, materialize=materialize, flags=flags, kv_head_of=kv_head_of)
+    L = mmsa.Layer(q, k, v, spec.heads, segs=spec.segs, materialize=materialize, flags=flags, kv_head_of=kv_head_of,
+                   scale=scale)
     o = torch.full((spec_B(q), spec.Hq, spec.L, spec.d), float("nan"), dtype=torch.bfloat16, device=device)
     lse_t = torch.full((spec_B(q), spec.Hq, spec.L), float("nan"), dtype=torch.float32, device=device) if lse else None
     L.forward(q, k, v, o, lse_t)
@@ -178,14 +180,14 @@ def sample_rows(Lq, n_uniform, seed, extra=()):
 
 
 def full_check(spec, rows_per_head=None, pair_tiles=None, seed=0, lse=True, materialize=False, flags=0,
-               q=None, k=None, v=None, kv_head_of=None):
+               q=None, k=None, v=None, kv_head_of=None, scale=None):
     L, q, k, v, o, lse_t = run_gpu(spec, lse=lse, materialize=materialize, flags=flags, q=q, k=k, v=v,
-                                   kv_head_of=kv_head_of)
+                                   kv_head_of=kv_head_of, scale=scale)
     qn, kn, vn = f64(q[0]), f64(k[0]), f64(v[0])
     on = f64(o[0])
     ln = lse_t[0].cpu().numpy().astype(np.float64) if lse_t is not None else None
     gmap = O.kv_head_map(spec.Hq, spec.Hkv, kv_head_of)
-    scale = 1.0 / math.sqrt(spec.d)
+    scale = 1.0 / math.sqrt(spec.d) if scale is None else float(scale)
     for h in range(spec.Hq):
         hi = check_head_indices(L, h, spec.heads[h], qn[h], kn[gmap[h]], spec.segs, scale)
         rows = np.arange(spec.L) if rows_per_head is None else sample_rows(spec.L, rows_per_head, seed + h)

@@ -195,6 +195,18 @@ def test_uneven_kv_head_map():
     full_check(spec, kv_head_of=[2, 0, 2, 1, 0, 2])
 
 
+@pytest.mark.parametrize("scale", [0.03, 0.25])
+def test_custom_softmax_scale(scale):
+    # a scale given in the descriptor (flatter and sharper than 1/sqrt(d)):
+    # estimation scores, index sets, attention and LSE all use it
+    segs = [(0, 150, TEXT), (150, 49 * 12, VIDEO), (738, 90, TEXT)]
+    heads = [synth.vs(20, 40), synth.vs(15, 30, "q_boundary"), synth.block(5),
+             synth.grid(1, 16, 64, layout="modality_grouped"), synth.ashape(16, 100), synth.vs(10, 20, "boundary_2d")]
+    spec = synth.small_spec("scale", 828, 6, 2, 128, heads, seed=49, segs=segs, period=49, period_amp=3.0,
+                            rope_base=1e4, strong_cols=16)
+    full_check(spec, scale=scale)
+
+
 def test_parallel_encoding_ragged():
     # sink, context and question blocks off the 64-token tiles, a partial last
     # context block, a head with no sink or question, and 5-token blocks
