@@ -207,6 +207,22 @@ def test_custom_softmax_scale(scale):
     full_check(spec, scale=scale)
 
 
+def test_saturated_budgets_select_every_causal_pair():
+    # budgets at or above the candidate counts (clamped, not errors): vertical
+    # and slash sets of L on every layout, more blocks than there are, a grid
+    # of stride 16 with all 16 phases (every key a line key) and a window of L.
+    # Every head then keeps every causal pair and equals dense attention.
+    L = 1500
+    segs = [(0, 300, TEXT), (300, 49 * 20, VIDEO), (1280, 220, TEXT)]
+    heads = [synth.vs(L, L), synth.vs(L, L, "q_boundary"), synth.vs(L, L, "boundary_2d"), synth.vs(L, L, "q_segment"),
+             synth.block(L // 64 + 5), synth.grid(16, 16, 16), synth.grid(16, 16, 16, layout="modality_grouped"),
+             synth.ashape(0, L)]
+    spec = synth.small_spec("saturated", L, 8, 2, 64, heads, seed=53, segs=segs, period=49, period_amp=3.0)
+    lay = full_check(spec, rows_per_head=300)
+    for h in range(spec.Hq):
+        assert int(lay.view("tile_pairs", h).sum().item()) == L * (L + 1) // 2, f"head {h}"
+
+
 def test_parallel_encoding_ragged():
     # sink, context and question blocks off the 64-token tiles, a partial last
     # context block, a head with no sink or question, and 5-token blocks
