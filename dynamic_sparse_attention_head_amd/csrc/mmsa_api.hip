@@ -352,6 +352,18 @@ mmsa_status build_layout(const mmsa_layer_desc* desc, Layout& Lo) {
     return MMSA_OK;
   }
 
+  // Work items pack a head and a pair of query tiles into 32 bits, the pair in
+  // the low 16.  Per-segment heads pad every segment to 64 rows, so many short
+  // segments can give such a head more pairs than that: refused here.
+  for (int h = 0; h < D.Hq; ++h) {
+    const mmsa_head_cfg& c = Lo.cfg[h];
+    const int64_t tiles = dm.L_seg / TILE;
+    if (c.pattern == MMSA_VS && c.layout == MMSA_Q_SEGMENT && (tiles + 1) / 2 > 0xffff) {
+      set_err("head %d: its segments, each padded to 64 rows, make %lld query tiles; a head may have at most 131070",
+              h, (long long)tiles);
+      return MMSA_UNSUPPORTED;
+    }
+  }
   const int L = D.L, nT = Lo.nT;
   Lo.nB = nT;
   Lo.set_of.assign(Lo.BH, std::vector<std::pair<int, int>>(std::max<size_t>(4, Lo.segs.size()), {-1, -1}));

@@ -46,7 +46,9 @@
  *    architecture of the current HIP device and returns MMSA_UNSUPPORTED, with
  *    nothing enqueued, on any other device or when there is none.
  *  - Limits: L < 2^22 tokens (tile indices are packed in 16 bits), B*Hq <= 4096;
- *    BLOCK heads need L <= 2^20 (one pooled-logit row per query block in LDS).
+ *    BLOCK heads need L <= 2^20 (one pooled-logit row per query block in LDS);
+ *    a Q_SEGMENT head needs its segments, each padded to a multiple of 64
+ *    rows, to fit in 131070 query tiles (else MMSA_UNSUPPORTED).
  */
 #ifndef MMSA_H
 #define MMSA_H

@@ -406,3 +406,16 @@ def test_binding_rejects_tensors_that_differ_from_the_descriptor():
     with pytest.raises(ValueError, match="lse: expected contiguous float32"):
         lay._lse(torch.zeros(B, Hq, Lq, dtype=torch.float64))
     assert lay._o(o) == o.data_ptr() and lay._lse(None) is None
+
+
+def test_per_segment_head_with_too_many_padded_tiles_is_refused(L):
+    # 131071 one-token segments: a per-segment head pads each to 64 rows and
+    # would need 131071 query tiles, one more than a work item can address
+    n = 131071
+    segs = [(i, 1, i % 2) for i in range(n)]
+    lay = host_layer([synth.vs(1, 2, "q_segment")], Lq=n, segs=segs)
+    assert ws_status(lay) == UNSUPPORTED and "131070" in last_error()
+    lay = host_layer([synth.vs(1, 2, "q_segment")], Lq=n - 1, segs=segs[:-1])
+    assert ws_status(lay) == OK
+    lay = host_layer([synth.vs(1, 2, "q_boundary")], Lq=n, segs=segs)   # no per-segment padding of rows
+    assert ws_status(lay) == OK
