@@ -229,3 +229,21 @@ def test_mixed_1m_segments():
     # edge (run_config adds them) of the per-segment heads; the other heads
     # are those of the 1M layer checked above
     run_config(7, n_uniform=6, n_tiles=1, layouts=("q_segment",), index_heads="representative", n_edge=8)
+
+
+@pytest.mark.timeout(600)
+def test_maximum_length():
+    # the longest layer the library accepts (L = 2^22 - 1 tokens; tile and
+    # pair indices then fill their 16-bit fields), with text / video / text
+    # segments: an A-shape head, a plain vertical-slash head and a
+    # 2D-boundary head (key view grouped by modality)
+    from parity_util import full_check
+    TEXT, VIDEO = 0, 1
+    L = (1 << 22) - 1
+    segs = [(0, 100000, TEXT), (100000, 3000000, VIDEO), (3100000, L - 3100000, TEXT)]
+    heads = [synth.ashape(128, 8192), synth.vs(200, 400), synth.vs(100, 200, "boundary_2d")]
+    spec = synth.small_spec("max-L", L, 3, 1, 64, heads, seed=59, segs=segs, period=49, period_amp=3.0)
+    nT = -(-L // 64)
+    t0 = time.time()
+    full_check(spec, rows_per_head=16, pair_tiles=[0, 1, nT // 2, nT - 2, nT - 1])
+    say(f"max-L: L={L} checked in {time.time() - t0:.1f} s")
