@@ -223,6 +223,34 @@ def test_saturated_budgets_select_every_causal_pair():
         assert int(lay.view("tile_pairs", h).sum().item()) == L * (L + 1) // 2, f"head {h}"
 
 
+def test_maximum_head_count():
+    # B*Hq at its limit (4096 q heads over 512 KV heads) on a short ragged
+    # layer, every pattern and layout in turn: host tables, launch grids and the
+    # head field of the work items at their largest
+    kinds = [synth.vs(5, 9), synth.vs(4, 8, "q_boundary"), synth.vs(3, 7, "boundary_2d"),
+             synth.vs(4, 6, "q_segment"), synth.block(2), synth.grid(1, 16, 32),
+             synth.grid(1, 16, 32, layout="modality_grouped"), synth.ashape(8, 40), synth.parallel(10, 30, 20)]
+    heads = [kinds[h % len(kinds)] for h in range(4096)]
+    segs = [(0, 70, TEXT), (70, 98, VIDEO), (168, 29, TEXT)]
+    spec = synth.small_spec("max-heads", 197, 4096, 512, 64, heads, seed=61, segs=segs, period=49, period_amp=3.0)
+    from parity_util import check_attention, check_head_indices, check_tile_pairs, f64
+    import oracle.mmsa_oracle as O
+    L, q, k, v, o, lse = run_gpu(spec)
+    assert torch.isfinite(o.float()).all().item()
+    causal = spec.L * (spec.L + 1) // 2   # every head's plan: selected pairs bounded by the causal count
+    for h in range(spec.Hq):
+        assert 0 <= int(L.view("tile_pairs", h).sum().item()) <= causal
+    gmap = O.kv_head_map(spec.Hq, spec.Hkv)
+    scale = 1 / np.sqrt(spec.d)
+    rows = np.arange(0, spec.L, 7)
+    for h in list(range(9)) + list(range(spec.Hq - 9, spec.Hq)):   # every kind, and the largest head indices
+        qn, kn, vn = f64(q[0, h]), f64(k[0, gmap[h]]), f64(v[0, gmap[h]])
+        hi = check_head_indices(L, h, spec.heads[h], qn, kn, spec.segs, scale)
+        check_attention(hi, qn, kn, vn, f64(o[0, h]), lse[0, h].cpu().numpy().astype(np.float64), scale, rows,
+                        name=f"head {h}")
+        check_tile_pairs(L, h, hi)
+
+
 def test_parallel_encoding_ragged():
     # sink, context and question blocks off the 64-token tiles, a partial last
     # context block, a head with no sink or question, and 5-token blocks
