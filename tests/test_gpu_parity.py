@@ -251,6 +251,18 @@ def test_maximum_head_count():
         check_tile_pairs(L, h, hi)
 
 
+def test_grid_at_its_parameter_limits():
+    # strides up to the largest searched (1024), all 16 phases, the widest and
+    # the narrowest clip, plain and modality-grouped, with a sink and window
+    segs = [(0, 1000, TEXT), (1000, 700 * 26, VIDEO), (19200, 800, TEXT)]
+    heads = [synth.grid(16, 512, 1024, clip=64), synth.grid(16, 512, 1024, clip=64, layout="modality_grouped"),
+             synth.grid(4, 1000, 1024, clip=1, layout="modality_grouped"),
+             synth.grid(16, 16, 1024, clip=64, sink=64, window=700)]
+    spec = synth.small_spec("grid-limits", 20000, 4, 1, 128, heads, seed=67, segs=segs, period=700, period_amp=3.0)
+    rng = np.random.default_rng(67)
+    full_check(spec, rows_per_head=200, pair_tiles=sorted({0, 312} | set(int(t) for t in rng.integers(0, 313, 40))))
+
+
 def test_parallel_encoding_ragged():
     # sink, context and question blocks off the 64-token tiles, a partial last
     # context block, a head with no sink or question, and 5-token blocks
