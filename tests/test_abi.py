@@ -9,6 +9,8 @@ import ctypes
 import os
 import re
 
+import numpy as np
+
 import pytest
 import torch
 
@@ -419,3 +421,93 @@ def test_per_segment_head_with_too_many_padded_tiles_is_refused(L):
     assert ws_status(lay) == OK
     lay = host_layer([synth.vs(1, 2, "q_boundary")], Lq=n, segs=segs)   # no per-segment padding of rows
     assert ws_status(lay) == OK
+
+
+def _fuzz_desc(rng):
+    """A random descriptor: mostly plausible, often invalid in one or more
+    fields (shape, strides, flags, segments, head patterns and budgets, GQA
+    map).  Returns the host layer object keeping its arrays alive."""
+    B = int(rng.choice([0, 1, 1, 1, 2, 3]))
+    Hkv = int(rng.choice([0, 1, 1, 2, 2, 3]))
+    Hq = Hkv * int(rng.integers(0, 4)) if rng.random() < 0.85 else int(rng.integers(0, 7))
+    L = int(rng.choice([0, 1, 63, 64, 65, int(rng.integers(2, 5000)), int(rng.integers(2, 5000)), (1 << 22) - 1,
+                        1 << 22, -1]))
+    d = int(rng.choice([64, 128, 64, 128, 64, 128, 64, 128, 96, 32]))
+    pats = list(mmsa.PATTERNS)
+    lays = list(mmsa.LAYOUTS)
+    heads = []
+    valid = [lambda: synth.vs(int(rng.integers(0, 400)), int(rng.integers(0, 900)),
+                              str(rng.choice(["plain", "q_boundary", "boundary_2d", "q_segment"]))),
+             lambda: synth.ashape(int(rng.integers(0, 200)), int(rng.integers(1, 3000))),
+             lambda: synth.block(int(rng.integers(0, 80))),
+             lambda: synth.grid(int(rng.integers(1, 17)), int(rng.integers(16, 600)), int(rng.integers(600, 1025)),
+                                layout=str(rng.choice(["plain", "modality_grouped"])),
+                                sink=int(rng.integers(0, 100)), window=int(rng.integers(0, 800))),
+             lambda: synth.parallel(int(rng.integers(0, 300)), int(rng.integers(1, 500)), int(rng.integers(0, 300)))]
+    for _ in range(max(Hq, 0)):
+        if rng.random() < 0.7:
+            heads.append(valid[int(rng.integers(0, len(valid)))]())
+            continue
+        h = {"pattern": str(rng.choice(pats)), "layout": str(rng.choice(lays))}
+        for key, lo, hi in (("sink", -2, 300), ("window", -2, 3000), ("k_vertical", -2, 3000), ("k_slash", -2, 3000),
+                            ("k_blocks", -2, 100), ("grid_phases", 0, 18), ("stride_lo", 0, 1100),
+                            ("stride_hi", 0, 1100), ("grid_clip", 0, 70), ("question", -2, 500)):
+            if rng.random() < 0.7:
+                h[key] = int(rng.integers(lo, hi))
+        heads.append(h)
+    segs = None
+    if rng.random() < 0.6 and L > 0:
+        n = int(rng.integers(1, 9))
+        cuts = sorted(set(int(x) for x in rng.integers(0, L + 1, n - 1))) if n > 1 else []
+        bounds = [0, *cuts, L]
+        segs = [(bounds[i], bounds[i + 1] - bounds[i], int(rng.integers(0, 2))) for i in range(len(bounds) - 1)]
+        if rng.random() < 0.15:     # break the tiling: a gap, an overlap, a bad modality or a segment past L
+            i = int(rng.integers(0, len(segs)))
+            s, ln, m = segs[i]
+            segs[i] = [(s + 1, ln, m), (s, ln + 1, m), (s, ln, 2), (s, ln + 5, m), (s, -1, m)][int(rng.integers(0, 5))]
+    lay = mmsa.Layer(None, None, None, heads, segs=segs, shape=(B, Hq, max(Hkv, 0), max(L, 0), d), device="cpu")
+    D = lay.desc
+    D.B, D.Hkv, D.L, D.d = B, Hkv, L, d
+    if rng.random() < 0.15:
+        D.flags = int(rng.integers(0, 64))
+    if rng.random() < 0.15:
+        t = [D.q_strides, D.k_strides, D.v_strides, D.o_strides][int(rng.integers(0, 4))]
+        t[int(rng.integers(0, 3))] = int(rng.choice([-8, 0, 7, 8, d - 8, 1 << 21]))
+    if rng.random() < 0.1:
+        D.scale = float(rng.choice([-1.0, float("inf"), 0.0, 0.1]))
+    if rng.random() < 0.2 and Hq > 0:
+        lay._kvmap = (ctypes.c_int32 * Hq)(*[int(x) for x in rng.integers(-1, max(Hkv, 1) + 1, Hq)])
+        D.kv_head_of = lay._kvmap
+    for i in range(Hq):
+        if rng.random() < 0.05:
+            D.heads[i].pattern = int(rng.choice([-1, 5, 9]))
+        if rng.random() < 0.05:
+            D.heads[i].layout = int(rng.choice([-1, 5, 9]))
+    return lay
+
+
+def test_random_descriptors_are_accepted_or_refused_cleanly(L):
+    # 300 seeded descriptors through the host-only calls: each is accepted with
+    # a positive workspace size and viewable buffers, or refused with a status
+    # and a message; nothing crashes (and, under the host-ASan rerun of this
+    # file, nothing reads or writes out of bounds)
+    rng = np.random.default_rng(2024)
+    accepted = 0
+    for _ in range(300):
+        lay = _fuzz_desc(rng)
+        n = L.mmsa_workspace_bytes(ctypes.byref(lay.desc))
+        st = ws_status(lay)
+        if n == 0:
+            assert st != OK and last_error()
+            continue
+        assert st == OK
+        accepted += 1
+        off, cnt = ctypes.c_int64(), ctypes.c_int64()
+        for bh in range(lay.desc.B * lay.desc.Hq):
+            for name, buf in mmsa.BUF.items():
+                s2 = L.mmsa_workspace_view(ctypes.byref(lay.desc), buf, bh, 0, ctypes.byref(off), ctypes.byref(cnt))
+                assert s2 in (OK, INVALID)
+                if s2 == OK and cnt.value > 0:   # every view lies inside the workspace
+                    size = cnt.value * torch.tensor([], dtype=mmsa.BUF_DTYPE[name]).element_size()
+                    assert 0 <= off.value and off.value + size <= n, (name, off.value, size, n)
+    assert accepted >= 60, accepted
