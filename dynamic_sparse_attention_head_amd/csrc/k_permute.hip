@@ -240,7 +240,9 @@ __global__ __launch_bounds__(256) void k_vs_shift(Tables tb, char* ws) {
   }
 }
 
-__global__ __launch_bounds__(256) void k_plan(Dims dm, Tables tb, char* ws) {
+template <int NT>
+__global__ __launch_bounds__(NT) void k_plan(Dims dm, Tables tb, char* ws) {
+  constexpr int NW = NT / 64;   // waves
   const int bh = blockIdx.y, t = blockIdx.x;
   const HeadDev& H = wsp<const HeadDev>(ws, tb.off_heads)[bh];
   if (t >= H.nT_rows) return;
@@ -253,7 +255,7 @@ __global__ __launch_bounds__(256) void k_plan(Dims dm, Tables tb, char* ws) {
   const int W = H.bm_words;
   const int32_t* pgrp = wsp<const int32_t>(ws, dm.ws_pgrp);
 
-  for (int w = tid; w < W; w += 256) bm[w] = 0ull;
+  for (int w = tid; w < W; w += NT) bm[w] = 0ull;
   int pos = -1;
   if (tid < 64) {
     const int slot = 64 * t + tid;
@@ -284,7 +286,7 @@ __global__ __launch_bounds__(256) void k_plan(Dims dm, Tables tb, char* ws) {
   long long* pairs_out = wsp<long long>(ws, H.ws_pairs) + t;
   uint64_t* bm_out = wsp<uint64_t>(ws, H.ws_bm) + (int64_t)t * W;
   if (nrows == 0) {
-    for (int w = tid; w < W; w += 256) bm_out[w] = 0ull;
+    for (int w = tid; w < W; w += NT) bm_out[w] = 0ull;
     if (tid == 0) {
       *info = make_int4(0, 0, 0, 0);
       *pairs_out = 0;
@@ -319,7 +321,7 @@ __global__ __launch_bounds__(256) void k_plan(Dims dm, Tables tb, char* ws) {
     if (red[3] != 0x7fffffff) bm_set_range(bm, red[3] >> 6, tmax);
   } else if (H.pattern == MMSA_BLOCK) {
     const int32_t* ci = wsp<const int32_t>(ws, H.ws_blk_idx) + (int64_t)t * H.k_blocks;
-    for (int i = tid; i < H.k_blocks; i += 256) {
+    for (int i = tid; i < H.k_blocks; i += NT) {
       const int c = ci[i];
       if (c >= 0) bm_set(bm, c);
     }
@@ -388,7 +390,7 @@ __global__ __launch_bounds__(256) void k_plan(Dims dm, Tables tb, char* ws) {
       const uint64_t* M = wsp<const uint64_t>(ws, shift_off);
       const int SW = J.pair[0].shift_words;
       const int t0 = sh_run_r0[0] >> 6;
-      for (int w = tid; w < W; w += 256) {
+      for (int w = tid; w < W; w += NT) {
         const int base = t0 - 64 * w - 63;   // bit b of word w (key tile 64w + b) <- shift bit t0 - 64w - b
         const int wi = base >> 6, sh = base & 63;
         uint64_t X = (wi >= 0 && wi < SW) ? M[wi] >> sh : 0ull;
@@ -411,7 +413,7 @@ __global__ __launch_bounds__(256) void k_plan(Dims dm, Tables tb, char* ws) {
         const int tb0 = (Pd.m_k == MMSA_VIDEO ? dm.video_base : dm.text_base) >> 6;
         const int ntk = (Pd.n_k + 63) >> 6;
         const int T = tr + ((Pd.n_k - 1 + 63) >> 6) + tb0;   // shift bit of view tile v: T - v
-        for (int w = tid; w < W; w += 256) {
+        for (int w = tid; w < W; w += NT) {
           const int lo = max(tb0, 64 * w), hi = min(tb0 + ntk, 64 * w + 64);
           if (lo >= hi) continue;
           const int base = T - 64 * w - 63;
@@ -433,7 +435,7 @@ __global__ __launch_bounds__(256) void k_plan(Dims dm, Tables tb, char* ws) {
         const int32_t* S = wsp<const int32_t>(ws, Pd.ws_sidx);
         const int r_lo = Pd.n_k & ~63, r_hi = Pd.n_k - 1, a = sh_run_r0[0];
         int hit = 0;
-        for (int e = tid; e < ns; e += 256) {
+        for (int e = tid; e < ns; e += NT) {
           const int o = S[e] - (Pd.n_k - 1);
           hit |= (a - o <= r_hi) && (a + 63 - o >= r_lo);
         }
@@ -452,7 +454,7 @@ __global__ __launch_bounds__(256) void k_plan(Dims dm, Tables tb, char* ws) {
       const int ns = min(max(nsel[1], 0), Pd.ks);
       const int32_t* S = wsp<const int32_t>(ws, Pd.ws_sidx);
       const int tile_base = twod ? ((Pd.m_k == MMSA_VIDEO ? dm.video_base : dm.text_base) >> 6) : 0;
-      for (int e = tid; e < ns; e += 256) {
+      for (int e = tid; e < ns; e += NT) {
         const int o = twod ? S[e] - (Pd.n_k - 1) : max(S[e], 0);
         for (int ru = 0; ru < nruns; ++ru) {
           const int a = sh_run_r0[ru], len = sh_run_len[ru];
@@ -500,7 +502,7 @@ __global__ __launch_bounds__(256) void k_plan(Dims dm, Tables tb, char* ws) {
         if (lo >= hi) return 0ull;
         return (hi == 64 ? ~0ull : ((1ull << hi) - 1)) & ~((1ull << lo) - 1);
       };
-      for (int w = tid; w < W; w += 256) bm[w] &= range_bits(w, tt0, tt1) | range_bits(w, tv0, tv1);
+      for (int w = tid; w < W; w += NT) bm[w] &= range_bits(w, tt0, tt1) | range_bits(w, tv0, tv1);
       __syncthreads();
     }
     // gathered verticals not held by a listed tile, ascending per key modality
@@ -510,7 +512,7 @@ __global__ __launch_bounds__(256) void k_plan(Dims dm, Tables tb, char* ws) {
       const int nv = min(max(wsp<const int32_t>(ws, Pd.ws_nsel)[0], 0), Pd.kv);
       const int32_t* V = wsp<const int32_t>(ws, Pd.ws_vidx);
       const int kbase = twod ? (Pd.m_k == MMSA_VIDEO ? dm.video_base : dm.text_base) : 0;
-      for (int s0 = 0; s0 < nv; s0 += 256) {
+      for (int s0 = 0; s0 < nv; s0 += NT) {
         const int e = s0 + tid;
         bool keep = false;
         int p = -1;
@@ -540,7 +542,7 @@ __global__ __launch_bounds__(256) void k_plan(Dims dm, Tables tb, char* ws) {
   const bool use_pre = W > 16;   // short bitmaps: the walk is cheaper than the scan's barriers
   if (use_pre) {
     int carry = 0;
-    for (int base = 0; base < W; base += 256) {
+    for (int base = 0; base < W; base += NT) {
       const int w = base + tid;
       const int c = w < W ? __popcll(bm[w]) : 0;
       int tot;
@@ -619,7 +621,7 @@ __global__ __launch_bounds__(256) void k_plan(Dims dm, Tables tb, char* ws) {
   for (int m = 1; m < 64; m <<= 1) my_pairs += __shfl_xor(my_pairs, m, 64);
   // tiles in the bitmap
   int nt = 0;
-  for (int w = tid; w < W; w += 256) {
+  for (int w = tid; w < W; w += NT) {
     nt += __popcll(bm[w]);
     bm_out[w] = bm[w];
   }
@@ -630,7 +632,9 @@ __global__ __launch_bounds__(256) void k_plan(Dims dm, Tables tb, char* ws) {
   }
   __syncthreads();
   if (tid == 0) {
-    const int ntiles = red[0] + red[1] + red[2] + red[3];
+    int ntiles = 0;
+#pragma unroll
+    for (int i = 0; i < NW; ++i) ntiles += red[i];
     const int cost = ntiles + (g_cnt + 63) / 64;
     *info = make_int4(ntiles, g_cnt, cost, nrows);
     *pairs_out = pred[0];
@@ -733,7 +737,7 @@ hipError_t launch_plan(const Dims& dm, const Tables& tb, char* ws, int max_tiles
     if (tb.n_jobs > 0 && max_shift_words > 0)
       k_vs_shift<<<(unsigned)tb.n_jobs, 256, (size_t)max_shift_words * 8, s>>>(tb, ws);
     // dynamic LDS: the bitmap words, then their popcount prefix
-    k_plan<<<dim3(max_tiles, (unsigned)tb.n_heads), 256, (size_t)max_bm_words * 12 + 4, s>>>(dm, tb, ws);
+    k_plan<64><<<dim3(max_tiles, (unsigned)tb.n_heads), 64, (size_t)max_bm_words * 12 + 4, s>>>(dm, tb, ws);
     k_queue_enum<<<dim3((max_tiles / 2 + 64) / 64, (unsigned)tb.n_heads), 64, 0, s>>>(dm, tb, ws);
   }
   return hipGetLastError();
