@@ -270,6 +270,36 @@ def test_grid_rule_matches_bruteforce(seed):
     assert got[0] == per and ph in list(got[1])
 
 
+@pytest.mark.parametrize("seed", range(30))
+def test_grid_rule_matches_bruteforce_without_a_planted_period(seed):
+    # unstructured scores over a length that no stride divides evenly: the
+    # winner then turns on small differences, including the classes that
+    # hold one position fewer than the others
+    rng = np.random.default_rng(100 + seed)
+    D = int(rng.integers(150, 400))
+    v = (rng.random(D) * rng.choice([0.01, 0.05, 1.0])).astype(np.float32)
+    lo = int(rng.integers(16, 40))
+    hi = lo + int(rng.integers(0, 60))
+    w = int(rng.integers(1, 4))
+    got = O.grid_rule(v, D, 64, 8, lo, hi, w)
+    ref = zscore_bruteforce(v, D, 64, 8, lo, hi, w)
+    assert got[0] == ref[0] and list(got[1]) == ref[1]
+
+
+def test_grid_rule_exact_phase_tie_goes_to_the_lower_phase():
+    # equal spikes at phases 3 and 11 of period 30 over 600 positions: both
+    # classes have the same sum and size, so their scores tie exactly
+    D = 600
+    v = np.full(D, 0.001, np.float32)
+    v[3::30] = 0.02
+    v[11::30] = 0.02
+    sig, ph = O.grid_rule(v, D, 64, 8, 20, 40, 1)
+    assert sig == 30 and list(ph) == [3]
+    sig, ph = O.grid_rule(v, D, 64, 8, 20, 40, 2)
+    assert sig == 30 and list(ph) == [3, 11]
+    assert zscore_bruteforce(v, D, 64, 8, 20, 40, 1) == (30, [3])
+
+
 def test_grid_rule_prefers_true_period_over_multiples_and_divisors():
     rng = np.random.default_rng(11)
     D = 196 * 60
@@ -860,3 +890,16 @@ def test_golden_pair_counts_cover_the_128k_layer():
     # so the fixture's value is checked against the row-by-row sum of the rule
     (row,) = [r for r in _golden_pair_counts() if r[0] == "ashape" and r[1] == 131072]
     assert row[-1] == ashape_pairs_closed_form(131072, row[2], row[3])
+
+
+def test_pooled_logits_of_constant_blocks_are_scaled_dot_products():
+    # blocks whose 64 rows are equal pool to that row exactly, so each pooled
+    # logit is the scaled dot product of the two rows, summed here by a loop
+    rng = np.random.default_rng(5)
+    nB, d, scale = 5, 8, 0.37
+    qr, kr = rng.standard_normal((nB, d)), rng.standard_normal((nB, d))
+    z = O.block_logits(O.pool_blocks(np.repeat(qr, 64, axis=0)), O.pool_blocks(np.repeat(kr, 64, axis=0)), scale)
+    for b in range(nB):
+        for c in range(nB):
+            ref = scale * sum(float(qr[b, i]) * float(kr[c, i]) for i in range(d))
+            assert abs(float(z[b, c]) - ref) <= 1e-6 * max(1.0, abs(ref))
