@@ -903,3 +903,27 @@ def test_pooled_logits_of_constant_blocks_are_scaled_dot_products():
         for c in range(nB):
             ref = scale * sum(float(qr[b, i]) * float(kr[c, i]) for i in range(d))
             assert abs(float(z[b, c]) - ref) <= 1e-6 * max(1.0, abs(ref))
+
+
+def test_slash_tiles_only_where_the_diagonal_has_started():
+    # slashes at offsets beyond the rows of the first query tiles: a diagonal
+    # i - j = o crosses a tile only through rows i >= o, so those tiles select
+    # no key tile from it.  Loop reference over the tile's rows and offsets.
+    L = 300
+    S = np.array([0, 150, 200, 290])
+    V = np.array([5, 77])
+    hi = O.HeadIndex(cfg=O.HeadCfg.of(synth.vs(len(V), len(S))), L=L, segs=[(0, L, 0)])
+    hi.vs['all'] = (V, S)
+    for i in range(L):
+        t = i // TILE
+        tiles = set()
+        for p in range(TILE * t, min(L, TILE * t + TILE)):
+            for o in S:
+                if p >= o:
+                    tiles.add((p - o) // TILE)
+        ref = np.array([j <= i and (j // TILE in tiles or j in V) for j in range(L)])
+        assert (O.row_mask(hi, i) == ref).all(), i
+    # tile 1 (rows 64..127): offsets 150, 200 and 290 have not started, so of
+    # key tile 0 only the vertical key 5 is selected; offset 0 gives tile 1
+    m = O.row_mask(hi, 100)
+    assert list(np.nonzero(m[:64])[0]) == [5] and m[64:101].all() and not m[101:].any()
