@@ -927,3 +927,18 @@ def test_slash_tiles_only_where_the_diagonal_has_started():
     # key tile 0 only the vertical key 5 is selected; offset 0 gives tile 1
     m = O.row_mask(hi, 100)
     assert list(np.nonzero(m[:64])[0]) == [5] and m[64:101].all() and not m[101:].any()
+
+
+def test_saturated_vertical_and_slash_sets_hold_every_candidate():
+    # the last 64 rows of a layer reach every column 0..L-1 and every
+    # diagonal offset 0..L-1, so budgets of L select all of them (the
+    # candidate ranges, independent of the masks, which overlap at saturation)
+    L, d = 200, 8
+    q, k, _, _ = small_layer(L, d, [synth.vs(L, L)], seed=4)
+    hi = O.estimate_head(synth.vs(L, L), q[0], k[0], None, 1 / math.sqrt(d))
+    V, S = hi.vs['all']
+    assert list(V) == list(range(L)) and list(S) == list(range(L))
+    # a budget of L - 1 leaves out exactly one candidate of each
+    hi = O.estimate_head(synth.vs(L - 1, L - 1), q[0], k[0], None, 1 / math.sqrt(d))
+    V, S = hi.vs['all']
+    assert len(V) == L - 1 and len(S) == L - 1
